@@ -1,0 +1,220 @@
+/*
+ * ps.h -- C ABI of the Prefix Sliding attention library (libprefix_sliding.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * Prefix Sliding keeps, for every query, the pinned task prefix (the first P
+ * tokens of the sequence) plus the most recent W tokens; every token in
+ * between leaves the KV cache for good (njhaofan.com article on Prefix
+ * Sliding, section "PrefixSliding如何丢掉中间Token？"; agihunt.info summary
+ * "Prefix Sliding for efficient test-time scaling", paragraphs on the two kept
+ * slices and the 4,196-token memory cap).  Key j is visible to query i iff
+ *
+ *     j <= i  and  (j < P  or  j > i - W).
+ *
+ * Position IDs keep climbing (Continue PE, agihunt.info summary, paragraph on
+ * position encodings): keys are stored already rotated at their own position
+ * and are never re-encoded, so evicting a token never touches another.
+ *
+ * Conventions shared by every entry point
+ *  - Memory: the caller owns all device memory and every stream.  The library
+ *    allocates nothing on the device, ever; a cache handle owns only a small
+ *    host struct.  Pointers documented "device" must be device-accessible
+ *    (hipMalloc / torch CUDA tensors); "host" pointers are read before return.
+ *  - Streams: `stream` is a hipStream_t passed as void* (NULL = the null
+ *    stream).  All device work is enqueued on it and the call returns without
+ *    waiting; outputs are valid once the stream reaches that point.
+ *  - Errors: every function validates its host-visible arguments before any
+ *    device work and returns a ps_status; nothing is enqueued on error.  A
+ *    failed launch is reported as PS_ERR_HIP.  No C++ exception crosses the
+ *    ABI.  Device-resident arguments (positions, prefix lengths, cache rows)
+ *    are not read by the host; their preconditions are listed per call and
+ *    are the caller's responsibility.
+ *  - Concurrency: calls that use the same cache must be ordered (one stream, or
+ *    streams joined by events): decode calls share one split-K workspace
+ *    inside the cache buffer.
+ *  - dtypes: PS_BF16 (the production path; fp32 accumulation) and PS_F32 (a
+ *    debug path computing in fp32 throughout).  head_dim is 64 or 128.
+ *  - Layouts are row-major C arrays; the last index is contiguous.
+ */
+#ifndef PREFIX_SLIDING_PS_H
+#define PREFIX_SLIDING_PS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PS_OK = 0,
+    PS_ERR_INVALID = 1,      /* bad argument (NULL pointer, out-of-range index, size) */
+    PS_ERR_UNSUPPORTED = 2,  /* valid but not implemented (head_dim, dtype, GQA ratio) */
+    PS_ERR_CAPACITY = 3,     /* buffer too small for the described cache */
+    PS_ERR_HIP = 4           /* a HIP runtime call or kernel launch failed */
+} ps_status;
+
+typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
+
+/* Static shape of a cache.  One cache holds every layer of up to max_seqs
+ * sequences.  Per (layer, sequence, kv head) it has prefix_cap PREFIX slots
+ * and a W-slot RING: the two-region cache of the papers.ananclaw.com explainer,
+ * section "核心方法" (PREFIX block kept read-only after prefill, WINDOW block of
+ * the last W tokens, middle evicted).  Its size is bounded by P + W tokens no
+ * matter how long the trace grows (njhaofan.com, same section as above). */
+typedef struct {
+    int32_t n_layers;    /* >= 1 */
+    int32_t max_seqs;    /* >= 1 */
+    int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
+    int32_t n_kv_heads;  /* Hkv >= 1 */
+    int32_t head_dim;    /* d: 64 or 128 */
+    int32_t prefix_cap;  /* largest prefix length P any sequence may use, >= 0 */
+    int32_t window;      /* W >= 1 */
+    int32_t dtype;       /* ps_dtype of K, V, queries and outputs */
+} ps_cache_desc;
+
+typedef struct ps_cache ps_cache; /* opaque host handle */
+
+/* A batch of sequences for append / decode.  All three arrays are DEVICE
+ * arrays of length n.  Preconditions (not checked): rows are distinct values
+ * in [0, max_seqs); 0 <= prefix_len[b] <= prefix_cap; pos[b] >= 0. */
+typedef struct {
+    int32_t n;                  /* number of sequences in the call, 1..max_seqs */
+    const int32_t* rows;        /* device: cache row of each sequence */
+    const int32_t* prefix_len;  /* device: P of each sequence */
+    const int64_t* pos;         /* device: position of the first new token /
+                                   of the query (see each call) */
+} ps_seq_batch;
+
+/* Bytes of device memory a cache with this shape needs (K and V for every
+ * layer, plus the decode split-K workspace).  0 if the descriptor is invalid. */
+size_t ps_cache_bytes(const ps_cache_desc* desc);
+
+/* Carve `dev_mem` (device, >= ps_cache_bytes(desc) bytes, 256-byte aligned,
+ * owned by the caller and kept alive until ps_cache_destroy) into the cache
+ * regions, clear the workspace counters with a kernel on `stream`, and return
+ * a handle in *out.  K/V slots are NOT cleared: a slot is read only after the
+ * position it holds was appended.
+ * Errors: PS_ERR_INVALID (NULL, bad shape, misaligned), PS_ERR_UNSUPPORTED
+ * (head_dim or dtype), PS_ERR_CAPACITY (bytes too small), PS_ERR_HIP. */
+int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void* stream,
+                    ps_cache** out);
+
+/* Free the host handle.  The device buffer stays the caller's.  NULL is a no-op. */
+int ps_cache_destroy(ps_cache* cache);
+
+/* Device addresses of layer `layer`'s K and V regions.  Layout of each:
+ *   [max_seqs][n_kv_heads][prefix_cap + window][head_dim]   (cache dtype)
+ * Row s < prefix_cap of a (sequence, kv head) holds prefix position s; row
+ * prefix_cap + r holds the token at the position p >= P with
+ * (p - P) mod W == r that was appended last.  For inspection and snapshot /
+ * restore (a plain device copy of the whole buffer restores a cache).
+ * Errors: PS_ERR_INVALID. */
+int ps_cache_kv(const ps_cache* cache, int32_t layer, void** k, void** v);
+
+/* Split-K granularity of decode: rows (keys) handled per workgroup.  0 picks
+ * automatically (default); otherwise one of 16, 32, 64, 128, 256 for bf16
+ * head_dim 128 (the set scales with row size).  Errors: PS_ERR_INVALID,
+ * PS_ERR_UNSUPPORTED. */
+int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
+
+/* Append n_new consecutive tokens per sequence to layer `layer`: token t of
+ * sequence b has position pos[b] + t.  A position p < P goes to prefix row p;
+ * p >= P goes to ring row (p - P) mod W, overwriting the token at p - W, which
+ * is exactly the token that falls out of the window (positional eviction:
+ * njhaofan.com section above; papers.ananclaw.com "被丢弃的中间区").  When more
+ * than W ring-bound tokens arrive in one call only the last W are written, so
+ * the resulting cache is bit-identical to n_new single-token appends.
+ *   k_new, v_new: device [n][n_new][n_kv_heads][head_dim], pre-rotated keys.
+ * Preconditions: positions of a sequence are appended in increasing order and
+ * a decode/prefill query at position i sees the cache as left by appending
+ * every position < i (Continue PE: nothing is ever re-encoded).
+ * Errors: PS_ERR_INVALID, PS_ERR_HIP. */
+int ps_kv_append_evict(ps_cache* cache, int32_t layer, const ps_seq_batch* batch,
+                       int32_t n_new, const void* k_new, const void* v_new, void* stream);
+
+/* One decode query per sequence at position i = pos[b], which must already be
+ * appended: GQA attention over the visible keys of i, which are exactly the
+ * retained cache rows (prefix rows [0, min(P, i+1)) and ring rows of positions
+ * (i - W, i]).  Query head h reads kv head floor(h * Hkv / Hq).
+ *   q:   device [n][n_q_heads][head_dim]
+ *   out: device [n][n_q_heads][head_dim]  (cache dtype; normalised output)
+ *   lse: device [n][n_q_heads] float, natural-log log-sum-exp of the scaled
+ *        scores, or NULL
+ *   scale: multiplier of q.k (1/sqrt(head_dim) for standard attention)
+ * Split-K over the keys with a log-sum-exp combine done by the last finishing
+ * workgroup of each (sequence, kv head).  Errors: PS_ERR_INVALID, PS_ERR_HIP. */
+int ps_decode_attn(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, const void* q,
+                   void* out, float* lse, float scale, void* stream);
+
+/* Fused decode step: append the token at position pos[b] (k_new, v_new: device
+ * [n][n_kv_heads][head_dim]) and attend from it in one launch.  Same cache
+ * state and same result as ps_kv_append_evict(n_new = 1) followed by
+ * ps_decode_attn.  Errors: PS_ERR_INVALID, PS_ERR_HIP. */
+int ps_decode_step(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, const void* q,
+                   const void* k_new, const void* v_new, void* out, float* lse, float scale,
+                   void* stream);
+
+/* Chunked prefill (cache != NULL) or trainer-side forward (cache == NULL).
+ *
+ * Every sequence of the batch has the same prefix length P and its chunk
+ * occupies positions start_pos .. start_pos + seq_len - 1.  Query i of the
+ * chunk attends to the visible keys among
+ *   - the cached prefix rows [0, min(P, start_pos))          (cache mode)
+ *   - the cached ring rows holding positions
+ *     [max(P, start_pos - W), start_pos)                      (cache mode)
+ *   - the chunk's own keys start_pos .. i.
+ * Cache mode reads the cache as left by appending every position < start_pos
+ * and does NOT append the chunk: commit it afterwards with
+ * ps_kv_append_evict(n_new = seq_len).  Trainer mode sees only the chunk
+ * (start_pos is normally 0: the prefix is the first P tokens of the slice,
+ * and the trainer receives the last 4W tokens of a rollout -- njhaofan.com
+ * section "无需训练最高提速3倍，RL扩展到10万Token"; agihunt.info, paragraph on
+ * truncated backprop).
+ *
+ * Key tiles wholly outside prefix and window are skipped without a load, tiles
+ * entirely visible run unmasked, and only tiles that straddle the boundary
+ * apply an elementwise mask (the two-level filtering of the pages' Hopper
+ * kernel: agihunt.info paragraph on the FlashAttention kernel; njhaofan.com
+ * section "PrefixSliding如何丢掉中间Token？").  bf16 uses MFMA for Q.K^T and P.V. */
+typedef struct {
+    ps_cache* cache;        /* NULL: trainer mode */
+    int32_t layer;          /* cache mode only */
+    int32_t batch;          /* B >= 1 (<= max_seqs in cache mode) */
+    int32_t seq_len;        /* T >= 0 tokens per sequence (0: nothing to do) */
+    int32_t n_q_heads;      /* trainer mode; must match the cache in cache mode */
+    int32_t n_kv_heads;     /* trainer mode; must match the cache in cache mode */
+    int32_t head_dim;       /* trainer mode; must match the cache in cache mode */
+    int32_t dtype;          /* trainer mode; must match the cache in cache mode */
+    int64_t start_pos;      /* position of chunk token 0, >= 0 */
+    int64_t prefix_len;     /* P >= 0 (<= prefix_cap in cache mode) */
+    int64_t window;         /* W >= 1 (must equal the cache's W in cache mode) */
+    const int32_t* rows;    /* device [B] cache rows (cache mode), else NULL */
+    const void* q;          /* device [B][T][n_q_heads][head_dim] */
+    const void* k;          /* device [B][T][n_kv_heads][head_dim] */
+    const void* v;          /* device [B][T][n_kv_heads][head_dim] */
+    void* out;              /* device [B][T][n_q_heads][head_dim] */
+    float* lse;             /* device [B][T][n_q_heads] natural log, or NULL */
+    float scale;            /* multiplier of q.k */
+} ps_prefill_args;
+
+int ps_prefill_attn(const ps_prefill_args* args, void* stream);
+
+/* Class of a (query tile, key tile) pair, query positions [i0, i1] and key
+ * positions [j0, j1] (both non-empty, contiguous): 0 SKIP (no visible pair),
+ * 1 FULL (every pair visible), 2 MASKED.  The same closed form the prefill
+ * kernel uses on the device; exported for host-side planning and tests.
+ * Returns -1 for an empty range, P < 0 or W < 1. */
+int ps_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P, int64_t W);
+
+/* Static description of a status code. */
+const char* ps_status_str(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char* ps_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PREFIX_SLIDING_PS_H */

@@ -1,0 +1,233 @@
+"""Python binding of libprefix_sliding.so (Prefix Sliding attention on MI355X).
+
+Argument marshalling only: every step of the attention path runs in the
+library's HIP kernels.  PyTorch provides device memory and streams.  The
+functions keep the C names (``ps_cache_create``, ``ps_kv_append_evict``,
+``ps_decode_attn``, ``ps_decode_step``, ``ps_prefill_attn`` ...) and raise
+``PSError`` on a non-OK status.  If the shared library is missing this module
+fails to import: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "PS_BF16", "PS_F32", "PSError", "CacheDesc", "Cache", "lib",
+    "ps_cache_bytes", "ps_cache_create", "ps_cache_destroy", "ps_cache_kv",
+    "ps_cache_set_decode_split", "ps_kv_append_evict", "ps_decode_attn", "ps_decode_step",
+    "ps_prefill_attn", "ps_tile_class", "ps_status_str", "ps_version", "SeqBatch",
+]
+
+PS_OK, PS_ERR_INVALID, PS_ERR_UNSUPPORTED, PS_ERR_CAPACITY, PS_ERR_HIP = range(5)
+PS_BF16, PS_F32 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprefix_sliding.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m prefix_sliding_kv_amd.build` "
+                      "(or __graft_entry__.build()); there is no non-HIP fallback")
+lib = ctypes.CDLL(LIB_PATH)
+
+
+class CacheDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
+                ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("prefix_cap", ctypes.c_int32),
+                ("window", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class _SeqBatch(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("rows", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
+                ("pos", ctypes.c_void_p)]
+
+
+class _PrefillArgs(ctypes.Structure):
+    _fields_ = [("cache", ctypes.c_void_p), ("layer", ctypes.c_int32), ("batch", ctypes.c_int32),
+                ("seq_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("start_pos", ctypes.c_int64),
+                ("prefix_len", ctypes.c_int64), ("window", ctypes.c_int64),
+                ("rows", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
+                ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
+                ("scale", ctypes.c_float)]
+
+
+_vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+_SIGS = {
+    "ps_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc)]),
+    "ps_cache_create": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _vp, ctypes.c_size_t, _vp,
+                                       ctypes.POINTER(_vp)]),
+    "ps_cache_destroy": (ctypes.c_int, [_vp]),
+    "ps_cache_kv": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "ps_cache_set_decode_split": (ctypes.c_int, [_vp, _i32]),
+    "ps_kv_append_evict": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, _vp]),
+    "ps_decode_attn": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _vp, _vp, _vp,
+                                      ctypes.c_float, _vp]),
+    "ps_decode_step": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _vp, _vp, _vp, _vp, _vp,
+                                      ctypes.c_float, _vp]),
+    "ps_prefill_attn": (ctypes.c_int, [ctypes.POINTER(_PrefillArgs), _vp]),
+    "ps_tile_class": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _i64]),
+    "ps_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "ps_version": (ctypes.c_char_p, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PSError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {lib.ps_status_str(status).decode()} (status {status})")
+        self.status = status
+
+
+def _check(status: int, where: str) -> None:
+    if status != PS_OK:
+        raise PSError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_TORCH_DTYPE = {PS_BF16: torch.bfloat16, PS_F32: torch.float32}
+
+
+def ps_status_str(status: int) -> str:
+    return lib.ps_status_str(status).decode()
+
+
+def ps_version() -> str:
+    return lib.ps_version().decode()
+
+
+def ps_tile_class(i0: int, i1: int, j0: int, j1: int, P: int, W: int) -> int:
+    return lib.ps_tile_class(i0, i1, j0, j1, P, W)
+
+
+def ps_cache_bytes(desc: CacheDesc) -> int:
+    return lib.ps_cache_bytes(ctypes.byref(desc))
+
+
+def ps_cache_create(desc: CacheDesc, buffer: torch.Tensor, stream=None) -> int:
+    """Returns the opaque handle (an int).  ``buffer`` is a CUDA uint8 tensor."""
+    h = ctypes.c_void_p()
+    _check(lib.ps_cache_create(ctypes.byref(desc), _ptr(buffer), buffer.numel() * buffer.element_size(),
+                               _stream(stream), ctypes.byref(h)), "ps_cache_create")
+    return h.value
+
+
+def ps_cache_destroy(handle: int) -> None:
+    _check(lib.ps_cache_destroy(ctypes.c_void_p(handle)), "ps_cache_destroy")
+
+
+def ps_cache_kv(handle: int, layer: int):
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(lib.ps_cache_kv(ctypes.c_void_p(handle), layer, ctypes.byref(k), ctypes.byref(v)), "ps_cache_kv")
+    return k.value, v.value
+
+
+def ps_cache_set_decode_split(handle: int, rows_per_split: int) -> None:
+    _check(lib.ps_cache_set_decode_split(ctypes.c_void_p(handle), rows_per_split),
+           "ps_cache_set_decode_split")
+
+
+class SeqBatch:
+    """Device-resident per-sequence metadata: cache rows (int32), prefix
+    lengths (int32) and positions (int64), each a CUDA tensor of length n."""
+
+    def __init__(self, rows: torch.Tensor, prefix_len: torch.Tensor, pos: torch.Tensor):
+        assert rows.dtype == torch.int32 and prefix_len.dtype == torch.int32 and pos.dtype == torch.int64
+        assert rows.is_cuda and prefix_len.is_cuda and pos.is_cuda
+        assert rows.numel() == prefix_len.numel() == pos.numel()
+        self.rows, self.prefix_len, self.pos = rows, prefix_len, pos
+        self._c = _SeqBatch(rows.numel(), rows.data_ptr(), prefix_len.data_ptr(), pos.data_ptr())
+
+    @property
+    def n(self) -> int:
+        return self.rows.numel()
+
+
+def ps_kv_append_evict(handle: int, layer: int, batch: SeqBatch, n_new: int, k_new, v_new,
+                       stream=None) -> None:
+    _check(lib.ps_kv_append_evict(ctypes.c_void_p(handle), layer, ctypes.byref(batch._c), n_new,
+                                  _ptr(k_new), _ptr(v_new), _stream(stream)), "ps_kv_append_evict")
+
+
+def ps_decode_attn(handle: int, layer: int, batch: SeqBatch, q, out, lse=None, scale: float = 1.0,
+                   stream=None) -> None:
+    _check(lib.ps_decode_attn(ctypes.c_void_p(handle), layer, ctypes.byref(batch._c), _ptr(q), _ptr(out),
+                              _ptr(lse), scale, _stream(stream)), "ps_decode_attn")
+
+
+def ps_decode_step(handle: int, layer: int, batch: SeqBatch, q, k_new, v_new, out, lse=None,
+                   scale: float = 1.0, stream=None) -> None:
+    _check(lib.ps_decode_step(ctypes.c_void_p(handle), layer, ctypes.byref(batch._c), _ptr(q), _ptr(k_new),
+                              _ptr(v_new), _ptr(out), _ptr(lse), scale, _stream(stream)), "ps_decode_step")
+
+
+def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: int, scale: float,
+                    lse=None, cache: int | None = None, layer: int = 0, rows=None,
+                    dtype: int | None = None, stream=None) -> None:
+    """q/out [B][T][Hq][d], k/v [B][T][Hkv][d] CUDA tensors; ``cache`` None means
+    trainer mode (self-attention over the given tokens only)."""
+    B, T, hq, d = q.shape
+    hkv = k.shape[2]
+    if dtype is None:
+        dtype = PS_BF16 if q.dtype == torch.bfloat16 else PS_F32
+    a = _PrefillArgs(cache or 0, layer, B, T, hq, hkv, d, dtype, start_pos, prefix_len, window,
+                     rows.data_ptr() if rows is not None else 0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     out.data_ptr(), lse.data_ptr() if lse is not None else 0, scale)
+    _check(lib.ps_prefill_attn(ctypes.byref(a), _stream(stream)), "ps_prefill_attn")
+
+
+class Cache:
+    """A cache whose device buffer is a torch uint8 tensor (torch allocates it;
+    the library only carves it)."""
+
+    def __init__(self, n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window,
+                 dtype=PS_BF16, device="cuda", stream=None):
+        self.desc = CacheDesc(n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window, dtype)
+        nbytes = ps_cache_bytes(self.desc)
+        if nbytes == 0:
+            raise PSError(PS_ERR_INVALID, "ps_cache_bytes")
+        self.nbytes = nbytes
+        self.buffer = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.handle = ps_cache_create(self.desc, self.buffer, stream)
+        self.dtype = _TORCH_DTYPE[dtype]
+
+    def kv(self, layer: int):
+        """Views of layer's K and V regions: [max_seqs][Hkv][prefix_cap+W][d]."""
+        kp, vp = ps_cache_kv(self.handle, layer)
+        d = self.desc
+        shape = (d.max_seqs, d.n_kv_heads, d.prefix_cap + d.window, d.head_dim)
+        esz = 2 if d.dtype == PS_BF16 else 4
+        base = self.buffer.data_ptr()
+        n = d.max_seqs * d.n_kv_heads * (d.prefix_cap + d.window) * d.head_dim
+        out = []
+        for p in (kp, vp):
+            off = p - base
+            out.append(self.buffer[off:off + n * esz].view(self.dtype).view(shape))
+        return out[0], out[1]
+
+    def close(self):
+        if getattr(self, "handle", None):
+            ps_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

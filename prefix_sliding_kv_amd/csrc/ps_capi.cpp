@@ -1,0 +1,304 @@
+// C ABI of the Prefix Sliding library: argument validation, cache layout,
+// launch planning.  Every device step runs in the library's own HIP kernels;
+// nothing here touches tensor data on the host.
+#include <math.h>
+#include <new>
+#include <string.h>
+
+#include "ps_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool desc_ok(const ps_cache_desc* d) {
+    if (!d) return false;
+    if (d->n_layers < 1 || d->max_seqs < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
+    if (d->n_q_heads % d->n_kv_heads != 0) return false;
+    if (d->prefix_cap < 0 || d->window < 1) return false;
+    return true;
+}
+
+bool desc_supported(const ps_cache_desc* d) {
+    if (d->head_dim != 64 && d->head_dim != 128) return false;
+    if (d->dtype != PS_BF16 && d->dtype != PS_F32) return false;
+    const int g = d->n_q_heads / d->n_kv_heads;
+    return g == 1 || g == 2 || g == 4 || g == 8;
+}
+
+struct Layout {
+    size_t elem, layer_bytes, kv_bytes, ws_o_bytes, ws_ml_bytes, ticket_bytes, total;
+    int64_t rows_per_head;
+    int32_t s_max;
+};
+
+Layout layout_of(const ps_cache_desc* d) {
+    Layout l{};
+    l.elem = d->dtype == PS_BF16 ? 2 : 4;
+    l.rows_per_head = (int64_t)d->prefix_cap + d->window;
+    l.layer_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * l.rows_per_head * d->head_dim * l.elem);
+    l.kv_bytes = l.layer_bytes * (size_t)d->n_layers;
+    l.s_max = (int32_t)((l.rows_per_head + ps::kMinSplitRows - 1) / ps::kMinSplitRows);
+    l.ws_o_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * d->head_dim * 4);
+    l.ws_ml_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * 2 * 4);
+    l.ticket_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * 4);
+    l.total = 2 * l.kv_bytes + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes;
+    return l;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PS_OK : PS_ERR_HIP; }
+
+bool batch_ok(const ps_cache* c, const ps_seq_batch* b) {
+    return b && b->n >= 1 && b->n <= c->desc.max_seqs && b->rows && b->prefix_len && b->pos;
+}
+
+// Rows per decode split: the largest that still gives at least two
+// workgroups per CU (256 CUs), else the smallest allowed.
+int auto_decode_rows(const ps_cache* c, int n_seqs) {
+    const int r1 = ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
+    int best = 0;
+    for (int u = 1; u <= 16; u *= 2) {
+        const int rows = r1 * u;
+        if (rows < ps::kMinSplitRows) continue;
+        if (best == 0) best = rows;
+        const int64_t splits = (c->rows_per_head + rows - 1) / rows;
+        if ((int64_t)n_seqs * c->desc.n_kv_heads * splits >= 512) best = rows;
+    }
+    return best;
+}
+
+bool decode_rows_ok(const ps_cache* c, int rows) {
+    const int r1 = ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
+    if (rows < ps::kMinSplitRows || rows % r1 != 0) return false;
+    const int u = rows / r1;
+    return u == 1 || u == 2 || u == 4 || u == 8 || u == 16;
+}
+
+int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const void* q, const void* knew,
+                  const void* vnew, void* out, float* lse, float scale, void* stream) {
+    if (!c || !batch_ok(c, batch) || !q || !out) return PS_ERR_INVALID;
+    if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
+    if (!isfinite(scale)) return PS_ERR_INVALID;
+    ps::DecodeParams p{};
+    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
+    p.vc = c->v_region + (size_t)layer * c->layer_bytes;
+    p.hq = c->desc.n_q_heads;
+    p.hkv = c->desc.n_kv_heads;
+    p.pcap = c->desc.prefix_cap;
+    p.window = c->desc.window;
+    p.rows_per_head = c->rows_per_head;
+    p.rows = batch->rows;
+    p.plen = batch->prefix_len;
+    p.pos = batch->pos;
+    p.q = q;
+    p.out = out;
+    p.lse = lse;
+    p.scale_log2 = scale * kLog2e;
+    p.knew = knew;
+    p.vnew = vnew;
+    p.ws_o = c->ws_o;
+    p.ws_ml = c->ws_ml;
+    p.tickets = c->tickets;
+    p.s_max = c->s_max;
+    p.n_seqs = batch->n;
+    const int rows = c->decode_rows > 0 ? c->decode_rows : auto_decode_rows(c, batch->n);
+    const int group = c->desc.n_q_heads / c->desc.n_kv_heads;
+    return hip_status(ps::launch_decode(c->desc.dtype, c->desc.head_dim, group, rows, p, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ps_cache_bytes(const ps_cache_desc* desc) {
+    if (!desc_ok(desc) || !desc_supported(desc)) return 0;
+    return layout_of(desc).total;
+}
+
+int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void* stream, ps_cache** out) {
+    if (!out) return PS_ERR_INVALID;
+    *out = nullptr;
+    if (!desc_ok(desc) || !dev_mem) return PS_ERR_INVALID;
+    if (!desc_supported(desc)) return PS_ERR_UNSUPPORTED;
+    if (reinterpret_cast<uintptr_t>(dev_mem) % kAlign != 0) return PS_ERR_INVALID;
+    const Layout l = layout_of(desc);
+    if (bytes < l.total) return PS_ERR_CAPACITY;
+    ps_cache* c = new (std::nothrow) ps_cache;
+    if (!c) return PS_ERR_INVALID;
+    c->desc = *desc;
+    c->base = static_cast<char*>(dev_mem);
+    c->bytes = bytes;
+    c->elem_bytes = l.elem;
+    c->rows_per_head = l.rows_per_head;
+    c->layer_bytes = l.layer_bytes;
+    c->k_region = c->base;
+    c->v_region = c->base + l.kv_bytes;
+    c->ws_o = reinterpret_cast<float*>(c->base + 2 * l.kv_bytes);
+    c->ws_ml = reinterpret_cast<float*>(c->base + 2 * l.kv_bytes + l.ws_o_bytes);
+    c->tickets = reinterpret_cast<uint32_t*>(c->base + 2 * l.kv_bytes + l.ws_o_bytes + l.ws_ml_bytes);
+    c->s_max = l.s_max;
+    c->decode_rows = 0;
+    const hipError_t e = ps::launch_fill_u32(c->tickets, (size_t)desc->max_seqs * desc->n_kv_heads, 0u,
+                                             (hipStream_t)stream);
+    if (e != hipSuccess) {
+        delete c;
+        return PS_ERR_HIP;
+    }
+    *out = c;
+    return PS_OK;
+}
+
+int ps_cache_destroy(ps_cache* cache) {
+    delete cache;
+    return PS_OK;
+}
+
+int ps_cache_kv(const ps_cache* c, int32_t layer, void** k, void** v) {
+    if (!c || !k || !v || layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
+    *k = c->k_region + (size_t)layer * c->layer_bytes;
+    *v = c->v_region + (size_t)layer * c->layer_bytes;
+    return PS_OK;
+}
+
+int ps_cache_set_decode_split(ps_cache* c, int32_t rows_per_split) {
+    if (!c || rows_per_split < 0) return PS_ERR_INVALID;
+    if (rows_per_split != 0 && !decode_rows_ok(c, rows_per_split)) return PS_ERR_UNSUPPORTED;
+    c->decode_rows = rows_per_split;
+    return PS_OK;
+}
+
+int ps_kv_append_evict(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int32_t n_new, const void* k_new,
+                       const void* v_new, void* stream) {
+    if (!c || !batch_ok(c, batch) || n_new < 0) return PS_ERR_INVALID;
+    if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
+    if (n_new == 0) return PS_OK;
+    if (!k_new || !v_new) return PS_ERR_INVALID;
+    ps::AppendParams p{};
+    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
+    p.vc = c->v_region + (size_t)layer * c->layer_bytes;
+    p.hkv = c->desc.n_kv_heads;
+    p.pcap = c->desc.prefix_cap;
+    p.window = c->desc.window;
+    p.rows_per_head = c->rows_per_head;
+    p.rows = batch->rows;
+    p.plen = batch->prefix_len;
+    p.pos = batch->pos;
+    p.n_seqs = batch->n;
+    p.n_new = n_new;
+    p.knew = k_new;
+    p.vnew = v_new;
+    return hip_status(ps::launch_append(c->desc.dtype, c->desc.head_dim, p, (hipStream_t)stream));
+}
+
+int ps_decode_attn(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const void* q, void* out, float* lse,
+                   float scale, void* stream) {
+    return decode_common(c, layer, batch, q, nullptr, nullptr, out, lse, scale, stream);
+}
+
+int ps_decode_step(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const void* q, const void* k_new,
+                   const void* v_new, void* out, float* lse, float scale, void* stream) {
+    if (!k_new || !v_new) return PS_ERR_INVALID;
+    return decode_common(c, layer, batch, q, k_new, v_new, out, lse, scale, stream);
+}
+
+int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
+    if (!a) return PS_ERR_INVALID;
+    if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1)
+        return PS_ERR_INVALID;
+    if (!isfinite(a->scale)) return PS_ERR_INVALID;
+    int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim, dtype = a->dtype;
+    const ps_cache* c = a->cache;
+    if (c) {
+        if (a->layer < 0 || a->layer >= c->desc.n_layers || a->batch > c->desc.max_seqs || !a->rows)
+            return PS_ERR_INVALID;
+        if (hq != c->desc.n_q_heads || hkv != c->desc.n_kv_heads || d != c->desc.head_dim ||
+            dtype != c->desc.dtype)
+            return PS_ERR_INVALID;
+        if (a->window != c->desc.window || a->prefix_len > c->desc.prefix_cap) return PS_ERR_INVALID;
+    }
+    if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
+    if (dtype != PS_BF16 && dtype != PS_F32) return PS_ERR_UNSUPPORTED;
+    if (d != 64 && d != 128) return PS_ERR_UNSUPPORTED;
+    const int group = hq / hkv;
+    if (dtype == PS_BF16 && (d != 128 || (group != 1 && group != 2 && group != 4))) return PS_ERR_UNSUPPORTED;
+    if (a->seq_len == 0) return PS_OK;
+    if (!a->q || !a->k || !a->v || !a->out) return PS_ERR_INVALID;
+
+    ps::PrefillParams p{};
+    const int64_t P = a->prefix_len, W = a->window, S = a->start_pos, T = a->seq_len;
+    int nr = 0;
+    if (c) {
+        const char* kl = c->k_region + (size_t)a->layer * c->layer_bytes;
+        const char* vl = c->v_region + (size_t)a->layer * c->layer_bytes;
+        const int64_t rph = c->rows_per_head;
+        const size_t el = c->elem_bytes;
+        auto cache_run = [&](int64_t first_row, int64_t pos0, int64_t n) {
+            ps::KeyRun& r = p.runs[nr++];
+            r.k = kl + (size_t)first_row * d * el;
+            r.v = vl + (size_t)first_row * d * el;
+            r.seq_stride = (int64_t)hkv * rph * d;
+            r.head_stride = rph * d;
+            r.row_stride = d;
+            r.pos0 = pos0;
+            r.n = n;
+            r.rows = a->rows;
+        };
+        const int64_t n_pre = S < P ? S : P;
+        if (n_pre > 0) cache_run(0, 0, n_pre);
+        if (S > P) {
+            const int64_t first = S - W > P ? S - W : P;  // oldest position the ring still holds
+            const int64_t cnt = S - first;
+            const int64_t slot = (first - P) % W;
+            const int64_t n_a = slot + cnt <= W ? cnt : W - slot;
+            cache_run(c->desc.prefix_cap + slot, first, n_a);
+            if (n_a < cnt) cache_run(c->desc.prefix_cap, first + n_a, cnt - n_a);
+        }
+    }
+    {
+        ps::KeyRun& r = p.runs[nr++];
+        r.k = a->k;
+        r.v = a->v;
+        r.seq_stride = T * hkv * d;
+        r.head_stride = d;
+        r.row_stride = (int64_t)hkv * d;
+        r.pos0 = S;
+        r.n = T;
+        r.rows = nullptr;
+    }
+    p.n_runs = nr;
+    p.batch = a->batch;
+    p.seq_len = a->seq_len;
+    p.hq = hq;
+    p.hkv = hkv;
+    p.start_pos = S;
+    p.P = P;
+    p.W = W;
+    p.q = a->q;
+    p.out = a->out;
+    p.lse = a->lse;
+    p.scale_log2 = a->scale * kLog2e;
+    return hip_status(ps::launch_prefill(dtype, d, group, p, (hipStream_t)stream));
+}
+
+int ps_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P, int64_t W) {
+    if (i1 < i0 || j1 < j0 || P < 0 || W < 1) return -1;
+    return ps::tile_class(i0, i1, j0, j1, P, W);
+}
+
+const char* ps_status_str(int s) {
+    switch (s) {
+        case PS_OK: return "ok";
+        case PS_ERR_INVALID: return "invalid argument";
+        case PS_ERR_UNSUPPORTED: return "unsupported configuration";
+        case PS_ERR_CAPACITY: return "buffer too small";
+        case PS_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* ps_version(void) { return "0.1.0"; }
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Internal declarations shared by the library's host code and kernels.
+// Not part of the C ABI (see include/ps.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/ps.h"
+
+// Host handle behind the opaque ps_cache.
+struct ps_cache {
+    ps_cache_desc desc;
+    char* base = nullptr;        // caller's device buffer
+    size_t bytes = 0;
+    size_t elem_bytes = 0;       // 2 (bf16) or 4 (f32)
+    int64_t rows_per_head = 0;   // prefix_cap + window
+    size_t layer_bytes = 0;      // bytes of one layer's K (or V) region
+    char* k_region = nullptr;    // [L][max_seqs][Hkv][Pcap+W][d]
+    char* v_region = nullptr;
+    float* ws_o = nullptr;       // [max_seqs][Hq][s_max][d]  unnormalised partial outputs
+    float* ws_ml = nullptr;      // [max_seqs][Hq][s_max][2]  (running max in log2 units, sum)
+    uint32_t* tickets = nullptr; // [max_seqs][Hkv] arrival counters (self-resetting)
+    int32_t s_max = 0;           // split slots per (seq, q head) in the workspace
+    int32_t decode_rows = 0;     // requested rows per split, 0 = automatic
+};
+
+namespace ps {
+
+constexpr int kMinSplitRows = 16;  // smallest rows-per-split the workspace is sized for
+
+// Visibility of key position j to query position i (prefix + window, causal).
+__host__ __device__ inline bool visible(int64_t i, int64_t j, int64_t P, int64_t W) {
+    return j <= i && (j < P || j > i - W);
+}
+
+// Tile classes of the prefill kernel.
+enum TileClass : int { kSkip = 0, kFull = 1, kMasked = 2 };
+
+// Closed-form class of query positions [i0, i1] against key positions [j0, j1]:
+//   SKIP   iff j0 > i1, or every key is a non-prefix key older than the window
+//          of the earliest query (j0 >= P and j1 <= i0 - W);
+//   FULL   iff every key is causal for the earliest query (j1 <= i0) and every
+//          non-prefix key is inside the window of the latest query
+//          (j1 < P or max(j0, P) > i1 - W);
+//   MASKED otherwise.
+__host__ __device__ inline int tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P,
+                                          int64_t W) {
+    if (j0 > i1 || (j0 >= P && j1 <= i0 - W)) return kSkip;
+    const int64_t lo = j0 > P ? j0 : P;
+    if (j1 <= i0 && (j1 < P || lo > i1 - W)) return kFull;
+    return kMasked;
+}
+
+// ------------------------------------------------------------ decode
+struct DecodeParams {
+    const void* kc;        // layer's K region
+    const void* vc;        // layer's V region
+    int32_t hq, hkv;
+    int32_t pcap, window;
+    int64_t rows_per_head; // pcap + window
+    const int32_t* rows;
+    const int32_t* plen;
+    const int64_t* pos;
+    const void* q;
+    void* out;
+    float* lse;
+    float scale_log2;      // scale * log2(e)
+    const void* knew;      // fused append: [n][Hkv][d]; nullptr for attention only
+    const void* vnew;
+    float* ws_o;
+    float* ws_ml;
+    uint32_t* tickets;
+    int32_t s_max;
+    int32_t n_seqs;
+};
+
+// Launch decode attention; rows_per_split chosen by the caller (host).
+hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split,
+                         const DecodeParams& p, hipStream_t stream);
+// Valid rows-per-split values for a (dtype, head_dim): rows_per_split must equal
+// 4 waves * rows-per-wave-load * U with U in {1,2,4,8,16}.
+int decode_rows_per_load(int dtype, int head_dim);
+
+// ------------------------------------------------------------ append
+struct AppendParams {
+    void* kc;
+    void* vc;
+    int32_t hkv;
+    int32_t pcap, window;
+    int64_t rows_per_head;
+    const int32_t* rows;
+    const int32_t* plen;
+    const int64_t* pos;
+    int32_t n_seqs, n_new;
+    const void* knew;      // [n][n_new][Hkv][d]
+    const void* vnew;
+};
+hipError_t launch_append(int dtype, int head_dim, const AppendParams& p, hipStream_t stream);
+
+// Zero-fill of a u32 array with a kernel (safe inside captured graphs).
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
+
+// ------------------------------------------------------------ prefill
+// A run of keys with contiguous positions and contiguous storage.
+struct KeyRun {
+    const void* k;         // row 0 of the run for (seq 0, kv head 0)
+    const void* v;
+    int64_t seq_stride;    // elements between sequences
+    int64_t head_stride;   // elements between kv heads
+    int64_t row_stride;    // elements between consecutive rows
+    int64_t pos0;          // position of row 0
+    int64_t n;             // rows in the run
+    const int32_t* rows;   // if non-null: sequence b uses cache row rows[b] (seq_stride applies to it)
+};
+
+constexpr int kMaxRuns = 4;
+
+struct PrefillParams {
+    KeyRun runs[kMaxRuns];
+    int32_t n_runs;
+    int32_t batch, seq_len, hq, hkv;
+    int64_t start_pos, P, W;
+    const void* q;         // [B][T][Hq][d]
+    void* out;
+    float* lse;
+    float scale_log2;
+};
+hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p,
+                          hipStream_t stream);
+
+}  // namespace ps

@@ -1,0 +1,441 @@
+// Chunked-prefill / trainer-side forward for Prefix Sliding on gfx950.
+//
+// Query i sees key j iff j <= i and (j < P or j > i - W).  Keys come in at
+// most four runs of contiguous positions and contiguous storage: the cached
+// prefix, the two halves of the ring (split where it wraps), and the chunk's
+// own keys.  For a query tile with positions [i0, i1] only two intervals of a
+// run can hold visible keys: positions below min(P, i1+1), and positions in
+// (i0 - W, i1].  Key tiles outside both are never visited (SKIP costs
+// nothing); a visited tile is FULL when every (query, key) pair is visible and
+// runs without any mask, and MASKED otherwise, where the rule is applied per
+// element.  This is the two-level filtering the pages describe for their
+// Hopper FlashAttention kernel (agihunt.info summary, paragraph on the
+// FlashAttention kernel; njhaofan.com article, section
+// "PrefixSliding如何丢掉中间Token？"), rebuilt for CDNA4.
+//
+// bf16 path (head_dim 128): a workgroup of 4 waves owns 128 query rows, the G
+// heads of one GQA group stacked over 128/G positions, so every K/V tile
+// staged in LDS serves all heads that share it.  Per 64-key tile each wave
+// computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (a lane then holds 16
+// scores of a single query, so the online softmax needs one cross-lane step),
+// and O^T += V^T P^T with the same instruction, reading V from a transposed
+// LDS copy written while staging.  The next tile's global loads are issued
+// before the current tile's math (register prefetch, two LDS buffers, one
+// barrier per tile).  fp32 path: a plain debug kernel with the same tile
+// walk and classification.
+#include "ps_internal.h"
+
+namespace ps {
+namespace {
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kBN = 64;  // keys per tile
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct alignas(16) Vec16 {
+    uint32_t w[4];
+};
+struct alignas(8) Vec8 {
+    uint32_t w[2];
+};
+
+// Ranges of key tiles of one run that may hold keys visible to queries [i0, i1].
+struct TileWalk {
+    int n_ranges;
+    int run[2 * kMaxRuns];
+    int begin[2 * kMaxRuns];
+    int end[2 * kMaxRuns];
+};
+
+__device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+__device__ inline void plan_walk(const PrefillParams& p, int64_t i0, int64_t i1, TileWalk& w) {
+    w.n_ranges = 0;
+    for (int r = 0; r < p.n_runs; ++r) {
+        const KeyRun& run = p.runs[r];
+        const int64_t n = run.n;
+        if (n <= 0) continue;
+        // prefix part: positions < min(P, i1 + 1)
+        const int64_t hiA = clamp64((p.P < i1 + 1 ? p.P : i1 + 1) - run.pos0, 0, n);
+        // window part: positions in [i0 - W + 1, i1]
+        const int64_t loB = clamp64(i0 - p.W + 1 - run.pos0, 0, n);
+        const int64_t hiB = clamp64(i1 + 1 - run.pos0, 0, n);
+        const int endA = (int)((hiA + kBN - 1) / kBN);
+        int begB = (int)(loB / kBN);
+        const int endB = hiB > loB ? (int)((hiB + kBN - 1) / kBN) : 0;
+        if (endA > 0) {
+            w.run[w.n_ranges] = r;
+            w.begin[w.n_ranges] = 0;
+            w.end[w.n_ranges] = endA;
+            ++w.n_ranges;
+        }
+        if (begB < endA) begB = endA;
+        if (endB > begB) {
+            w.run[w.n_ranges] = r;
+            w.begin[w.n_ranges] = begB;
+            w.end[w.n_ranges] = endB;
+            ++w.n_ranges;
+        }
+    }
+}
+
+// ----------------------------------------------------------------- bf16 MFMA
+constexpr int kKStride = 128 * 2 + 16;  // bytes per K row in LDS (padded)
+constexpr int kVStride = kBN * 2 + 8;   // bytes per transposed V row (one dim) in LDS
+constexpr int kKBytes = kBN * kKStride;
+constexpr int kVBytes = 128 * kVStride;
+constexpr int kStageBytes = kKBytes + kVBytes;
+
+struct TileRegs {
+    Vec16 k[4];
+    Vec16 v[4];
+};
+
+__device__ inline void load_tile_bf16(const PrefillParams& p, int run_idx, int tile, int b, int g, int tid,
+                                      TileRegs& t) {
+    const KeyRun& run = p.runs[run_idx];
+    const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
+    const char* kb = static_cast<const char*>(run.k) + (seq * run.seq_stride + (int64_t)g * run.head_stride) * 2;
+    const char* vb = static_cast<const char*>(run.v) + (seq * run.seq_stride + (int64_t)g * run.head_stride) * 2;
+    const int64_t row0 = (int64_t)tile * kBN;
+    const int piece = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // K: rows tid/16 + 16 i, 16-byte piece tid%16
+        const int64_t rk = row0 + (tid >> 4) + 16 * i;
+        if (rk < run.n)
+            t.k[i] = *reinterpret_cast<const Vec16*>(kb + (rk * run.row_stride) * 2 + piece * 16);
+        else
+            t.k[i] = Vec16{{0, 0, 0, 0}};
+        // V: rows 4*(tid/16) + i, dims 8*(tid%16) .. +8
+        const int64_t rv = row0 + 4 * (tid >> 4) + i;
+        if (rv < run.n)
+            t.v[i] = *reinterpret_cast<const Vec16*>(vb + (rv * run.row_stride) * 2 + piece * 16);
+        else
+            t.v[i] = Vec16{{0, 0, 0, 0}};
+    }
+}
+
+__device__ inline void store_tile_bf16(char* stage, int tid, const TileRegs& t) {
+    char* ks = stage;
+    char* vs = stage + kKBytes;
+    const int piece = tid & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<Vec16*>(ks + ((tid >> 4) + 16 * i) * kKStride + piece * 16) = t.k[i];
+    // transpose: dims 8*piece+e, keys 4*(tid/16) .. +4
+    const int kg = tid >> 4;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1;
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        Vec8 o;
+        o.w[0] = __builtin_amdgcn_perm(t.v[1].w[w], t.v[0].w[w], sel);
+        o.w[1] = __builtin_amdgcn_perm(t.v[3].w[w], t.v[2].w[w], sel);
+        *reinterpret_cast<Vec8*>(vs + (8 * piece + e) * kVStride + kg * 8) = o;
+    }
+}
+
+__device__ inline bf16x8 as_bf16x8(const Vec16& v) {
+    bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+    // round to nearest even (inputs are finite probabilities in [0, 1])
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    ua += 0x7FFFu + ((ua >> 16) & 1u);
+    ub += 0x7FFFu + ((ub >> 16) & 1u);
+    return (ua >> 16) | (ub & 0xFFFF0000u);
+}
+
+template <int G>
+__global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
+    constexpr int D = 128;
+    constexpr int QP = 128 / G;  // positions per query tile
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int h = lane >> 5, col = lane & 31;
+    const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int hw = (wave * 32) / QP;           // head within the group
+    const int pw = (wave * 32) % QP;           // position offset of this wave
+    const int head = g * G + hw;
+
+    const int64_t t0 = (int64_t)qt * QP;       // first chunk row of the tile
+    const int64_t t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
+    const int64_t i0 = p.start_pos + t0;
+    const int64_t i1 = p.start_pos + t_last;
+    const int64_t my_t = t0 + pw + col;
+    const bool q_ok = my_t < p.seq_len;
+    const int64_t my_i = p.start_pos + my_t;
+
+    // Q of this lane's query (B operand): dims 8h + 16ks .. +8
+    Vec16 qreg[8];
+    {
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
+                             (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            qreg[ks] = q_ok ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
+    }
+
+    __shared__ TileWalk walk;
+    if (tid == 0) plan_walk(p, i0, i1, walk);
+    __syncthreads();
+    int total = 0;
+    for (int r = 0; r < walk.n_ranges; ++r) total += walk.end[r] - walk.begin[r];
+
+    f32x16 o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    int cr = 0, ct = walk.n_ranges ? walk.begin[0] : 0;  // cursor (range, tile)
+    TileRegs regs;
+    if (total > 0) {
+        load_tile_bf16(p, walk.run[0], ct, b, g, tid, regs);
+        store_tile_bf16(smem, tid, regs);
+    }
+    __syncthreads();
+
+    for (int f = 0; f < total; ++f) {
+        const int run_idx = walk.run[cr];
+        const int tile = ct;
+        // advance the cursor and prefetch the next tile
+        if (++ct >= walk.end[cr]) {
+            ++cr;
+            if (cr < walk.n_ranges) ct = walk.begin[cr];
+        }
+        const bool has_next = f + 1 < total;
+        if (has_next) load_tile_bf16(p, walk.run[cr], ct, b, g, tid, regs);
+
+        const KeyRun& run = p.runs[run_idx];
+        const int64_t row0 = (int64_t)tile * kBN;
+        const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
+        const int64_t j0 = run.pos0 + row0;
+        const int64_t j1 = j0 + nrows - 1;
+        const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j1, p.P, p.W);
+
+        const char* stage = smem + (f & 1) * kStageBytes;
+        const char* ks_lds = stage;
+        const char* vs_lds = stage + kKBytes;
+
+        // S^T = K Q^T for two blocks of 32 keys
+        f32x16 s[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk) {
+                const Vec16 a = *reinterpret_cast<const Vec16*>(ks_lds + (32 * mb + col) * kKStride + (8 * h + 16 * kk) * 2);
+                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[mb], 0, 0, 0);
+            }
+        }
+        // scale (log2 units) and mask
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                float x = s[mb][r] * p.scale_log2;
+                if (cls == kMasked) {
+                    const int kr = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int64_t j = j0 + kr;
+                    if (kr >= nrows || !visible(my_i, j, p.P, p.W)) x = -INFINITY;
+                }
+                s[mb][r] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float m_new = fmaxf(m_run, tmax);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        m_run = m_new;
+        float lsum = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float e = exp2f(s[mb][r] - m_use);
+                s[mb][r] = e;
+                lsum += e;
+            }
+        l_run = l_run * alpha + lsum;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
+
+        // P^T as B operand: k-step st covers keys 16 st .. 16 st + 15
+        Vec16 pb[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            const int mb = st >> 1, base = 8 * (st & 1);
+#pragma unroll
+            for (int w = 0; w < 4; ++w) pb[st].w[w] = pack_bf16x2(s[mb][base + 2 * w], s[mb][base + 2 * w + 1]);
+        }
+        // O^T += V^T P^T
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const char* vrow = vs_lds + (32 * m + col) * kVStride;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                Vec16 a;
+                const Vec8 lo = *reinterpret_cast<const Vec8*>(vrow + (16 * st + 4 * h) * 2);
+                const Vec8 hi = *reinterpret_cast<const Vec8*>(vrow + (16 * st + 8 + 4 * h) * 2);
+                a.w[0] = lo.w[0];
+                a.w[1] = lo.w[1];
+                a.w[2] = hi.w[0];
+                a.w[3] = hi.w[1];
+                o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), o[m], 0, 0, 0);
+            }
+        }
+
+        if (has_next) store_tile_bf16(smem + ((f + 1) & 1) * kStageBytes, tid, regs);
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!q_ok) return;
+    const float inv = 1.f / l_tot;
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b * p.seq_len + my_t) * p.hq + head) * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            Vec8 w;
+            w.w[0] = pack_bf16x2(o[m][4 * c] * inv, o[m][4 * c + 1] * inv);
+            w.w[1] = pack_bf16x2(o[m][4 * c + 2] * inv, o[m][4 * c + 3] * inv);
+            *reinterpret_cast<Vec8*>(op + 32 * m + 8 * c + 4 * h) = w;
+        }
+    if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run + log2f(l_tot)) * kLn2;
+}
+
+// ----------------------------------------------------------------- fp32 debug
+// One thread per query row of a 64-position tile of one q head; K/V tiles in
+// LDS; two passes per tile (scores for the tile maximum, then the weighted sum).
+template <int D>
+__global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
+    constexpr int BR = 32;  // rows staged per LDS fill (two fills per 64-key tile)
+    __shared__ float ks[BR][D];
+    __shared__ float vs[BR][D];
+    __shared__ TileWalk walk;
+    const int tid = threadIdx.x;
+    const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
+    const int group = p.hq / p.hkv;
+    const int g = head / group;
+    const int64_t t0 = (int64_t)qt * 64;
+    const int64_t t_last = (t0 + 64 < p.seq_len ? t0 + 64 : p.seq_len) - 1;
+    const int64_t i0 = p.start_pos + t0, i1 = p.start_pos + t_last;
+    const int64_t my_t = t0 + tid;
+    const bool q_ok = my_t < p.seq_len;
+    const int64_t my_i = p.start_pos + my_t;
+
+    float q[D], o[D];
+    const float* qp = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
+    for (int e = 0; e < D; ++e) {
+        q[e] = q_ok ? qp[e] * p.scale_log2 : 0.f;
+        o[e] = 0.f;
+    }
+    float m_run = -INFINITY, l_run = 0.f;
+
+    if (tid == 0) plan_walk(p, i0, i1, walk);
+    __syncthreads();
+    for (int rr = 0; rr < walk.n_ranges; ++rr) {
+        const KeyRun& run = p.runs[walk.run[rr]];
+        const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
+        const float* kb = reinterpret_cast<const float*>(run.k) + seq * run.seq_stride + (int64_t)g * run.head_stride;
+        const float* vb = reinterpret_cast<const float*>(run.v) + seq * run.seq_stride + (int64_t)g * run.head_stride;
+        for (int tile = walk.begin[rr]; tile < walk.end[rr]; ++tile) {
+            const int64_t row0 = (int64_t)tile * kBN;
+            const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
+            const int64_t j0 = run.pos0 + row0;
+            const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j0 + nrows - 1, p.P, p.W);
+            if (cls == kSkip) continue;
+            for (int pass = 0; pass < 2; ++pass) {
+                float tmax = -INFINITY;
+                for (int half = 0; half < kBN / BR; ++half) {
+                    __syncthreads();
+                    for (int idx = tid; idx < BR * D; idx += 64) {
+                        const int r = idx / D, e = idx % D;
+                        const int64_t row = half * BR + r;
+                        const bool ok = row < nrows;
+                        ks[r][e] = ok ? kb[(row0 + row) * run.row_stride + e] : 0.f;
+                        vs[r][e] = ok ? vb[(row0 + row) * run.row_stride + e] : 0.f;
+                    }
+                    __syncthreads();
+                    for (int r = 0; r < BR; ++r) {
+                        const int64_t row = half * BR + r;
+                        float acc = 0.f;
+                        for (int e = 0; e < D; ++e) acc = fmaf(q[e], ks[r][e], acc);
+                        if (cls == kMasked && (row >= nrows || !visible(my_i, j0 + row, p.P, p.W))) acc = -INFINITY;
+                        if (pass == 0) {
+                            tmax = fmaxf(tmax, acc);
+                        } else {
+                            const float w = exp2f(acc - (m_run == -INFINITY ? 0.f : m_run));
+                            l_run += w;
+                            for (int e = 0; e < D; ++e) o[e] = fmaf(w, vs[r][e], o[e]);
+                        }
+                    }
+                }
+                if (pass == 0) {
+                    const float m_new = fmaxf(m_run, tmax);
+                    const float alpha = exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+                    m_run = m_new;
+                    l_run *= alpha;
+                    for (int e = 0; e < D; ++e) o[e] *= alpha;
+                }
+            }
+        }
+    }
+    if (!q_ok) return;
+    float* op = reinterpret_cast<float*>(p.out) + (((int64_t)b * p.seq_len + my_t) * p.hq + head) * D;
+    for (int e = 0; e < D; ++e) op[e] = o[e] / l_run;
+    if (p.lse) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run + log2f(l_run)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p, hipStream_t stream) {
+    if (p.seq_len == 0) return hipSuccess;
+    if (dtype == PS_BF16) {
+        if (head_dim != 128) return hipErrorInvalidValue;
+        const int qp = 128 / group;
+        dim3 grid((unsigned)((p.seq_len + qp - 1) / qp), (unsigned)p.hkv, (unsigned)p.batch);
+        const size_t lds = 2 * kStageBytes;
+        switch (group) {
+            case 1:
+                hipFuncSetAttribute((const void*)prefill_bf16_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                hipLaunchKernelGGL(prefill_bf16_kernel<1>, grid, dim3(256), lds, stream, p);
+                break;
+            case 2:
+                hipFuncSetAttribute((const void*)prefill_bf16_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                hipLaunchKernelGGL(prefill_bf16_kernel<2>, grid, dim3(256), lds, stream, p);
+                break;
+            case 4:
+                hipFuncSetAttribute((const void*)prefill_bf16_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                hipLaunchKernelGGL(prefill_bf16_kernel<4>, grid, dim3(256), lds, stream, p);
+                break;
+            default:
+                return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
+    dim3 grid((unsigned)((p.seq_len + 63) / 64), (unsigned)p.hq, (unsigned)p.batch);
+    if (head_dim == 64)
+        hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, stream, p);
+    else if (head_dim == 128)
+        hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, stream, p);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+}  // namespace ps

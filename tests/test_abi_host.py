@@ -1,0 +1,132 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/ps.h declares, validates arguments before any device
+work, and its tile classifier (the closed form the prefill kernel uses)
+agrees with the oracle's exhaustive enumeration."""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+ps = pytest.importorskip("prefix_sliding_kv_amd")
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "ps.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ps_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = header_functions()
+    assert len(names) >= 12, names
+    for n in names:
+        assert hasattr(ps.lib, n), f"{n} declared in ps.h but not exported"
+    assert set(names) == set(ps.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert re.match(r"\d+\.\d+\.\d+", ps.ps_version())
+    for s in range(5):
+        assert ps.ps_status_str(s) != "unknown status"
+    assert ps.ps_status_str(99) == "unknown status"
+
+
+def test_tile_class_closed_form_matches_enumeration():
+    rng = random.Random(0)
+    cases = 0
+    for _ in range(3000):
+        P = rng.choice([0, 1, 3, 8, 20, 64])
+        W = rng.choice([1, 2, 5, 16, 40])
+        i0 = rng.randrange(0, 150)
+        i1 = i0 + rng.randrange(0, 12)
+        j0 = rng.randrange(0, 160)
+        j1 = j0 + rng.randrange(0, 12)
+        assert ps.ps_tile_class(i0, i1, j0, j1, P, W) == oracle.tile_class(i0, i1, j0, j1, P, W), \
+            (i0, i1, j0, j1, P, W)
+        cases += 1
+    # the pages' configurations, tile sizes of the kernel
+    for (P, W, start, T) in [(1024, 8192, 98304, 4096), (256, 2048, 0, 8192)]:
+        for i0 in range(start, start + T, 64 * 7):
+            for j0 in range(0, start + T, 64 * 13):
+                a = ps.ps_tile_class(i0, i0 + 63, j0, j0 + 63, P, W)
+                b = oracle.tile_class(i0, i0 + 63, j0, j0 + 63, P, W)
+                assert a == b
+                cases += 1
+    assert cases > 3000
+    assert ps.ps_tile_class(5, 4, 0, 0, 0, 1) == -1
+    assert ps.ps_tile_class(0, 1, 0, 0, 0, 0) == -1
+
+
+def _desc(**kw):
+    base = dict(n_layers=2, max_seqs=1, n_q_heads=16, n_kv_heads=8, head_dim=128, prefix_cap=100,
+                window=4096, dtype=ps.PS_BF16)
+    base.update(kw)
+    return ps.CacheDesc(**base)
+
+
+def test_cache_bytes_formula():
+    d = _desc()
+    kv = 2 * 1 * 8 * (100 + 4096) * 128 * 2  # per layer, K and V
+    assert ps.ps_cache_bytes(d) >= 2 * kv
+    assert ps.ps_cache_bytes(d) < 2 * kv + 8 * 1024 * 1024
+    for bad in [dict(window=0), dict(n_kv_heads=3), dict(prefix_cap=-1), dict(head_dim=96),
+                dict(dtype=7), dict(n_q_heads=24, n_kv_heads=8)]:
+        assert ps.ps_cache_bytes(_desc(**bad)) == 0, bad
+
+
+def _create(desc, ptr, nbytes):
+    h = ctypes.c_void_p()
+    return ps.lib.ps_cache_create(ctypes.byref(desc), ctypes.c_void_p(ptr), nbytes, None, ctypes.byref(h))
+
+
+def test_create_rejects_before_device_work():
+    d = _desc()
+    need = ps.ps_cache_bytes(d)
+    assert _create(_desc(window=0), 1 << 20, need) == ps.PS_ERR_INVALID
+    assert _create(_desc(head_dim=96), 1 << 20, need) == ps.PS_ERR_UNSUPPORTED
+    assert _create(d, 0, need) == ps.PS_ERR_INVALID
+    assert _create(d, (1 << 20) + 8, need) == ps.PS_ERR_INVALID  # misaligned
+    assert _create(d, 1 << 20, need - 1) == ps.PS_ERR_CAPACITY
+    assert ps.lib.ps_cache_create(ctypes.byref(d), ctypes.c_void_p(1 << 20), need, None, None) == \
+        ps.PS_ERR_INVALID
+
+
+def test_calls_reject_null_handles_and_args():
+    b = ps._SeqBatch(1, 0, 0, 0)
+    assert ps.lib.ps_kv_append_evict(None, 0, ctypes.byref(b), 1, None, None, None) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_decode_attn(None, 0, ctypes.byref(b), None, None, None, 1.0, None) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_decode_step(None, 0, ctypes.byref(b), None, None, None, None, None, 1.0, None) == \
+        ps.PS_ERR_INVALID
+    assert ps.lib.ps_prefill_attn(None, None) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_cache_kv(None, 0, None, None) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_cache_set_decode_split(None, 0) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_cache_destroy(None) == ps.PS_OK
+
+
+def _prefill_args(**kw):
+    a = dict(cache=0, layer=0, batch=1, seq_len=0, n_q_heads=16, n_kv_heads=8, head_dim=128,
+             dtype=ps.PS_BF16, start_pos=0, prefix_len=4, window=8, rows=0, q=0, k=0, v=0, out=0,
+             lse=0, scale=0.1)
+    a.update(kw)
+    return ps._PrefillArgs(**a)
+
+
+def test_prefill_validation():
+    call = lambda **kw: ps.lib.ps_prefill_attn(ctypes.byref(_prefill_args(**kw)), None)
+    assert call() == ps.PS_OK                                   # empty chunk: nothing to do
+    assert call(window=0) == ps.PS_ERR_INVALID
+    assert call(prefix_len=-1) == ps.PS_ERR_INVALID
+    assert call(start_pos=-1) == ps.PS_ERR_INVALID
+    assert call(batch=0) == ps.PS_ERR_INVALID
+    assert call(n_kv_heads=3) == ps.PS_ERR_INVALID
+    assert call(head_dim=96) == ps.PS_ERR_UNSUPPORTED
+    assert call(head_dim=64) == ps.PS_ERR_UNSUPPORTED          # bf16 MFMA path is d=128 only
+    assert call(dtype=5) == ps.PS_ERR_UNSUPPORTED
+    assert call(n_q_heads=64, n_kv_heads=8) == ps.PS_ERR_UNSUPPORTED  # GQA group 8 on the MFMA path
+    assert call(seq_len=4) == ps.PS_ERR_INVALID                # null tensors
+    assert call(scale=float("nan")) == ps.PS_ERR_INVALID
