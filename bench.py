@@ -1,0 +1,355 @@
+#!/usr/bin/env python3
+"""Benchmark of the Prefix Sliding attention hot path on one MI355X.
+
+A step is one decode token of the Qwen3-1.7B-shaped workload: for each of 28
+layers, one fused launch that appends the token's K/V to that layer's cache
+(prefix P=100 + 4096-slot ring, 128K-token trace) and runs split-K GQA
+decode attention with the in-kernel log-sum-exp combine.  Inputs (28
+distinct per-layer caches, 481 MB, and every step's q/k/v) are resident in
+HBM before timing starts.
+
+Printed as one JSON line (rank 0, N=1):
+  value        decode tok/s, HIP-graph replay of the 28-layer step
+  roofline     decode kernel: algorithmic bytes per launch / mean launch
+               duration from HIP events around each launch (eager pass)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+  prefill      chunked prefill (28 layers, P=1024, W=8192, 4096 queries at
+               98304..102399) and trainer forward (B=8, T=8192, P=256,
+               W=2048): TFLOP/s on exact visible pairs and on unskipped tiles
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode tok/s at Qwen3-1.7B shape, P=100 W=4096, 128K trace; % HBM peak"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+LAYERS, HQ, HKV, D, P, W = 28, 16, 8, 128, 100, 4096
+TRACE = 131072
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def bf16_dev(torch, a):
+    import numpy as np
+    return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def decode_bench(args, torch, ps, synth, np):
+    """Returns dict with eager/graph timings and the kernel roofline."""
+    seed, base = 0, 1e6
+    cache = ps.Cache(LAYERS, 1, HQ, HKV, D, P, W, ps.PS_BF16)
+    rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plen = torch.full((1,), P, dtype=torch.int32, device="cuda")
+    last = TRACE - 2  # positions 0..TRACE-2 are in the cache; step s decodes TRACE-1+s
+    pre = np.arange(0, P)
+    win = np.arange(last - W + 1, last + 1)
+    log("filling 28 layer caches (prefix + window of a 128K trace)")
+    for layer in range(LAYERS):
+        for pos in (pre, win):
+            k = synth.rows(seed, synth.K, layer, 0, pos, HKV, D, base)
+            v = synth.rows(seed, synth.V, layer, 0, pos, HKV, D)
+            b = ps.SeqBatch(rows, plen, torch.full((1,), int(pos[0]), dtype=torch.int64, device="cuda"))
+            ps.ps_kv_append_evict(cache.handle, layer, b, len(pos), bf16_dev(torch, k), bf16_dev(torch, v))
+    n_steps = args.warmup + args.steps
+    log(f"generating q/k/v for {n_steps} steps x 28 layers")
+    steps_pos = np.arange(TRACE - 1, TRACE - 1 + n_steps)
+    q_all, k_all, v_all = [], [], []
+    for layer in range(LAYERS):
+        q_all.append(bf16_dev(torch, synth.rows(seed, synth.Q, layer, 0, steps_pos, HQ, D, base)))
+        k_all.append(bf16_dev(torch, synth.rows(seed, synth.K, layer, 0, steps_pos, HKV, D, base)))
+        v_all.append(bf16_dev(torch, synth.rows(seed, synth.V, layer, 0, steps_pos, HKV, D)))
+    out = torch.empty(LAYERS, 1, HQ, D, device="cuda", dtype=torch.bfloat16)
+    pos_t = torch.full((1,), TRACE - 1, dtype=torch.int64, device="cuda")
+    batch = ps.SeqBatch(rows, plen, pos_t)
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+
+    def step(s, events=None):
+        for layer in range(LAYERS):
+            if events is not None:
+                events[layer][0].record(stream)
+            ps.ps_decode_step(cache.handle, layer, batch, q_all[layer][s:s + 1], k_all[layer][s:s + 1],
+                              v_all[layer][s:s + 1], out[layer], None, scale, stream)
+            if events is not None:
+                events[layer][1].record(stream)
+        pos_t.add_(1)
+
+    # eager: warmup, then timed steps with an event pair around every launch
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)] for _ in range(LAYERS)]
+          for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(args.warmup + s, ev[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = t_start.elapsed_time(t_end) / args.steps
+    launch_us = [ev[s][l][0].elapsed_time(ev[s][l][1]) * 1e3 for s in range(args.steps) for l in range(LAYERS)]
+    mean_launch_us = float(np.mean(launch_us))
+    log(f"eager: {eager_ms * 1e3:.1f} us/step, decode launch mean {mean_launch_us:.2f} us")
+
+    # graph: capture one 28-layer step (inputs of the last step slot), replay
+    pos_t.fill_(TRACE - 1)
+    gstream = torch.cuda.Stream()
+    gstream.wait_stream(stream)
+    graph = torch.cuda.CUDAGraph()
+    s_fixed = n_steps - 1
+    with torch.cuda.stream(gstream):
+        step_g = lambda: [ps.ps_decode_step(cache.handle, layer, batch, q_all[layer][s_fixed:s_fixed + 1],
+                                            k_all[layer][s_fixed:s_fixed + 1], v_all[layer][s_fixed:s_fixed + 1],
+                                            out[layer], None, scale, gstream) for layer in range(LAYERS)]
+        step_g()  # one eager run on the side stream before capture
+        pos_t.add_(1)
+        with torch.cuda.graph(graph, stream=gstream):
+            step_g()
+            pos_t.add_(1)
+    torch.cuda.synchronize()
+    # correctness of replay vs eager on the same position
+    pos_t.fill_(TRACE + 5)
+    for layer in range(LAYERS):
+        ps.ps_decode_step(cache.handle, layer, batch, q_all[layer][s_fixed:s_fixed + 1],
+                          k_all[layer][s_fixed:s_fixed + 1], v_all[layer][s_fixed:s_fixed + 1], out[layer], None,
+                          scale, stream)
+    torch.cuda.synchronize()
+    eager_out = out.clone()
+    pos_t.fill_(TRACE + 5)
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(eager_out.view(torch.int16), out.view(torch.int16)))
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = t_start.elapsed_time(t_end) / args.steps
+    log(f"graph: {graph_ms * 1e3:.1f} us/step (replay matches eager: {graph_ok})")
+
+    # flat cost: same caches, query positions before and after the window fills
+    flat = {}
+    for L in (1024, 2048, P + W, 8192, 32768, 131072):
+        pos_t.fill_(L - 1)
+        torch.cuda.synchronize()
+        reps = 20
+        t_start.record(stream)
+        for _ in range(reps):
+            for layer in range(LAYERS):
+                ps.ps_decode_attn(cache.handle, layer, batch, q_all[layer][:1], out[layer], None, scale, stream)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        flat[str(L)] = round(1e3 / (t_start.elapsed_time(t_end) / reps), 1)
+    log(f"flat cost tok/s by trace length (eager, attention only): {flat}")
+    cache.close()
+    return dict(eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok, mean_launch_us=mean_launch_us,
+                flat=flat)
+
+
+def tile_flops(ps, q_lo, q_hi, key_hi, P, Wn, hq, d, tile=64):
+    """Flops of unskipped 64x64 (query position, key position) tiles."""
+    n = 0
+    for i0 in range(q_lo, q_hi, tile):
+        i1 = min(i0 + tile, q_hi) - 1
+        for j0 in range(0, key_hi, tile):
+            j1 = min(j0 + tile, key_hi) - 1
+            if ps.ps_tile_class(i0, i1, j0, j1, P, Wn) != 0:
+                n += (i1 - i0 + 1) * (j1 - j0 + 1)
+    return 4.0 * d * hq * n
+
+
+def exact_flops(q_lo, q_hi, P, Wn, hq, d):
+    tot = 0
+    for i in range(q_lo, q_hi):
+        tot += min(i + 1, P + Wn)
+    return 4.0 * d * hq * tot
+
+
+def prefill_bench(torch, ps, synth, np):
+    res = {}
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    # chunked prefill: 28 layers, P=1024, W=8192, chunk 98304..102399
+    Pc, Wc, start, T = 1024, 8192, 98304, 4096
+    log("chunked prefill: filling caches")
+    cache = ps.Cache(LAYERS, 1, HQ, HKV, D, Pc, Wc, ps.PS_BF16)
+    rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    plen = torch.full((1,), Pc, dtype=torch.int32, device="cuda")
+    pre, win = np.arange(0, Pc), np.arange(start - Wc, start)
+    kv = []
+    for pos in (pre, win):
+        kv.append((bf16_dev(torch, synth.rows(0, synth.K, 0, 0, pos, HKV, D, 1e6)),
+                   bf16_dev(torch, synth.rows(0, synth.V, 0, 0, pos, HKV, D))))
+    for layer in range(LAYERS):  # same values in every layer (throughput does not depend on them)
+        for pos, (k, v) in zip((pre, win), kv):
+            b = ps.SeqBatch(rows, plen, torch.full((1,), int(pos[0]), dtype=torch.int64, device="cuda"))
+            ps.ps_kv_append_evict(cache.handle, layer, b, len(pos), k, v)
+    cpos = np.arange(start, start + T)
+    q = bf16_dev(torch, synth.rows(0, synth.Q, 0, 0, cpos, HQ, D, 1e6))[None]
+    k = bf16_dev(torch, synth.rows(0, synth.K, 0, 0, cpos, HKV, D, 1e6))[None]
+    v = bf16_dev(torch, synth.rows(0, synth.V, 0, 0, cpos, HKV, D))[None]
+    out = torch.empty_like(q)
+
+    def run():
+        for layer in range(LAYERS):
+            ps.ps_prefill_attn(q, k, v, out, start_pos=start, prefix_len=Pc, window=Wc, scale=scale,
+                               cache=cache.handle, layer=layer, rows=rows, stream=stream)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fx = exact_flops(start, start + T, Pc, Wc, HQ, D) * LAYERS
+    ft = tile_flops(ps, start, start + T, start + T, Pc, Wc, HQ, D) * LAYERS
+    res["chunked"] = {"workload": "28 layers, P=1024, W=8192, 4096 queries at 98304..102399, Hq=16, Hkv=8, d=128",
+                      "ms": round(ms, 3), "tflops_exact": round(fx / ms / 1e9, 1),
+                      "tflops_tiles": round(ft / ms / 1e9, 1),
+                      "frac_mfma_tiles": round(ft / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"chunked prefill: {res['chunked']}")
+    cache.close()
+    del q, k, v, out
+
+    # trainer forward: B=8, T=8192, P=256, W=2048
+    B, T, Pt, Wt = 8, 8192, 256, 2048
+    log("trainer forward: generating inputs")
+    pos = np.arange(T)
+    q = torch.stack([bf16_dev(torch, synth.rows(0, synth.Q, 0, b, pos, HQ, D, 1e6)) for b in range(B)])
+    k = torch.stack([bf16_dev(torch, synth.rows(0, synth.K, 0, b, pos, HKV, D, 1e6)) for b in range(B)])
+    v = torch.stack([bf16_dev(torch, synth.rows(0, synth.V, 0, b, pos, HKV, D)) for b in range(B)])
+    out = torch.empty_like(q)
+    run2 = lambda: ps.ps_prefill_attn(q, k, v, out, start_pos=0, prefix_len=Pt, window=Wt, scale=scale, stream=stream)
+    run2()
+    torch.cuda.synchronize()
+    reps = 10
+    e0.record(stream)
+    for _ in range(reps):
+        run2()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    fx = exact_flops(0, T, Pt, Wt, HQ, D) * B
+    ft = tile_flops(ps, 0, T, T, Pt, Wt, HQ, D) * B
+    res["trainer"] = {"workload": "B=8, T=8192 (6144 context + 2048), P=256, W=2048, Hq=16, Hkv=8, d=128",
+                      "ms": round(ms, 3), "tflops_exact": round(fx / ms / 1e9, 1),
+                      "tflops_tiles": round(ft / ms / 1e9, 1),
+                      "frac_mfma_tiles": round(ft / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"trainer forward: {res['trainer']}")
+    return res
+
+
+def cpu_baseline(np, seconds):
+    """The CPU oracle on a bounded sample: one decode token of the same
+    workload on `n_layers` layers, repeated until `seconds` elapse; scaled to
+    tok/s for all 28 layers."""
+    import oracle
+    import synth
+    threads = max(1, min(16, os.cpu_count() or 1))
+    n_layers = 2
+    i = TRACE - 1
+    kpos = oracle.retained_positions(i, P, W)
+    data = []
+    for layer in range(n_layers):
+        q = synth.bf16_bits_to_f32(synth.rows(0, synth.Q, layer, 0, [i], HQ, D, 1e6))
+        k = synth.bf16_bits_to_f32(synth.rows(0, synth.K, layer, 0, kpos, HKV, D, 1e6))
+        v = synth.bf16_bits_to_f32(synth.rows(0, synth.V, layer, 0, kpos, HKV, D))
+        data.append((q, k, v))
+    t0 = time.perf_counter()
+    reps = 0
+    while True:
+        for q, k, v in data:
+            oracle.attention(q, [i], k, v, kpos, P, W, 1.0 / math.sqrt(D), threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    per_layer = dt / (reps * n_layers)
+    return {"value": round(1.0 / (per_layer * LAYERS), 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"one decode token at position {i} (P=100, W=4096, Hq=16, Hkv=8, d=128) on {n_layers} "
+                      f"layers, oracle run {reps} times ({dt:.1f} s); tok/s scaled to 28 layers"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the decode path is per-GPU and "
+              f"needs no collectives", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import prefix_sliding_kv_amd as ps
+    import synth
+
+    torch.cuda.set_device(0)
+    dec = decode_bench(args, torch, ps, synth, np)
+    bytes_per_launch = 2 * HKV * D * (P + W) * 2
+    achieved = bytes_per_launch / (dec["mean_launch_us"] * 1e-6) / 1e9
+    step_ms = dec["graph_ms"] if dec["graph_ok"] else dec["eager_ms"]
+    value = 1e3 / step_ms
+    pre = {} if args.no_prefill else prefill_bench(torch, ps, synth, np)
+    cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), RoPE base 1e6 at Continue-PE positions)",
+        "config": {"workload": "decode, batch 1, 28 layers, Hq=16, Hkv=8, head_dim=128, P=100, W=4096, "
+                               "trace 128K; per layer one fused append/evict + split-K decode launch",
+                   "timing": "hipGraph replay of the 28-layer step" if dec["graph_ok"] else "eager launches",
+                   "layers": LAYERS, "batch": 1, "trace_len": TRACE, "prefix_len": P, "window": W},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<bf16,128,G=2> (fused append + attention + combine)",
+                     "bytes_per_launch": bytes_per_launch, "mean_launch_us": round(dec["mean_launch_us"], 3)},
+        "step_hbm_frac": round(bytes_per_launch * LAYERS / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "eager_tok_s": round(1e3 / dec["eager_ms"], 1),
+        "flat_cost_tok_s": dec["flat"],
+        "prefill": pre,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -44,7 +44,7 @@ Layout layout_of(const ps_cache_desc* d) {
     l.s_max = (int32_t)((l.rows_per_head + ps::kMinSplitRows - 1) / ps::kMinSplitRows);
     l.ws_o_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * d->head_dim * 4);
     l.ws_ml_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * 2 * 4);
-    l.ticket_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * 4);
+    l.ticket_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * ps::kTicketStride * 4);
     l.total = 2 * l.kv_bytes + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes;
     return l;
 }
@@ -55,26 +55,26 @@ bool batch_ok(const ps_cache* c, const ps_seq_batch* b) {
     return b && b->n >= 1 && b->n <= c->desc.max_seqs && b->rows && b->prefix_len && b->pos;
 }
 
-// Rows per decode split: the largest that still gives at least two
-// workgroups per CU (256 CUs), else the smallest allowed.
+// Rows per decode split.  A decode launch is short (tens of MB at batch 1),
+// so the split count per (sequence, kv head) also sets the length of the
+// merge the last split performs: take the largest split that still leaves
+// about one workgroup per CU (>= 128 workgroups of 16 waves), else the
+// smallest valid one.
 int auto_decode_rows(const ps_cache* c, int n_seqs) {
-    const int r1 = ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
-    int best = 0;
-    for (int u = 1; u <= 16; u *= 2) {
-        const int rows = r1 * u;
-        if (rows < ps::kMinSplitRows) continue;
-        if (best == 0) best = rows;
+    const int r = ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
+    const int cand[] = {128 * r, 64 * r, 32 * r, 16 * r, 8 * r, 4 * r};
+    int smallest = 0;
+    for (int rows : cand) {
+        if (!ps::decode_rows_valid(c->desc.dtype, c->desc.head_dim, rows)) continue;
+        smallest = rows;
         const int64_t splits = (c->rows_per_head + rows - 1) / rows;
-        if ((int64_t)n_seqs * c->desc.n_kv_heads * splits >= 512) best = rows;
+        if ((int64_t)n_seqs * c->desc.n_kv_heads * splits >= 128) return rows;
     }
-    return best;
+    return smallest;
 }
 
 bool decode_rows_ok(const ps_cache* c, int rows) {
-    const int r1 = ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
-    if (rows < ps::kMinSplitRows || rows % r1 != 0) return false;
-    const int u = rows / r1;
-    return u == 1 || u == 2 || u == 4 || u == 8 || u == 16;
+    return ps::decode_rows_valid(c->desc.dtype, c->desc.head_dim, rows);
 }
 
 int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const void* q, const void* knew,
@@ -141,7 +141,7 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
     c->tickets = reinterpret_cast<uint32_t*>(c->base + 2 * l.kv_bytes + l.ws_o_bytes + l.ws_ml_bytes);
     c->s_max = l.s_max;
     c->decode_rows = 0;
-    const hipError_t e = ps::launch_fill_u32(c->tickets, (size_t)desc->max_seqs * desc->n_kv_heads, 0u,
+    const hipError_t e = ps::launch_fill_u32(c->tickets, (size_t)desc->max_seqs * desc->n_kv_heads * ps::kTicketStride, 0u,
                                              (hipStream_t)stream);
     if (e != hipSuccess) {
         delete c;

@@ -29,8 +29,6 @@
 namespace ps {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / 64;
 constexpr float kLn2 = 0.6931471805599453f;
 
 struct alignas(16) Vec16 {
@@ -91,27 +89,56 @@ __device__ inline float group_sum(float x) {
 
 __device__ inline Vec16 load16(const void* p) { return *reinterpret_cast<const Vec16*>(p); }
 
-template <typename T, int D, int G, int U>
-__global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
+// Split partials cross workgroups that may sit on different XCDs (separate
+// L2s): they are written and read with agent-scope atomic accesses, which
+// the hardware keeps coherent across the device without cache maintenance.
+__device__ inline void store_coherent(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float load_coherent(const float* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge of two softmax partials (m in log2 units, l, o) into the first.
+template <int VEC>
+__device__ inline void merge_into(float& m, float& l, float* o, float m2, float l2, const float* o2) {
+    const float M = fmaxf(m, m2);
+    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float c = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
+    m = M;
+    l = a * l + c * l2;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = a * o[e] + c * o2[e];
+}
+
+template <typename T, int D, int G, int NW, int U>
+__global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
+    constexpr int NT = NW * 64;
     constexpr int VEC = Elem<T>::kPerVec;
     constexpr int LPR = D / VEC;          // lanes per key row
     constexpr int RPW = 64 / LPR;         // rows per wave per load instruction
-    constexpr int NG = kWaves * RPW;      // row groups per workgroup
-    constexpr int R = NG * U;             // rows per split
+    constexpr int R = NW * RPW * U;       // rows per split
+    constexpr int PAIRS = G * D;          // (head, dim) outputs of a group
     static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
 
-    __shared__ float s_m[NG][G];
-    __shared__ float s_l[NG][G];
-    __shared__ float s_o[NG][G][D];
+    __shared__ float s_m[NW][G];
+    __shared__ float s_l[NW][G];
+    __shared__ float s_o[NW][G][D];
     __shared__ int s_last;
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane % LPR, rg = lane / LPR;
-    const int gi = wave * RPW + rg;
 
+    // Metadata and queries first: independent loads, issued together.
     const int64_t P = p.plen[b];
     const int64_t i = p.pos[b];
+    const int64_t crow = p.rows[b];
+    Vec16 qraw[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+        qraw[hh] = load16(reinterpret_cast<const T*>(p.q) + ((int64_t)b * p.hq + g * G + hh) * D + sub * VEC);
+
     const int64_t n_pre = i + 1 < P ? i + 1 : P;
     int64_t n_ring = i - P + 1;
     n_ring = n_ring < 0 ? 0 : (n_ring > p.window ? (int64_t)p.window : n_ring);
@@ -119,54 +146,43 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
     const int nsplit = (int)((n + R - 1) / R);
     if (split >= nsplit) return;
 
-    const int64_t head_off = ((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head;
+    const int64_t head_off = (crow * p.hkv + g) * p.rows_per_head;
     const T* kbase = reinterpret_cast<const T*>(p.kc) + head_off * D;
     const T* vbase = reinterpret_cast<const T*>(p.vc) + head_off * D;
     const bool fused = p.knew != nullptr;
-    const int64_t new_phys = i < P ? i : p.pcap + (i - P) % p.window;
+    int64_t new_phys = i;
+    if (fused && i >= P) {
+        const int64_t off = i - P;
+        new_phys = p.pcap + (off < 0x7FFFFFFF ? (int64_t)((uint32_t)off % (uint32_t)p.window) : off % p.window);
+    }
     const T* knew_row = fused ? reinterpret_cast<const T*>(p.knew) + ((int64_t)b * p.hkv + g) * D : nullptr;
     const T* vnew_row = fused ? reinterpret_cast<const T*>(p.vnew) + ((int64_t)b * p.hkv + g) * D : nullptr;
 
-    // Issue every K/V load of this lane's rows first.
+    // Issue every K/V load of this lane's rows before any math.  Rows past
+    // the end are clamped to the last valid row (a harmless in-bounds read,
+    // no branch) and masked out of the softmax below.
     const int64_t r0 = (int64_t)split * R;
     Vec16 kr[U], vr[U];
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        const int64_t r = r0 + (int64_t)(wave * U + u) * RPW + rg;
+        int64_t r = r0 + (int64_t)(wave * U + u) * RPW + rg;
         valid[u] = r < n;
+        r = valid[u] ? r : n - 1;
         const int64_t phys = r < n_pre ? r : p.pcap + (r - n_pre);
-        const T* kp = kbase + phys * D;
-        const T* vp = vbase + phys * D;
-        if (fused && phys == new_phys) {
-            kp = knew_row;
-            vp = vnew_row;
-        }
-        if (valid[u]) {
-            kr[u] = load16(kp + sub * VEC);
-            vr[u] = load16(vp + sub * VEC);
-        } else {
-            kr[u] = Vec16{{0, 0, 0, 0}};
-            vr[u] = Vec16{{0, 0, 0, 0}};
-        }
+        const bool is_new = fused && phys == new_phys;
+        const T* kp = is_new ? knew_row : kbase + phys * D;
+        const T* vp = is_new ? vnew_row : vbase + phys * D;
+        kr[u] = load16(kp + sub * VEC);
+        vr[u] = load16(vp + sub * VEC);
     }
 
-    // Queries of the GQA group (pre-multiplied by scale * log2 e).
     float qf[G][VEC];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        const T* qp = reinterpret_cast<const T*>(p.q) + ((int64_t)b * p.hq + g * G + hh) * D + sub * VEC;
-        Elem<T>::unpack(load16(qp), qf[hh]);
+        Elem<T>::unpack(qraw[hh], qf[hh]);
 #pragma unroll
         for (int e = 0; e < VEC; ++e) qf[hh][e] *= p.scale_log2;
-    }
-
-    // The split that owns the new token's slot also commits it to the cache.
-    if (fused && split == 0 && tid < LPR) {
-        T* kd = const_cast<T*>(kbase) + new_phys * D + tid * VEC;
-        T* vd = const_cast<T*>(vbase) + new_phys * D + tid * VEC;
-        *reinterpret_cast<Vec16*>(kd) = load16(knew_row + tid * VEC);
-        *reinterpret_cast<Vec16*>(vd) = load16(vnew_row + tid * VEC);
     }
 
     // Scores (log2 units).
@@ -180,9 +196,21 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
             float acc = 0.f;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) acc = fmaf(qf[hh][e], kf[e], acc);
-            acc = group_sum<LPR>(acc);
-            s[u][hh] = valid[u] ? acc : -INFINITY;
+            s[u][hh] = acc;
         }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s[u][hh] = valid[u] ? group_sum<LPR>(s[u][hh]) : -INFINITY;
+
+    // The split that owns the new token's slot also commits it to the cache
+    // (after the loads above, so no wait on them is forced here).
+    if (fused && split == 0 && tid < LPR) {
+        T* kd = const_cast<T*>(kbase) + new_phys * D + tid * VEC;
+        T* vd = const_cast<T*>(vbase) + new_phys * D + tid * VEC;
+        *reinterpret_cast<Vec16*>(kd) = load16(knew_row + tid * VEC);
+        *reinterpret_cast<Vec16*>(vd) = load16(vnew_row + tid * VEC);
     }
 
     // Softmax over this row group's rows and weighted sum of values.
@@ -210,27 +238,42 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
         }
     }
 
-    // Merge the NG row groups of the workgroup through LDS.
+    // Merge the RPW row groups of each wave with lane exchanges, then the NW
+    // waves through LDS.
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
+    for (int mask = LPR; mask < 64; mask <<= 1) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) s_o[gi][hh][sub * VEC + e] = og[hh][e];
-        if (sub == 0) {
-            s_m[gi][hh] = mg[hh];
-            s_l[gi][hh] = lg[hh];
+        for (int hh = 0; hh < G; ++hh) {
+            const float m2 = __shfl_xor(mg[hh], mask, 64);
+            const float l2 = __shfl_xor(lg[hh], mask, 64);
+            float o2[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) o2[e] = __shfl_xor(og[hh][e], mask, 64);
+            merge_into<VEC>(mg[hh], lg[hh], og[hh], m2, l2, o2);
+        }
+    }
+    if (rg == 0) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s_o[wave][hh][sub * VEC + e] = og[hh][e];
+            if (sub == 0) {
+                s_m[wave][hh] = mg[hh];
+                s_l[wave][hh] = lg[hh];
+            }
         }
     }
     __syncthreads();
 
     const int64_t ws_head0 = (int64_t)b * p.hq + g * G;
-    for (int idx = tid; idx < G * D; idx += kThreads) {
+    for (int idx = tid; idx < PAIRS; idx += NT) {
         const int hh = idx / D, dim = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int k = 0; k < NG; ++k) M = fmaxf(M, s_m[k][hh]);
+        for (int k = 0; k < NW; ++k) M = fmaxf(M, s_m[k][hh]);
         float L = 0.f, O = 0.f;
 #pragma unroll
-        for (int k = 0; k < NG; ++k) {
+        for (int k = 0; k < NW; ++k) {
             const float w = s_m[k][hh] == -INFINITY ? 0.f : exp2f(s_m[k][hh] - M);
             L = fmaf(w, s_l[k][hh], L);
             O = fmaf(w, s_o[k][hh][dim], O);
@@ -241,82 +284,135 @@ __global__ void __launch_bounds__(kThreads) decode_kernel(DecodeParams p) {
             if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (M + log2f(L)) * kLn2;
         } else {
             const int64_t slot = (ws_head0 + hh) * p.s_max + split;
-            p.ws_o[slot * D + dim] = O;
+            store_coherent(p.ws_o + slot * D + dim, O);
             if (dim == 0) {
-                p.ws_ml[slot * 2] = M;
-                p.ws_ml[slot * 2 + 1] = L;
+                store_coherent(p.ws_ml + slot * 2, M);
+                store_coherent(p.ws_ml + slot * 2 + 1, L);
             }
         }
     }
     if (nsplit == 1) return;
 
     // Arrival counter: the last split of this (sequence, kv head) merges.
-    __threadfence();
+    // The partials travel through agent-coherent stores and loads, so the
+    // only ordering needed is "every store of this workgroup has completed
+    // before the counter moves": each wave waits for its stores to be
+    // acknowledged (stores count in vmcnt on CDNA), then the barrier.  A
+    // device-scope fence would instead write back and invalidate the XCD's
+    // whole L2 for every workgroup.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-        uint32_t* t = p.tickets + (int64_t)b * p.hkv + g;
-        const uint32_t prev = __hip_atomic_fetch_add(t, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t* t = p.tickets + ((int64_t)b * p.hkv + g) * kTicketStride;
+        const uint32_t prev = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (uint32_t)(nsplit - 1));
         if (s_last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!s_last) return;
-    __threadfence();
 
-    // Stage (m, l) of every split in LDS (reuse s_o: nsplit * G * 2 floats).
-    float* ml = &s_o[0][0][0];
-    constexpr int kMlCap = NG * G * D;
-    const bool staged = nsplit * G * 2 <= kMlCap;
-    if (staged) {
-        for (int idx = tid; idx < nsplit * G * 2; idx += kThreads) {
-            const int hh = idx / (nsplit * 2), rem = idx % (nsplit * 2);
-            ml[idx] = p.ws_ml[((ws_head0 + hh) * p.s_max) * 2 + rem];
+    // Merge the splits.  Thread t owns output (head, dim) = t % PAIRS and the
+    // splits part, part + PARTS, ... (part = t / PAIRS); it requests (m, l, o)
+    // of a whole batch of its splits before using any, so a batch costs one
+    // round trip.  The PARTS partial results meet in LDS.
+    constexpr int PARTS = NT >= PAIRS ? NT / PAIRS : 1;
+    constexpr int kBatch = 16;
+    __shared__ float red[PARTS > 1 ? PARTS * 3 * PAIRS : 1];  // [PARTS][3][PAIRS]
+    const int part = NT >= PAIRS ? tid / PAIRS : 0;
+    for (int pair = (NT >= PAIRS ? tid % PAIRS : tid); pair < PAIRS; pair += (NT >= PAIRS ? PAIRS : NT)) {
+        const int hh = pair / D, dim = pair % D;
+        const float* oh = p.ws_o + ((ws_head0 + hh) * p.s_max) * D + dim;
+        const float* mlh = p.ws_ml + ((ws_head0 + hh) * p.s_max) * 2;
+        float M = -INFINITY, L = 0.f, O = 0.f;
+        for (int s0 = part; s0 < nsplit; s0 += kBatch * PARTS) {
+            float bm[kBatch], bl[kBatch], bo[kBatch];
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const int sidx = s0 + j * PARTS;
+                const bool ok = sidx < nsplit;
+                const int sc = ok ? sidx : s0;
+                bm[j] = load_coherent(mlh + 2 * sc);
+                bl[j] = load_coherent(mlh + 2 * sc + 1);
+                bo[j] = load_coherent(oh + (int64_t)sc * D);
+                if (!ok) bm[j] = -INFINITY;
+            }
+            float bM = M;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) bM = fmaxf(bM, bm[j]);
+            const float a = M == -INFINITY ? 0.f : exp2f(M - bM);
+            L *= a;
+            O *= a;
+#pragma unroll
+            for (int j = 0; j < kBatch; ++j) {
+                const float w = bm[j] == -INFINITY ? 0.f : exp2f(bm[j] - bM);
+                L = fmaf(w, bl[j], L);
+                O = fmaf(w, bo[j], O);
+            }
+            M = bM;
+        }
+        if constexpr (PARTS > 1) {
+            red[(part * 3 + 0) * PAIRS + pair] = M;
+            red[(part * 3 + 1) * PAIRS + pair] = L;
+            red[(part * 3 + 2) * PAIRS + pair] = O;
+        }
+        if constexpr (PARTS == 1) {
+            T* o = reinterpret_cast<T*>(p.out) + (ws_head0 + hh) * D + dim;
+            *o = Elem<T>::from_float(O / L);
+            if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (M + log2f(L)) * kLn2;
         }
     }
-    __syncthreads();
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int hh = idx / D, dim = idx % D;
-        const float* mlh = staged ? ml + hh * nsplit * 2 : p.ws_ml + ((ws_head0 + hh) * p.s_max) * 2;
-        float M = -INFINITY;
-        for (int sidx = 0; sidx < nsplit; ++sidx) M = fmaxf(M, mlh[2 * sidx]);
-        float L = 0.f, O = 0.f;
-        const float* oh = p.ws_o + ((ws_head0 + hh) * p.s_max) * D + dim;
-        for (int sidx = 0; sidx < nsplit; ++sidx) {
-            const float w = exp2f(mlh[2 * sidx] - M);
-            L = fmaf(w, mlh[2 * sidx + 1], L);
-            O = fmaf(w, oh[(int64_t)sidx * D], O);
+    if constexpr (PARTS > 1) {
+        __syncthreads();
+        if (tid < PAIRS) {
+            const int pair = tid, hh = pair / D, dim = pair % D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int k = 0; k < PARTS; ++k) M = fmaxf(M, red[(k * 3) * PAIRS + pair]);
+            float L = 0.f, O = 0.f;
+#pragma unroll
+            for (int k = 0; k < PARTS; ++k) {
+                const float mk = red[(k * 3) * PAIRS + pair];
+                const float w = mk == -INFINITY ? 0.f : exp2f(mk - M);
+                L = fmaf(w, red[(k * 3 + 1) * PAIRS + pair], L);
+                O = fmaf(w, red[(k * 3 + 2) * PAIRS + pair], O);
+            }
+            T* o = reinterpret_cast<T*>(p.out) + (ws_head0 + hh) * D + dim;
+            *o = Elem<T>::from_float(O / L);
+            if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (M + log2f(L)) * kLn2;
         }
-        T* o = reinterpret_cast<T*>(p.out) + (ws_head0 + hh) * D + dim;
-        *o = Elem<T>::from_float(O / L);
-        if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (M + log2f(L)) * kLn2;
     }
 }
 
-template <typename T, int D, int G>
-hipError_t dispatch_u(int u, const DecodeParams& p, hipStream_t stream) {
-    constexpr int VEC = Elem<T>::kPerVec;
-    constexpr int R1 = kWaves * (64 / (D / VEC));
-    dim3 block(kThreads);
-    const int rows = (int)p.rows_per_head;
-    auto grid_for = [&](int R) { return dim3((unsigned)((rows + R - 1) / R), (unsigned)p.hkv, (unsigned)p.n_seqs); };
-    switch (u) {
-        case 1: hipLaunchKernelGGL((decode_kernel<T, D, G, 1>), grid_for(R1), block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<T, D, G, 2>), grid_for(2 * R1), block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<T, D, G, 4>), grid_for(4 * R1), block, 0, stream, p); break;
-        case 8: hipLaunchKernelGGL((decode_kernel<T, D, G, 8>), grid_for(8 * R1), block, 0, stream, p); break;
-        case 16: hipLaunchKernelGGL((decode_kernel<T, D, G, 16>), grid_for(16 * R1), block, 0, stream, p); break;
-        default: return hipErrorInvalidValue;
-    }
+template <typename T, int D, int G, int NW, int U>
+hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
+    constexpr int R = NW * (64 / (D / Elem<T>::kPerVec)) * U;
+    const dim3 grid((unsigned)((p.rows_per_head + R - 1) / R), (unsigned)p.hkv, (unsigned)p.n_seqs);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U>), grid, dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
+// rows_per_split = NW * RPW * U: four waves for the two smallest sizes,
+// sixteen waves (short per-lane row chains, few splits) above.
+template <typename T, int D, int G>
+hipError_t dispatch_rows(int rows, const DecodeParams& p, hipStream_t stream) {
+    constexpr int RPW = 64 / (D / Elem<T>::kPerVec);
+    const int r4 = 4 * RPW, r16 = 16 * RPW;
+    if (rows == r4) return launch_one<T, D, G, 4, 1>(p, stream);
+    if (rows == 2 * r4) return launch_one<T, D, G, 4, 2>(p, stream);
+    if (rows == r16) return launch_one<T, D, G, 16, 1>(p, stream);
+    if (rows == 2 * r16) return launch_one<T, D, G, 16, 2>(p, stream);
+    if (rows == 4 * r16) return launch_one<T, D, G, 16, 4>(p, stream);
+    if (rows == 8 * r16) return launch_one<T, D, G, 16, 8>(p, stream);
+    return hipErrorInvalidValue;
+}
+
 template <typename T, int D>
-hipError_t dispatch_g(int group, int u, const DecodeParams& p, hipStream_t stream) {
+hipError_t dispatch_g(int group, int rows, const DecodeParams& p, hipStream_t stream) {
     switch (group) {
-        case 1: return dispatch_u<T, D, 1>(u, p, stream);
-        case 2: return dispatch_u<T, D, 2>(u, p, stream);
-        case 4: return dispatch_u<T, D, 4>(u, p, stream);
-        case 8: return dispatch_u<T, D, 8>(u, p, stream);
+        case 1: return dispatch_rows<T, D, 1>(rows, p, stream);
+        case 2: return dispatch_rows<T, D, 2>(rows, p, stream);
+        case 4: return dispatch_rows<T, D, 4>(rows, p, stream);
+        case 8: return dispatch_rows<T, D, 8>(rows, p, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -325,20 +421,25 @@ hipError_t dispatch_g(int group, int u, const DecodeParams& p, hipStream_t strea
 
 int decode_rows_per_load(int dtype, int head_dim) {
     const int vec = dtype == PS_BF16 ? 8 : 4;
-    return kWaves * (64 / (head_dim / vec));
+    return 64 / (head_dim / vec);  // rows one wave covers per load instruction
+}
+
+bool decode_rows_valid(int dtype, int head_dim, int rows) {
+    const int rpw = decode_rows_per_load(dtype, head_dim);
+    const int r4 = 4 * rpw, r16 = 16 * rpw;
+    if (rows < kMinSplitRows) return false;
+    return rows == r4 || rows == 2 * r4 || rows == r16 || rows == 2 * r16 || rows == 4 * r16 || rows == 8 * r16;
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split, const DecodeParams& p,
                          hipStream_t stream) {
-    const int r1 = decode_rows_per_load(dtype, head_dim);
-    if (rows_per_split % r1 != 0) return hipErrorInvalidValue;
-    const int u = rows_per_split / r1;
+    if (!decode_rows_valid(dtype, head_dim, rows_per_split)) return hipErrorInvalidValue;
     if (dtype == PS_BF16) {
-        if (head_dim == 128) return dispatch_g<uint16_t, 128>(group, u, p, stream);
-        if (head_dim == 64) return dispatch_g<uint16_t, 64>(group, u, p, stream);
+        if (head_dim == 128) return dispatch_g<uint16_t, 128>(group, rows_per_split, p, stream);
+        if (head_dim == 64) return dispatch_g<uint16_t, 64>(group, rows_per_split, p, stream);
     } else {
-        if (head_dim == 128) return dispatch_g<float, 128>(group, u, p, stream);
-        if (head_dim == 64) return dispatch_g<float, 64>(group, u, p, stream);
+        if (head_dim == 128) return dispatch_g<float, 128>(group, rows_per_split, p, stream);
+        if (head_dim == 64) return dispatch_g<float, 64>(group, rows_per_split, p, stream);
     }
     return hipErrorInvalidValue;
 }

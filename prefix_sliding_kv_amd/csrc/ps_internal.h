@@ -19,7 +19,7 @@ struct ps_cache {
     char* v_region = nullptr;
     float* ws_o = nullptr;       // [max_seqs][Hq][s_max][d]  unnormalised partial outputs
     float* ws_ml = nullptr;      // [max_seqs][Hq][s_max][2]  (running max in log2 units, sum)
-    uint32_t* tickets = nullptr; // [max_seqs][Hkv] arrival counters (self-resetting)
+    uint32_t* tickets = nullptr; // [max_seqs][Hkv] arrival counters, one per 256-byte line (self-resetting)
     int32_t s_max = 0;           // split slots per (seq, q head) in the workspace
     int32_t decode_rows = 0;     // requested rows per split, 0 = automatic
 };
@@ -27,6 +27,7 @@ struct ps_cache {
 namespace ps {
 
 constexpr int kMinSplitRows = 16;  // smallest rows-per-split the workspace is sized for
+constexpr int kTicketStride = 64;  // u32 words between arrival counters: one counter per 256-byte line
 
 // Visibility of key position j to query position i (prefix + window, causal).
 __host__ __device__ inline bool visible(int64_t i, int64_t j, int64_t P, int64_t W) {
@@ -77,9 +78,11 @@ struct DecodeParams {
 // Launch decode attention; rows_per_split chosen by the caller (host).
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split,
                          const DecodeParams& p, hipStream_t stream);
-// Valid rows-per-split values for a (dtype, head_dim): rows_per_split must equal
-// 4 waves * rows-per-wave-load * U with U in {1,2,4,8,16}.
+// Rows one wave covers per 16-byte load instruction for (dtype, head_dim).
 int decode_rows_per_load(int dtype, int head_dim);
+// Split sizes the decode kernel is built for: with r = decode_rows_per_load,
+// 4r and 8r (four waves) and 16r, 32r, 64r, 128r (sixteen waves), each >= 16.
+bool decode_rows_valid(int dtype, int head_dim, int rows);
 
 // ------------------------------------------------------------ append
 struct AppendParams {
