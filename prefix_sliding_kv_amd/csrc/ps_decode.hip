@@ -47,6 +47,19 @@ struct Elem<uint16_t> {  // bfloat16 storage
             f[2 * i + 1] = __uint_as_float(v.w[i] & 0xFFFF0000u);
         }
     }
+    // 8-element dot product: packed bf16 pairs, products exact, fp32 sums
+    __device__ static inline float dot(const Vec16& a, const Vec16& b) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16x2 x, y;
+            __builtin_memcpy(&x, &a.w[i], 4);
+            __builtin_memcpy(&y, &b.w[i], 4);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(x, y, acc, false);
+        }
+        return acc;
+    }
     __device__ static inline uint16_t from_float(float x) {
         // round to nearest even; NaN stays NaN
         uint32_t u = __float_as_uint(x);
@@ -61,6 +74,12 @@ struct Elem<float> {
     __device__ static inline void unpack(const Vec16& v, float* f) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) f[i] = __uint_as_float(v.w[i]);
+    }
+    __device__ static inline float dot(const Vec16& a, const Vec16& b) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc = fmaf(__uint_as_float(a.w[i]), __uint_as_float(b.w[i]), acc);
+        return acc;
     }
     __device__ static inline float from_float(float x) { return x; }
 };
@@ -177,32 +196,20 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         vr[u] = load16(vp + sub * VEC);
     }
 
-    float qf[G][VEC];
-#pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-        Elem<T>::unpack(qraw[hh], qf[hh]);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) qf[hh][e] *= p.scale_log2;
-    }
-
-    // Scores (log2 units).
+    // Scores (log2 units): q.k over this lane's slice, summed over the row's
+    // lanes, then scaled.
     float s[U][G];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-        float kf[VEC];
-        Elem<T>::unpack(kr[u], kf);
-#pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            float acc = 0.f;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc = fmaf(qf[hh][e], kf[e], acc);
-            s[u][hh] = acc;
-        }
-    }
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) s[u][hh] = valid[u] ? group_sum<LPR>(s[u][hh]) : -INFINITY;
+        for (int hh = 0; hh < G; ++hh) s[u][hh] = Elem<T>::dot(qraw[hh], kr[u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+            const float t = group_sum<LPR>(s[u][hh]) * p.scale_log2;
+            s[u][hh] = valid[u] ? t : -INFINITY;
+        }
 
     // The split that owns the new token's slot also commits it to the cache
     // (after the loads above, so no wait on them is forced here).
