@@ -113,9 +113,10 @@ int ps_cache_destroy(ps_cache* cache);
 int ps_cache_kv(const ps_cache* cache, int32_t layer, void** k, void** v);
 
 /* Split-K granularity of decode: rows (keys) handled per workgroup.  0 picks
- * automatically (default); otherwise one of 16, 32, 64, 128, 256 for bf16
- * head_dim 128 (the set scales with row size).  Errors: PS_ERR_INVALID,
- * PS_ERR_UNSUPPORTED. */
+ * automatically (default); otherwise one of 16, 32, 64, 128, 256, 512 for
+ * bf16 head_dim 128 and fp32 head_dim 64 (32..1024 for bf16 head_dim 64,
+ * 16..256 for fp32 head_dim 128).  Errors: PS_ERR_INVALID (NULL, negative),
+ * PS_ERR_UNSUPPORTED (a size the kernel is not built for). */
 int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
 
 /* Append n_new consecutive tokens per sequence to layer `layer`: token t of
@@ -195,8 +196,13 @@ typedef struct {
     const void* v;          /* device [B][T][n_kv_heads][head_dim] */
     void* out;              /* device [B][T][n_q_heads][head_dim] */
     float* lse;             /* device [B][T][n_q_heads] natural log, or NULL */
-    float scale;            /* multiplier of q.k */
+    float scale;            /* multiplier of q.k, > 0 */
 } ps_prefill_args;
+
+/* Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,
+ * scale <= 0 or not finite), PS_ERR_UNSUPPORTED (head_dim other than 128 for
+ * bf16, GQA group other than 1, 2 or 4 for bf16, a chunk reaching position
+ * 2^31), PS_ERR_HIP. */
 
 int ps_prefill_attn(const ps_prefill_args* args, void* stream);
 

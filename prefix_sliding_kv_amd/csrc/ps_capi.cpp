@@ -208,7 +208,9 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     if (!a) return PS_ERR_INVALID;
     if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1)
         return PS_ERR_INVALID;
-    if (!isfinite(a->scale)) return PS_ERR_INVALID;
+    if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
+    // positions are handled as 32-bit tile-relative offsets inside the kernel
+    if (a->start_pos + (int64_t)a->seq_len >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
     int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim, dtype = a->dtype;
     const ps_cache* c = a->cache;
     if (c) {

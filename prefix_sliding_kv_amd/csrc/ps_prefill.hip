@@ -82,6 +82,16 @@ __device__ inline void plan_walk(const PrefillParams& p, int64_t i0, int64_t i1,
 }
 
 // ----------------------------------------------------------------- bf16 MFMA
+constexpr int kXcds = 8;
+
+// Bijection from the dispatch-order id to a work index such that the ids an
+// XCD receives (id % 8 == x) map to one contiguous block of work indices.
+__device__ inline int xcd_remap(int id, int n) {
+    const int q = n / kXcds, r = n % kXcds;
+    const int x = id % kXcds, slot = id / kXcds;
+    return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+}
+
 constexpr int kKStride = 128 * 2 + 16;  // bytes per K row in LDS (padded)
 constexpr int kVStride = kBN * 2 + 8;   // bytes per transposed V row (one dim) in LDS
 constexpr int kKBytes = kBN * kKStride;
@@ -160,7 +170,13 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = lane >> 5, col = lane & 31;
-    const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    // Workgroups are dealt to the 8 XCDs round-robin by linear id; give each
+    // XCD a contiguous run of (sequence, kv head, q tile) work so the
+    // workgroups sharing an L2 walk neighbouring q tiles of the same head,
+    // whose key windows overlap almost entirely.
+    const int n_qt = (p.seq_len + QP - 1) / QP;
+    const int work = xcd_remap((int)blockIdx.x, n_qt * p.hkv * p.batch);
+    const int qt = work % n_qt, g = (work / n_qt) % p.hkv, b = work / (n_qt * p.hkv);
     const int hw = (wave * 32) / QP;           // head within the group
     const int pw = (wave * 32) % QP;           // position offset of this wave
     const int head = g * G + hw;
@@ -172,6 +188,8 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
     const int64_t my_t = t0 + pw + col;
     const bool q_ok = my_t < p.seq_len;
     const int64_t my_i = p.start_pos + my_t;
+    const float c = p.scale_log2;                              // > 0 (checked on the host)
+    const int w32 = p.W > (1 << 30) ? (1 << 30) : (int)p.W;    // a window beyond every position is the same
 
     // Q of this lane's query (B operand): dims 8h + 16ks .. +8
     Vec16 qreg[8];
@@ -217,7 +235,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
 
         const KeyRun& run = p.runs[run_idx];
         const int64_t row0 = (int64_t)tile * kBN;
-        const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
+        const int nrows = (int)(run.n - row0 < kBN ? run.n - row0 : kBN);
         const int64_t j0 = run.pos0 + row0;
         const int64_t j1 = j0 + nrows - 1;
         const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j1, p.P, p.W);
@@ -226,7 +244,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
         const char* ks_lds = stage;
         const char* vs_lds = stage + kKBytes;
 
-        // S^T = K Q^T for two blocks of 32 keys
+        // S^T = K Q^T for two blocks of 32 keys (raw scores, unscaled)
         f32x16 s[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
@@ -238,40 +256,51 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
                 s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[mb], 0, 0, 0);
             }
         }
-        // scale (log2 units) and mask
+        // Elementwise mask, straddling tiles only.  Positions are tile-relative
+        // 32-bit values: key kr of the tile is visible to this lane's query iff
+        // kr <= rel and (kr < pj or kr > rel - W), rel = i - j0, pj = P - j0.
+        if (cls == kMasked) {
+            const int rel = (int)(my_i - j0);
+            const int64_t pj64 = p.P - j0;
+            const int pj = pj64 > (1 << 30) ? (1 << 30) : (pj64 < -(1 << 30) ? -(1 << 30) : (int)pj64);
+            const int relw = rel - w32;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kr = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool vis = kr < nrows && kr <= rel && (kr < pj || kr > relw);
+                    s[mb][r] = vis ? s[mb][r] : -INFINITY;
+                }
+        }
+        // online softmax in raw-score units; exp2((s - m) * c) as one FMA + exp
         float tmax = -INFINITY;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                float x = s[mb][r] * p.scale_log2;
-                if (cls == kMasked) {
-                    const int kr = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int64_t j = j0 + kr;
-                    if (kr >= nrows || !visible(my_i, j, p.P, p.W)) x = -INFINITY;
-                }
-                s[mb][r] = x;
-                tmax = fmaxf(tmax, x);
-            }
+            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float m_new = fmaxf(m_run, tmax);
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float mc = m_new == -INFINITY ? 0.f : m_new * c;
+        if (__any(m_new > m_run)) {  // rescale only when some row's max rose
+            const float alpha = exp2f(fmaf(m_run, c, -mc));
+            l_run *= alpha;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
+        }
         m_run = m_new;
         float lsum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = exp2f(s[mb][r] - m_use);
+                const float e = exp2f(fmaf(s[mb][r], c, -mc));
                 s[mb][r] = e;
                 lsum += e;
             }
-        l_run = l_run * alpha + lsum;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
+        l_run += lsum;
 
         // P^T as B operand: k-step st covers keys 16 st .. 16 st + 15
         Vec16 pb[4];
@@ -315,7 +344,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
             w.w[1] = pack_bf16x2(o[m][4 * c + 2] * inv, o[m][4 * c + 3] * inv);
             *reinterpret_cast<Vec8*>(op + 32 * m + 8 * c + 4 * h) = w;
         }
-    if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run + log2f(l_tot)) * kLn2;
+    if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run * c + log2f(l_tot)) * kLn2;
 }
 
 // ----------------------------------------------------------------- fp32 debug
@@ -408,7 +437,7 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
     if (dtype == PS_BF16) {
         if (head_dim != 128) return hipErrorInvalidValue;
         const int qp = 128 / group;
-        dim3 grid((unsigned)((p.seq_len + qp - 1) / qp), (unsigned)p.hkv, (unsigned)p.batch);
+        dim3 grid((unsigned)(((p.seq_len + qp - 1) / qp) * p.hkv * p.batch));
         const size_t lds = 2 * kStageBytes;
         switch (group) {
             case 1:

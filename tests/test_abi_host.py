@@ -130,3 +130,6 @@ def test_prefill_validation():
     assert call(n_q_heads=64, n_kv_heads=8) == ps.PS_ERR_UNSUPPORTED  # GQA group 8 on the MFMA path
     assert call(seq_len=4) == ps.PS_ERR_INVALID                # null tensors
     assert call(scale=float("nan")) == ps.PS_ERR_INVALID
+    assert call(scale=0.0) == ps.PS_ERR_INVALID
+    assert call(scale=-0.1) == ps.PS_ERR_INVALID
+    assert call(start_pos=2**31 - 2, seq_len=4) == ps.PS_ERR_UNSUPPORTED  # positions are 32-bit in the kernel
