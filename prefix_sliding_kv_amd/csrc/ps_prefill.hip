@@ -92,51 +92,73 @@ __device__ inline int xcd_remap(int id, int n) {
     return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
 }
 
-constexpr int kKStride = 128 * 2 + 16;  // bytes per K row in LDS (padded)
-constexpr int kVStride = kBN * 2 + 8;   // bytes per transposed V row (one dim) in LDS
+constexpr int kKStride = 128 * 2;       // bytes per K row in LDS; 16-byte chunks xor-swizzled by row & 15
+constexpr int kVStride = kBN * 2;       // bytes per transposed V row (one head dimension), unpadded
 constexpr int kKBytes = kBN * kKStride;
 constexpr int kVBytes = 128 * kVStride;
 constexpr int kStageBytes = kKBytes + kVBytes;
 
+// Transposed V layout.  Row = head dimension, 64 keys of 2 bytes.  Keys are
+// stored in the order the P.V MFMA consumes them: the 8 keys lane half h
+// needs for k-step st (keys 16st + 8a + 4h + c, a, c in {0,1},{0..3}) sit in
+// columns 16st + 8h + 4a + c, i.e. key bits 2 and 3 swapped, so one 16-byte
+// read fetches them.  The 16-byte chunk of a row is xor-swizzled by
+// ((row >> 3) ^ row) & 7 so that both the staging writes and the operand
+// reads hit all LDS banks once.
+__device__ inline int vt_chunk_swz(int row) { return ((row >> 3) ^ row) & 7; }
+__device__ inline int swap01(int x) { return (x & ~3) | ((x & 1) << 1) | ((x >> 1) & 1); }
+// staging thread -> (dim group 0..15, key group 0..15) for V
+__device__ inline int v_dim_group(int t) { return (t & 7) | (((t >> 4) & 1) << 3); }
+__device__ inline int v_key_group(int t) { return (((t >> 3) & 1) << 1) | ((t >> 5) & 1) | ((t >> 6) << 2); }
+
+__device__ inline int k_chunk_swz(int row) { return row & 15; }
+
 struct TileRegs {
-    Vec16 k[4];
     Vec16 v[4];
 };
 
+// Stage one 64-key tile: K goes straight from global memory into LDS
+// (global_load_lds, 16 bytes per lane at LDS base + lane * 16; each lane picks
+// the global chunk that belongs at its swizzled LDS position), V is loaded to
+// registers for the transposed store.  Rows past the end of the run are
+// clamped to its last row for K (those keys are masked) and zero for V.
 __device__ inline void load_tile_bf16(const PrefillParams& p, int run_idx, int tile, int b, int g, int tid,
-                                      TileRegs& t) {
+                                      char* stage, TileRegs& t) {
     const KeyRun& run = p.runs[run_idx];
     const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
-    const char* kb = static_cast<const char*>(run.k) + (seq * run.seq_stride + (int64_t)g * run.head_stride) * 2;
-    const char* vb = static_cast<const char*>(run.v) + (seq * run.seq_stride + (int64_t)g * run.head_stride) * 2;
     const int64_t row0 = (int64_t)tile * kBN;
-    const int piece = tid & 15;
+    const char* kb = static_cast<const char*>(run.k) + (seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride) * 2;
+    const char* vb = static_cast<const char*>(run.v) + (seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride) * 2;
+    const int64_t rs = run.row_stride * 2;
+    const int nrows = run.n - row0 < kBN ? (int)(run.n - row0) : kBN;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // K: rows tid/16 + 16 i, 16-byte piece tid%16
-        const int64_t rk = row0 + (tid >> 4) + 16 * i;
-        if (rk < run.n)
-            t.k[i] = *reinterpret_cast<const Vec16*>(kb + (rk * run.row_stride) * 2 + piece * 16);
-        else
-            t.k[i] = Vec16{{0, 0, 0, 0}};
-        // V: rows 4*(tid/16) + i, dims 8*(tid%16) .. +8
-        const int64_t rv = row0 + 4 * (tid >> 4) + i;
-        if (rv < run.n)
-            t.v[i] = *reinterpret_cast<const Vec16*>(vb + (rv * run.row_stride) * 2 + piece * 16);
-        else
-            t.v[i] = Vec16{{0, 0, 0, 0}};
+        const int row = 16 * wave + 4 * i + (lane >> 4);
+        const int src_row = row < nrows ? row : nrows - 1;
+        const int chunk = (lane & 15) ^ k_chunk_swz(row);
+        __builtin_amdgcn_global_load_lds(kb + src_row * rs + chunk * 16,
+                                         (__attribute__((address_space(3))) void*)(stage + (16 * wave + 4 * i) * kKStride),
+                                         16, 0, 0);
+    }
+    const int vpiece = v_dim_group(tid), vrow = 4 * v_key_group(tid);
+    if (nrows == kBN) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) t.v[i] = *reinterpret_cast<const Vec16*>(vb + (vrow + i) * rs + vpiece * 16);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            t.v[i] = vrow + i < nrows ? *reinterpret_cast<const Vec16*>(vb + (vrow + i) * rs + vpiece * 16)
+                                      : Vec16{{0, 0, 0, 0}};
     }
 }
 
 __device__ inline void store_tile_bf16(char* stage, int tid, const TileRegs& t) {
-    char* ks = stage;
     char* vs = stage + kKBytes;
-    const int piece = tid & 15;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<Vec16*>(ks + ((tid >> 4) + 16 * i) * kKStride + piece * 16) = t.k[i];
-    // transpose: dims 8*piece+e, keys 4*(tid/16) .. +4
-    const int kg = tid >> 4;
+    // transpose: this thread holds keys 4kg..4kg+3 of dims 8dg..8dg+7
+    const int dg = v_dim_group(tid);
+    const int col = 4 * swap01(v_key_group(tid));  // permuted key column of the 4 keys
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int w = e >> 1;
@@ -144,7 +166,8 @@ __device__ inline void store_tile_bf16(char* stage, int tid, const TileRegs& t) 
         Vec8 o;
         o.w[0] = __builtin_amdgcn_perm(t.v[1].w[w], t.v[0].w[w], sel);
         o.w[1] = __builtin_amdgcn_perm(t.v[3].w[w], t.v[2].w[w], sel);
-        *reinterpret_cast<Vec8*>(vs + (8 * piece + e) * kVStride + kg * 8) = o;
+        const int row = 8 * dg + e;
+        *reinterpret_cast<Vec8*>(vs + row * kVStride + (((col >> 3) ^ vt_chunk_swz(row)) << 4) + (col & 7) * 2) = o;
     }
 }
 
@@ -155,11 +178,12 @@ __device__ inline bf16x8 as_bf16x8(const Vec16& v) {
 }
 
 __device__ inline uint32_t pack_bf16x2(float a, float b) {
-    // round to nearest even (inputs are finite probabilities in [0, 1])
-    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
-    ua += 0x7FFFu + ((ua >> 16) & 1u);
-    ub += 0x7FFFu + ((ub >> 16) & 1u);
-    return (ua >> 16) | (ub & 0xFFFF0000u);
+    // hardware round-to-nearest-even conversion (v_cvt_pk_bf16_f32)
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 r = {(__bf16)a, (__bf16)b};
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    return u;
 }
 
 template <int G>
@@ -217,9 +241,10 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
     int cr = 0, ct = walk.n_ranges ? walk.begin[0] : 0;  // cursor (range, tile)
     TileRegs regs;
     if (total > 0) {
-        load_tile_bf16(p, walk.run[0], ct, b, g, tid, regs);
+        load_tile_bf16(p, walk.run[0], ct, b, g, tid, smem, regs);
         store_tile_bf16(smem, tid, regs);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS K loads landed
     __syncthreads();
 
     for (int f = 0; f < total; ++f) {
@@ -231,7 +256,7 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
             if (cr < walk.n_ranges) ct = walk.begin[cr];
         }
         const bool has_next = f + 1 < total;
-        if (has_next) load_tile_bf16(p, walk.run[cr], ct, b, g, tid, regs);
+        if (has_next) load_tile_bf16(p, walk.run[cr], ct, b, g, tid, smem + ((f + 1) & 1) * kStageBytes, regs);
 
         const KeyRun& run = p.runs[run_idx];
         const int64_t row0 = (int64_t)tile * kBN;
@@ -248,12 +273,13 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
         f32x16 s[2];
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[mb][r] = 0.f;
+            const f32x16 zero = {};
 #pragma unroll
             for (int kk = 0; kk < 8; ++kk) {
-                const Vec16 a = *reinterpret_cast<const Vec16*>(ks_lds + (32 * mb + col) * kKStride + (8 * h + 16 * kk) * 2);
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), s[mb], 0, 0, 0);
+                const int krow = 32 * mb + col;
+                const Vec16 a = *reinterpret_cast<const Vec16*>(ks_lds + krow * kKStride + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
+                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), kk == 0 ? zero : s[mb],
+                                                                 0, 0, 0);
             }
         }
         // Elementwise mask, straddling tiles only.  Positions are tile-relative
@@ -313,21 +339,18 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
         // O^T += V^T P^T
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-            const char* vrow = vs_lds + (32 * m + col) * kVStride;
+            const int dim = 32 * m + col;
+            const char* vrow = vs_lds + dim * kVStride;
+            const int swz = vt_chunk_swz(dim);
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
-                Vec16 a;
-                const Vec8 lo = *reinterpret_cast<const Vec8*>(vrow + (16 * st + 4 * h) * 2);
-                const Vec8 hi = *reinterpret_cast<const Vec8*>(vrow + (16 * st + 8 + 4 * h) * 2);
-                a.w[0] = lo.w[0];
-                a.w[1] = lo.w[1];
-                a.w[2] = hi.w[0];
-                a.w[3] = hi.w[1];
+                const Vec16 a = *reinterpret_cast<const Vec16*>(vrow + (((2 * st + h) ^ swz) << 4));
                 o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), o[m], 0, 0, 0);
             }
         }
 
         if (has_next) store_tile_bf16(smem + ((f + 1) & 1) * kStageBytes, tid, regs);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS K loads landed
         __syncthreads();
     }
 
