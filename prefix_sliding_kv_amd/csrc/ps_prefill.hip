@@ -51,6 +51,11 @@ struct TileWalk {
 
 __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
+// v_exp_f32 without the denormal-range fix-up of exp2f: results below 2^-126
+// flush to zero, which is below the rounding error of any softmax row sum
+// (every row has a term equal to 1 at its running reference).
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ inline void plan_walk(const PrefillParams& p, int64_t i0, int64_t i1, TileWalk& w) {
     w.n_ranges = 0;
     for (int r = 0; r < p.n_runs; ++r) {
@@ -127,9 +132,11 @@ __device__ inline void load_tile_bf16(const PrefillParams& p, int run_idx, int t
     const KeyRun& run = p.runs[run_idx];
     const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
     const int64_t row0 = (int64_t)tile * kBN;
-    const char* kb = static_cast<const char*>(run.k) + (seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride) * 2;
-    const char* vb = static_cast<const char*>(run.v) + (seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride) * 2;
-    const int64_t rs = run.row_stride * 2;
+    // wave-uniform bases; per-lane offsets fit in 32 bits (64 rows of one run)
+    const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride;
+    const char* kb = static_cast<const char*>(run.k) + base_el * 2;
+    const char* vb = static_cast<const char*>(run.v) + base_el * 2;
+    const int rs = (int)(run.row_stride * 2);
     const int nrows = run.n - row0 < kBN ? (int)(run.n - row0) : kBN;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -138,19 +145,16 @@ __device__ inline void load_tile_bf16(const PrefillParams& p, int run_idx, int t
         const int row = 16 * wave + 4 * i + (lane >> 4);
         const int src_row = row < nrows ? row : nrows - 1;
         const int chunk = (lane & 15) ^ k_chunk_swz(row);
-        __builtin_amdgcn_global_load_lds(kb + src_row * rs + chunk * 16,
+        __builtin_amdgcn_global_load_lds(kb + (src_row * rs + chunk * 16),
                                          (__attribute__((address_space(3))) void*)(stage + (16 * wave + 4 * i) * kKStride),
                                          16, 0, 0);
     }
     const int vpiece = v_dim_group(tid), vrow = 4 * v_key_group(tid);
-    if (nrows == kBN) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) t.v[i] = *reinterpret_cast<const Vec16*>(vb + (vrow + i) * rs + vpiece * 16);
-    } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            t.v[i] = vrow + i < nrows ? *reinterpret_cast<const Vec16*>(vb + (vrow + i) * rs + vpiece * 16)
-                                      : Vec16{{0, 0, 0, 0}};
+    for (int i = 0; i < 4; ++i) {
+        const int row = vrow + i;
+        const Vec16 x = *reinterpret_cast<const Vec16*>(vb + ((row < nrows ? row : nrows - 1) * rs + vpiece * 16));
+        t.v[i] = row < nrows ? x : Vec16{{0, 0, 0, 0}};
     }
 }
 
@@ -306,23 +310,26 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float m_new = fmaxf(m_run, tmax);
-        const float mc = m_new == -INFINITY ? 0.f : m_new * c;
-        if (__any(m_new > m_run)) {  // rescale only when some row's max rose
-            const float alpha = exp2f(fmaf(m_run, c, -mc));
+        // The exponent reference m_run only moves when some row's maximum
+        // exceeds it by more than 8 (log2 units): until then terms stay below
+        // 2^8, and since l and O share the reference the result is the same.
+        if (__any(tmax * c > m_run * c + 8.f || (m_run == -INFINITY && tmax != -INFINITY))) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c);
             l_run *= alpha;
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
+            m_run = m_new;
         }
-        m_run = m_new;
+        const float mc = m_run == -INFINITY ? 0.f : m_run * c;
         float lsum = 0.f;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float e = exp2f(fmaf(s[mb][r], c, -mc));
+                const float e = fast_exp2(fmaf(s[mb][r], c, -mc));
                 s[mb][r] = e;
                 lsum += e;
             }
