@@ -33,6 +33,7 @@ constexpr int kBN = 64;  // keys per tile
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 struct alignas(16) Vec16 {
     uint32_t w[4];
@@ -122,39 +123,43 @@ struct TileRegs {
     Vec16 v[4];
 };
 
+// Buffer resource (V#) over [base, base + bytes): loads at offsets past the
+// end return zero, so partial tiles need no per-lane checks.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
 // Stage one 64-key tile: K goes straight from global memory into LDS
-// (global_load_lds, 16 bytes per lane at LDS base + lane * 16; each lane picks
-// the global chunk that belongs at its swizzled LDS position), V is loaded to
-// registers for the transposed store.  Rows past the end of the run are
-// clamped to its last row for K (those keys are masked) and zero for V.
+// (buffer_load ... lds, 16 bytes per lane at LDS base + lane * 16; each lane
+// picks the global chunk that belongs at its swizzled LDS position), V is
+// loaded to registers for the transposed store.  Both use a buffer resource
+// limited to the run's rows, so rows past the end read as zero (those keys are
+// masked out of the softmax; their zero V rows contribute nothing).
 __device__ inline void load_tile_bf16(const PrefillParams& p, int run_idx, int tile, int b, int g, int tid,
                                       char* stage, TileRegs& t) {
     const KeyRun& run = p.runs[run_idx];
     const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
     const int64_t row0 = (int64_t)tile * kBN;
-    // wave-uniform bases; per-lane offsets fit in 32 bits (64 rows of one run)
     const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride;
-    const char* kb = static_cast<const char*>(run.k) + base_el * 2;
-    const char* vb = static_cast<const char*>(run.v) + base_el * 2;
     const int rs = (int)(run.row_stride * 2);
     const int nrows = run.n - row0 < kBN ? (int)(run.n - row0) : kBN;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const char*>(run.k) + base_el * 2, nrows * rs);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(static_cast<const char*>(run.v) + base_el * 2, nrows * rs);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = 16 * wave + 4 * i + (lane >> 4);
-        const int src_row = row < nrows ? row : nrows - 1;
         const int chunk = (lane & 15) ^ k_chunk_swz(row);
-        __builtin_amdgcn_global_load_lds(kb + (src_row * rs + chunk * 16),
-                                         (__attribute__((address_space(3))) void*)(stage + (16 * wave + 4 * i) * kKStride),
-                                         16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void*)(stage + (16 * wave + 4 * i) * kKStride), 16,
+            row * rs + chunk * 16, 0, 0, 0);
     }
     const int vpiece = v_dim_group(tid), vrow = 4 * v_key_group(tid);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int row = vrow + i;
-        const Vec16 x = *reinterpret_cast<const Vec16*>(vb + ((row < nrows ? row : nrows - 1) * rs + vpiece * 16));
-        t.v[i] = row < nrows ? x : Vec16{{0, 0, 0, 0}};
+        const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vr, (vrow + i) * rs + vpiece * 16, 0, 0);
+        __builtin_memcpy(&t.v[i], &x, 16);
     }
 }
 
