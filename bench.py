@@ -34,6 +34,7 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 LAYERS, HQ, HKV, D, P, W = 28, 16, 8, 128, 100, 4096
+CALIB_BYTES = 256 * 1024 * 1024
 TRACE = 131072
 
 
@@ -274,6 +275,25 @@ def prefill_bench(torch, ps, synth, np):
     return res
 
 
+def decode_traffic():
+    """HBM bytes per decode launch from the committed hardware-counter
+    profile (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
+    reading for a device copy of known size), or None when the decode kernel
+    source has changed since those counters were taken."""
+    import hashlib
+    try:
+        prof = json.load(open(os.path.join(ROOT, "profiles", "decode_traffic.json")))
+        src = open(os.path.join(ROOT, "prefix_sliding_kv_amd", "csrc", "ps_decode.hip"), "rb").read()
+    except (OSError, ValueError):
+        return None
+    if hashlib.sha256(src).hexdigest() != prof.get("decode_source_sha256"):
+        return None
+    cb = prof["calibration_copy_bytes"]
+    fetch = prof["fetch_size_kib_per_launch_median"] * cb / prof["calibration_copy_fetch_kib"]
+    write = prof["write_size_kib_per_launch_median"] * cb / prof["calibration_copy_write_kib"]
+    return int(round(fetch + write))
+
+
 def cpu_baseline(np, seconds):
     """The CPU oracle on a bounded sample: one decode token of the same
     workload on `n_layers` layers, repeated until `seconds` elapse; scaled to
@@ -318,9 +338,18 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    # Calibration for hardware traffic counters: one device-to-device copy of
+    # exactly CALIB_BYTES (a blit kernel) whose FETCH_SIZE / WRITE_SIZE readings
+    # scale the decode kernel's readings to bytes.
+    calib_src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    calib_dst = torch.empty_like(calib_src)
+    calib_dst.copy_(calib_src)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     dec = decode_bench(args, torch, ps, synth, np)
     bytes_per_launch = 2 * HKV * D * (P + W) * 2
     achieved = bytes_per_launch / (dec["mean_launch_us"] * 1e-6) / 1e9
+    traffic = decode_traffic()
     step_ms = dec["graph_ms"] if dec["graph_ok"] else dec["eager_ms"]
     value = 1e3 / step_ms
     pre = {} if args.no_prefill else prefill_bench(torch, ps, synth, np)
@@ -343,7 +372,7 @@ def main():
                    "timing": "hipGraph replay of the 28-layer step" if dec["graph_ok"] else "eager launches",
                    "layers": LAYERS, "batch": 1, "trace_len": TRACE, "prefix_len": P, "window": W},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_kernel<bf16,128,G=2> (fused append + attention + combine)",
                      "bytes_per_launch": bytes_per_launch, "mean_launch_us": round(dec["mean_launch_us"], 3),
                      "launch_timing": "HIP events around the hipGraph replay of 28 decode launches, / 28"},
