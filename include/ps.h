@@ -201,7 +201,7 @@ typedef struct {
 
 /* Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,
  * scale <= 0 or not finite), PS_ERR_UNSUPPORTED (head_dim other than 128 for
- * bf16, GQA group other than 1, 2 or 4 for bf16, a chunk reaching position
+ * bf16, GQA group other than 1, 2, 4 or 8 for bf16, a chunk reaching position
  * 2^31), PS_ERR_HIP. */
 
 int ps_prefill_attn(const ps_prefill_args* args, void* stream);

@@ -50,6 +50,18 @@ struct TileWalk {
     int end[2 * kMaxRuns];
 };
 
+// Geometry of one key run resolved for one (sequence, kv head): the address
+// of its row 0, the byte stride between rows, its first position and length.
+// Kept in LDS so the tile loop reads it with a dynamic index instead of
+// holding every run of the kernel arguments in scalar registers.
+struct RunView {
+    const char* k;
+    const char* v;
+    int64_t pos0;
+    int n;
+    int row_bytes;
+};
+
 __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // v_exp_f32 without the denormal-range fix-up of exp2f: results below 2^-126
@@ -119,6 +131,14 @@ __device__ inline int v_key_group(int t) { return (((t >> 3) & 1) << 1) | ((t >>
 
 __device__ inline int k_chunk_swz(int row) { return row & 15; }
 
+// Bits [lo, hi) of a 32-bit word, with lo and hi clamped to [0, 32].
+__device__ inline uint32_t range_bits(int lo, int hi) {
+    lo = lo < 0 ? 0 : (lo > 32 ? 32 : lo);
+    hi = hi < 0 ? 0 : (hi > 32 ? 32 : hi);
+    if (hi <= lo) return 0u;
+    return (uint32_t)((((uint64_t)1 << hi) - 1) ^ (((uint64_t)1 << lo) - 1));
+}
+
 struct TileRegs {
     Vec16 v[4];
 };
@@ -135,16 +155,12 @@ __device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) 
 // loaded to registers for the transposed store.  Both use a buffer resource
 // limited to the run's rows, so rows past the end read as zero (those keys are
 // masked out of the softmax; their zero V rows contribute nothing).
-__device__ inline void load_tile_bf16(const PrefillParams& p, int run_idx, int tile, int b, int g, int tid,
-                                      char* stage, TileRegs& t) {
-    const KeyRun& run = p.runs[run_idx];
-    const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
-    const int64_t row0 = (int64_t)tile * kBN;
-    const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride + row0 * run.row_stride;
-    const int rs = (int)(run.row_stride * 2);
-    const int nrows = run.n - row0 < kBN ? (int)(run.n - row0) : kBN;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(static_cast<const char*>(run.k) + base_el * 2, nrows * rs);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(static_cast<const char*>(run.v) + base_el * 2, nrows * rs);
+__device__ inline void load_tile_bf16(const RunView& run, int tile, int tid, char* stage, TileRegs& t) {
+    const int row0 = tile * kBN;
+    const int rs = run.row_bytes;
+    const int nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(run.k + (int64_t)row0 * rs, nrows * rs);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(run.v + (int64_t)row0 * rs, nrows * rs);
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 #pragma unroll
@@ -195,10 +211,46 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
     return u;
 }
 
-template <int G>
-__global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
+// Scheduling recipe for a region with N LDS operand reads each feeding QB
+// MFMAs: issue 4 reads, then alternate one MFMA group with one read, then the
+// remaining MFMAs, so four reads are always in flight ahead of their use.
+template <int N, int QB>
+__device__ inline void pipeline_reads_and_mfma() {
+    constexpr int kAhead = 4;
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+#pragma unroll
+    for (int i = 0; i < N - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    }
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+}
+
+// Sum of the 8 bf16 values of a packed P operand, in fp32 (v_dot2 with ones):
+// the row sum then matches the bf16 P the P.V product uses.
+__device__ inline float sum_bf16x8(const Vec16& v) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        bf16x2 x;
+        __builtin_memcpy(&x, &v.w[i], 4);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(x, one, acc, false);
+    }
+    return acc;
+}
+
+// A workgroup of 4 waves owns 128*QB query rows: the G heads of a GQA group
+// stacked over 128*QB/G positions.  Each wave owns QB blocks of 32 rows, so
+// every K or V operand it reads from LDS feeds QB MFMAs; K and V operands of
+// a 32-key block are read into registers before the MFMAs that use them.
+template <int G, int QB>
+__global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) prefill_bf16_kernel(PrefillParams p) {
     constexpr int D = 128;
-    constexpr int QP = 128 / G;  // positions per query tile
+    constexpr int QP = 128 * QB / G;  // positions per query tile
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -210,47 +262,70 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
     const int n_qt = (p.seq_len + QP - 1) / QP;
     const int work = xcd_remap((int)blockIdx.x, n_qt * p.hkv * p.batch);
     const int qt = work % n_qt, g = (work / n_qt) % p.hkv, b = work / (n_qt * p.hkv);
-    const int hw = (wave * 32) / QP;           // head within the group
-    const int pw = (wave * 32) % QP;           // position offset of this wave
-    const int head = g * G + hw;
 
     const int64_t t0 = (int64_t)qt * QP;       // first chunk row of the tile
     const int64_t t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
     const int64_t i0 = p.start_pos + t0;
     const int64_t i1 = p.start_pos + t_last;
-    const int64_t my_t = t0 + pw + col;
-    const bool q_ok = my_t < p.seq_len;
-    const int64_t my_i = p.start_pos + my_t;
     const float c = p.scale_log2;                              // > 0 (checked on the host)
     const int w32 = p.W > (1 << 30) ? (1 << 30) : (int)p.W;    // a window beyond every position is the same
 
-    // Q of this lane's query (B operand): dims 8h + 16ks .. +8
-    Vec16 qreg[8];
-    {
+    // this lane's query in each block: stacked row 32*(QB*wave + qb) + col
+    int head[QB];
+    int64_t my_t[QB], my_i[QB];
+    bool q_ok[QB];
+    Vec16 qreg[QB][8];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        const int row = 32 * (QB * wave + qb) + col;
+        head[qb] = g * G + row / QP;
+        my_t[qb] = t0 + row % QP;
+        q_ok[qb] = my_t[qb] < p.seq_len;
+        my_i[qb] = p.start_pos + my_t[qb];
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
-                             (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
+                             (((int64_t)b * p.seq_len + (q_ok[qb] ? my_t[qb] : 0)) * p.hq + head[qb]) * D;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-            qreg[ks] = q_ok ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
+            qreg[qb][ks] = q_ok[qb] ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
     }
 
     __shared__ TileWalk walk;
-    if (tid == 0) plan_walk(p, i0, i1, walk);
+    __shared__ RunView views[kMaxRuns];
+    if (tid == 0) {
+        plan_walk(p, i0, i1, walk);
+        for (int r = 0; r < p.n_runs; ++r) {
+            const KeyRun& run = p.runs[r];
+            const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
+            const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride;
+            views[r].k = static_cast<const char*>(run.k) + base_el * 2;
+            views[r].v = static_cast<const char*>(run.v) + base_el * 2;
+            views[r].pos0 = run.pos0;
+            views[r].n = (int)run.n;
+            views[r].row_bytes = (int)(run.row_stride * 2);
+        }
+    }
     __syncthreads();
     int total = 0;
     for (int r = 0; r < walk.n_ranges; ++r) total += walk.end[r] - walk.begin[r];
 
-    f32x16 o[4];
+    f32x16 o[QB][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[qb][m][r] = 0.f;
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.f;
+    }
 
     int cr = 0, ct = walk.n_ranges ? walk.begin[0] : 0;  // cursor (range, tile)
     TileRegs regs;
     if (total > 0) {
-        load_tile_bf16(p, walk.run[0], ct, b, g, tid, smem, regs);
+        load_tile_bf16(views[walk.run[0]], ct, tid, smem, regs);
         store_tile_bf16(smem, tid, regs);
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS K loads landed
@@ -265,121 +340,158 @@ __global__ void __launch_bounds__(256, 2) prefill_bf16_kernel(PrefillParams p) {
             if (cr < walk.n_ranges) ct = walk.begin[cr];
         }
         const bool has_next = f + 1 < total;
-        if (has_next) load_tile_bf16(p, walk.run[cr], ct, b, g, tid, smem + ((f + 1) & 1) * kStageBytes, regs);
+        if (has_next) load_tile_bf16(views[walk.run[cr]], ct, tid, smem + ((f + 1) & 1) * kStageBytes, regs);
 
-        const KeyRun& run = p.runs[run_idx];
-        const int64_t row0 = (int64_t)tile * kBN;
-        const int nrows = (int)(run.n - row0 < kBN ? run.n - row0 : kBN);
-        const int64_t j0 = run.pos0 + row0;
+        const int row0 = tile * kBN;
+        const int run_n = views[run_idx].n;
+        const int nrows = run_n - row0 < kBN ? run_n - row0 : kBN;
+        const int64_t j0 = views[run_idx].pos0 + row0;
         const int64_t j1 = j0 + nrows - 1;
         const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j1, p.P, p.W);
 
         const char* stage = smem + (f & 1) * kStageBytes;
         const char* ks_lds = stage;
         const char* vs_lds = stage + kKBytes;
+        __builtin_amdgcn_sched_barrier(0);
 
-        // S^T = K Q^T for two blocks of 32 keys (raw scores, unscaled)
-        f32x16 s[2];
+        // S^T = K Q^T (raw scores, unscaled).  The 16 K operands of the tile
+        // are read from LDS once and feed QB MFMAs each; the schedule keeps
+        // four reads in flight ahead of the MFMAs.
+        f32x16 s[QB][2];
+        {
+            Vec16 ka[2][8];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const f32x16 zero = {};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
+            for (int mb = 0; mb < 2; ++mb) {
                 const int krow = 32 * mb + col;
-                const Vec16 a = *reinterpret_cast<const Vec16*>(ks_lds + krow * kKStride + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
-                s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qreg[kk]), kk == 0 ? zero : s[mb],
-                                                                 0, 0, 0);
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+                    ka[mb][kk] = *reinterpret_cast<const Vec16*>(ks_lds + krow * kKStride + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
             }
-        }
-        // Elementwise mask, straddling tiles only.  Positions are tile-relative
-        // 32-bit values: key kr of the tile is visible to this lane's query iff
-        // kr <= rel and (kr < pj or kr > rel - W), rel = i - j0, pj = P - j0.
-        if (cls == kMasked) {
-            const int rel = (int)(my_i - j0);
-            const int64_t pj64 = p.P - j0;
-            const int pj = pj64 > (1 << 30) ? (1 << 30) : (pj64 < -(1 << 30) ? -(1 << 30) : (int)pj64);
-            const int relw = rel - w32;
+            const f32x16 zero = {};
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int kr = 32 * mb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool vis = kr < nrows && kr <= rel && (kr < pj || kr > relw);
-                    s[mb][r] = vis ? s[mb][r] : -INFINITY;
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        s[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[mb][kk]), as_bf16x8(qreg[qb][kk]),
+                                                                            kk == 0 ? zero : s[qb][mb], 0, 0, 0);
+            pipeline_reads_and_mfma<16, QB>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // Elementwise mask, straddling tiles only.  For this lane's query the
+        // visible keys of the tile (tile-relative index kr) form at most two
+        // intervals: [0, min(pj, hic + 1)) -- the prefix -- and
+        // [max(relw + 1, 0), hic + 1) -- the window -- with rel = i - j0,
+        // relw = rel - W, pj = P - j0, hic = min(rel, nrows - 1).  They become
+        // one 32-bit bitmap per 32-key block, and each score is kept or set to
+        // -inf with a bit extract and a bitfield select (no per-element compares).
+        if (cls == kMasked) {
+            const int64_t pj64 = p.P - j0;
+            const int pj = pj64 > (1 << 30) ? (1 << 30) : (pj64 < -(1 << 30) ? -(1 << 30) : (int)pj64);
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+                const int rel = (int)(my_i[qb] - j0);
+                const int hic = rel < nrows - 1 ? rel : nrows - 1;
+                const int a_hi = pj < hic + 1 ? pj : hic + 1;
+                const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb) {
+                    const uint32_t bits = range_bits(0, a_hi - 32 * mb) | range_bits(b_lo - 32 * mb, hic + 1 - 32 * mb);
+                    const uint32_t bits_h = bits >> (4 * h);  // this lane half's keys start at bit 4h
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int keep = __builtin_amdgcn_sbfe((int)bits_h, 8 * (r >> 2) + (r & 3), 1);  // 0 or -1
+                        const uint32_t km = (uint32_t)keep;
+                        s[qb][mb][r] = __uint_as_float((km & __float_as_uint(s[qb][mb][r])) | (~km & 0xFF800000u));
+                    }
                 }
+            }
         }
         // online softmax in raw-score units; exp2((s - m) * c) as one FMA + exp
-        float tmax = -INFINITY;
+        Vec16 pb[QB][4];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
+        for (int qb = 0; qb < QB; ++qb) {
+            float tmax = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        // The exponent reference m_run only moves when some row's maximum
-        // exceeds it by more than 8 (log2 units): until then terms stay below
-        // 2^8, and since l and O share the reference the result is the same.
-        if (__any(tmax * c > m_run * c + 8.f || (m_run == -INFINITY && tmax != -INFINITY))) {
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c);
-            l_run *= alpha;
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[qb][mb][r]);
+            tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+            // The exponent reference only moves when some row's maximum
+            // exceeds it by more than 8 (log2 units): until then terms stay
+            // below 2^8, and since l and O share the reference the result is
+            // the same.
+            if (__any(tmax * c > m_run[qb] * c + 8.f)) {
+                const float m_new = fmaxf(m_run[qb], tmax);
+                const float alpha = m_run[qb] == -INFINITY ? 0.f : fast_exp2((m_run[qb] - m_new) * c);
+                l_run[qb] *= alpha;
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[qb][m][r] *= alpha;
+                m_run[qb] = m_new;
+            }
+            const float mc = m_run[qb] == -INFINITY ? 0.f : m_run[qb] * c;
+            // P^T as B operand: k-step st covers keys 16 st .. 16 st + 15
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int mb = st >> 1, base = 8 * (st & 1);
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    pb[qb][st].w[w] = pack_bf16x2(fast_exp2(fmaf(s[qb][mb][base + 2 * w], c, -mc)),
+                                                  fast_exp2(fmaf(s[qb][mb][base + 2 * w + 1], c, -mc)));
+                l_run[qb] += sum_bf16x8(pb[qb][st]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // O^T += V^T P^T: the 16 V operands are read once and feed QB MFMAs
+        // each, with the same read-ahead schedule.
+        {
+            Vec16 va[4][4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int dim = 32 * m + col;
+                const char* vrow = vs_lds + dim * kVStride;
+                const int swz = vt_chunk_swz(dim);
+#pragma unroll
+                for (int st = 0; st < 4; ++st) va[m][st] = *reinterpret_cast<const Vec16*>(vrow + (((2 * st + h) ^ swz) << 4));
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
-            m_run = m_new;
+                for (int st = 0; st < 4; ++st)
+#pragma unroll
+                    for (int qb = 0; qb < QB; ++qb)
+                        o[qb][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m][st]), as_bf16x8(pb[qb][st]),
+                                                                           o[qb][m], 0, 0, 0);
+            pipeline_reads_and_mfma<16, QB>();
         }
-        const float mc = m_run == -INFINITY ? 0.f : m_run * c;
-        float lsum = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(fmaf(s[mb][r], c, -mc));
-                s[mb][r] = e;
-                lsum += e;
-            }
-        l_run += lsum;
-
-        // P^T as B operand: k-step st covers keys 16 st .. 16 st + 15
-        Vec16 pb[4];
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const int mb = st >> 1, base = 8 * (st & 1);
-#pragma unroll
-            for (int w = 0; w < 4; ++w) pb[st].w[w] = pack_bf16x2(s[mb][base + 2 * w], s[mb][base + 2 * w + 1]);
-        }
-        // O^T += V^T P^T
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int dim = 32 * m + col;
-            const char* vrow = vs_lds + dim * kVStride;
-            const int swz = vt_chunk_swz(dim);
-#pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const Vec16 a = *reinterpret_cast<const Vec16*>(vrow + (((2 * st + h) ^ swz) << 4));
-                o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pb[st]), o[m], 0, 0, 0);
-            }
-        }
+        __builtin_amdgcn_sched_barrier(0);
 
         if (has_next) store_tile_bf16(smem + ((f + 1) & 1) * kStageBytes, tid, regs);
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS K loads landed
         __syncthreads();
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (!q_ok) return;
-    const float inv = 1.f / l_tot;
-    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b * p.seq_len + my_t) * p.hq + head) * D;
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int qb = 0; qb < QB; ++qb) {
+        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
+        if (!q_ok[qb]) continue;
+        const float inv = 1.f / l_tot;
+        uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b * p.seq_len + my_t[qb]) * p.hq + head[qb]) * D;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            Vec8 w;
-            w.w[0] = pack_bf16x2(o[m][4 * c] * inv, o[m][4 * c + 1] * inv);
-            w.w[1] = pack_bf16x2(o[m][4 * c + 2] * inv, o[m][4 * c + 3] * inv);
-            *reinterpret_cast<Vec8*>(op + 32 * m + 8 * c + 4 * h) = w;
-        }
-    if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run * c + log2f(l_tot)) * kLn2;
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                Vec8 w;
+                w.w[0] = pack_bf16x2(o[qb][m][4 * cc] * inv, o[qb][m][4 * cc + 1] * inv);
+                w.w[1] = pack_bf16x2(o[qb][m][4 * cc + 2] * inv, o[qb][m][4 * cc + 3] * inv);
+                *reinterpret_cast<Vec8*>(op + 32 * m + 8 * cc + 4 * h) = w;
+            }
+        if (p.lse && h == 0)
+            p.lse[((int64_t)b * p.seq_len + my_t[qb]) * p.hq + head[qb]] = (m_run[qb] * c + log2f(l_tot)) * kLn2;
+    }
 }
 
 // ----------------------------------------------------------------- fp32 debug
@@ -471,24 +583,24 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
     if (p.seq_len == 0) return hipSuccess;
     if (dtype == PS_BF16) {
         if (head_dim != 128) return hipErrorInvalidValue;
-        const int qp = 128 / group;
+        constexpr int QB = 1;
+        const int qp = 128 * QB / group;
         dim3 grid((unsigned)(((p.seq_len + qp - 1) / qp) * p.hkv * p.batch));
         const size_t lds = 2 * kStageBytes;
+        const void* fn = nullptr;
         switch (group) {
-            case 1:
-                hipFuncSetAttribute((const void*)prefill_bf16_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-                hipLaunchKernelGGL(prefill_bf16_kernel<1>, grid, dim3(256), lds, stream, p);
-                break;
-            case 2:
-                hipFuncSetAttribute((const void*)prefill_bf16_kernel<2>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-                hipLaunchKernelGGL(prefill_bf16_kernel<2>, grid, dim3(256), lds, stream, p);
-                break;
-            case 4:
-                hipFuncSetAttribute((const void*)prefill_bf16_kernel<4>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-                hipLaunchKernelGGL(prefill_bf16_kernel<4>, grid, dim3(256), lds, stream, p);
-                break;
-            default:
-                return hipErrorInvalidValue;
+            case 1: fn = (const void*)prefill_bf16_kernel<1, QB>; break;
+            case 2: fn = (const void*)prefill_bf16_kernel<2, QB>; break;
+            case 4: fn = (const void*)prefill_bf16_kernel<4, QB>; break;
+            case 8: fn = (const void*)prefill_bf16_kernel<8, QB>; break;
+            default: return hipErrorInvalidValue;
+        }
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        switch (group) {
+            case 1: hipLaunchKernelGGL((prefill_bf16_kernel<1, QB>), grid, dim3(256), lds, stream, p); break;
+            case 2: hipLaunchKernelGGL((prefill_bf16_kernel<2, QB>), grid, dim3(256), lds, stream, p); break;
+            case 4: hipLaunchKernelGGL((prefill_bf16_kernel<4, QB>), grid, dim3(256), lds, stream, p); break;
+            case 8: hipLaunchKernelGGL((prefill_bf16_kernel<8, QB>), grid, dim3(256), lds, stream, p); break;
         }
         return hipGetLastError();
     }

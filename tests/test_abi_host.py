@@ -127,7 +127,7 @@ def test_prefill_validation():
     assert call(head_dim=96) == ps.PS_ERR_UNSUPPORTED
     assert call(head_dim=64) == ps.PS_ERR_UNSUPPORTED          # bf16 MFMA path is d=128 only
     assert call(dtype=5) == ps.PS_ERR_UNSUPPORTED
-    assert call(n_q_heads=64, n_kv_heads=8) == ps.PS_ERR_UNSUPPORTED  # GQA group 8 on the MFMA path
+    assert call(n_q_heads=128, n_kv_heads=8) == ps.PS_ERR_UNSUPPORTED  # GQA group 16 on the MFMA path
     assert call(seq_len=4) == ps.PS_ERR_INVALID                # null tensors
     assert call(scale=float("nan")) == ps.PS_ERR_INVALID
     assert call(scale=0.0) == ps.PS_ERR_INVALID

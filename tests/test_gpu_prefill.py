@@ -56,6 +56,7 @@ def run_trainer(q, k, v, P, W, start, dtype, with_lse=True):
     (DT_BF16, 128, 4, 2, 1, 333, 17, 100, 3.0),  # peaky: mask errors show
     (DT_BF16, 128, 2, 2, 1, 260, 0, 33, 3.0),   # G=1, vanilla sliding window
     (DT_BF16, 128, 8, 2, 1, 200, 5, 64, 3.0),   # G=4
+    (DT_BF16, 128, 16, 2, 1, 150, 9, 40, 3.0),  # G=8
     (DT_BF16, 128, 2, 1, 1, 190, 3, 1, 3.0),    # W=1: prefix + self
     (DT_BF16, 128, 2, 1, 1, 64, 100, 8, 1.0),   # exactly one tile, all prefix
     (DT_BF16, 128, 2, 1, 1, 1, 0, 5, 1.0),      # single token
