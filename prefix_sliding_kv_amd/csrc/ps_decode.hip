@@ -118,16 +118,43 @@ __device__ inline float load_coherent(const float* p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Merge of two softmax partials (m in log2 units, l, o) into the first.
-template <int VEC>
-__device__ inline void merge_into(float& m, float& l, float* o, float m2, float l2, const float* o2) {
-    const float M = fmaxf(m, m2);
-    const float a = m == -INFINITY ? 0.f : exp2f(m - M);
-    const float c = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
-    m = M;
-    l = a * l + c * l2;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) o[e] = a * o[e] + c * o2[e];
+// v_exp_f32 without the denormal-range fix-up of exp2f.  Every argument here
+// is a score minus a maximum over a set that contains it (so <= 0), and a
+// result below 2^-126 is far below the rounding error of a sum that holds a
+// term equal to 1.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Reductions over the row groups of a wave: lanes that hold the same slice
+// (lane % LPR) of different key rows.  Lane pairs l, l ^ 8 inside a 16-lane
+// row meet through a DPP rotation; l, l ^ 16 and l, l ^ 32 through the
+// permlane swaps, which leave the value of each lane and of its partner in
+// the two results, in an order that depends on the lane, so a symmetric op
+// of the pair gives the same answer on both lanes.
+template <int LPR>
+__device__ inline float rowgroup_sum(float x) {
+    if constexpr (LPR <= 8) x += dpp_f<0x128>(x);
+    if constexpr (LPR <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    if constexpr (LPR <= 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    return x;
+}
+template <int LPR>
+__device__ inline float rowgroup_max(float x) {
+    if constexpr (LPR <= 8) x = fmaxf(x, dpp_f<0x128>(x));
+    if constexpr (LPR <= 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    if constexpr (LPR <= 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    }
+    return x;
 }
 
 template <typename T, int D, int G, int NW, int U>
@@ -140,9 +167,13 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     constexpr int PAIRS = G * D;          // (head, dim) outputs of a group
     static_assert(LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "row must map onto a wave");
 
-    __shared__ float s_m[NW][G];
-    __shared__ float s_l[NW][G];
-    __shared__ float s_o[NW][G][D];
+    // per-wave partials; maxima, sums and weights with the wave index
+    // innermost so a reader takes them with 16-byte LDS reads
+    __shared__ __attribute__((aligned(16))) float s_m[G][NW];
+    __shared__ __attribute__((aligned(16))) float s_l[G][NW];
+    __shared__ __attribute__((aligned(16))) float s_w[G][NW];
+    __shared__ float s_ref[G];
+    __shared__ float s_o[NW][G * D];
     __shared__ int s_last;
 
     const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -220,14 +251,19 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         *reinterpret_cast<Vec16*>(vd) = load16(vnew_row + tid * VEC);
     }
 
-    // Softmax over this row group's rows and weighted sum of values.
-    float mg[G], lg[G], og[G][VEC];
+    // Softmax per wave: each head's reference is the wave's maximum score
+    // (row groups meet through lane swaps), so a wave finishes its rows as
+    // soon as they are in, without waiting for the rest of the workgroup.
+    // Row-group partials then add without rescaling; the waves are combined
+    // through LDS with one weight per (head, wave).  A wave whose rows all
+    // lie past the end has reference -inf and weight 0.
+    float mw[G], lg[G], og[G][VEC];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
-        float m = -INFINITY;
+        float m = s[0][hh];
 #pragma unroll
-        for (int u = 0; u < U; ++u) m = fmaxf(m, s[u][hh]);
-        mg[hh] = m;
+        for (int u = 1; u < U; ++u) m = fmaxf(m, s[u][hh]);
+        mw[hh] = rowgroup_max<LPR>(m);
         lg[hh] = 0.f;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) og[hh][e] = 0.f;
@@ -238,53 +274,57 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         Elem<T>::unpack(vr[u], vf);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-            const float w = valid[u] ? exp2f(s[u][hh] - mg[hh]) : 0.f;
+            const float w = valid[u] ? fast_exp2(s[u][hh] - mw[hh]) : 0.f;
             lg[hh] += w;
 #pragma unroll
             for (int e = 0; e < VEC; ++e) og[hh][e] = fmaf(w, vf[e], og[hh][e]);
         }
     }
-
-    // Merge the RPW row groups of each wave with lane exchanges, then the NW
-    // waves through LDS.
 #pragma unroll
-    for (int mask = LPR; mask < 64; mask <<= 1) {
+    for (int hh = 0; hh < G; ++hh) {
+        lg[hh] = rowgroup_sum<LPR>(lg[hh]);
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-            const float m2 = __shfl_xor(mg[hh], mask, 64);
-            const float l2 = __shfl_xor(lg[hh], mask, 64);
-            float o2[VEC];
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) o2[e] = __shfl_xor(og[hh][e], mask, 64);
-            merge_into<VEC>(mg[hh], lg[hh], og[hh], m2, l2, o2);
-        }
+        for (int e = 0; e < VEC; ++e) og[hh][e] = rowgroup_sum<LPR>(og[hh][e]);
     }
     if (rg == 0) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) s_o[wave][hh][sub * VEC + e] = og[hh][e];
+            for (int e = 0; e < VEC; ++e) s_o[wave][hh * D + sub * VEC + e] = og[hh][e];
             if (sub == 0) {
-                s_m[wave][hh] = mg[hh];
-                s_l[wave][hh] = lg[hh];
+                s_m[hh][wave] = mw[hh];
+                s_l[hh][wave] = lg[hh];
             }
         }
+    }
+    __syncthreads();
+    // weight of each (head, wave) against the split's maximum
+    if (tid < G * NW) {
+        const int hh = tid / NW, k = tid % NW;
+        float M = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NW; j += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(&s_m[hh][j]);
+            M = fmaxf(fmaxf(M, fmaxf(x.x, x.y)), fmaxf(x.z, x.w));
+        }
+        const float mk = s_m[hh][k];
+        s_w[hh][k] = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
+        if (k == 0) s_ref[hh] = M;  // finite: every split holds at least one valid row
     }
     __syncthreads();
 
     const int64_t ws_head0 = (int64_t)b * p.hq + g * G;
     for (int idx = tid; idx < PAIRS; idx += NT) {
         const int hh = idx / D, dim = idx % D;
-        float M = -INFINITY;
+        float O = 0.f, L = 0.f;
 #pragma unroll
-        for (int k = 0; k < NW; ++k) M = fmaxf(M, s_m[k][hh]);
-        float L = 0.f, O = 0.f;
-#pragma unroll
-        for (int k = 0; k < NW; ++k) {
-            const float w = s_m[k][hh] == -INFINITY ? 0.f : exp2f(s_m[k][hh] - M);
-            L = fmaf(w, s_l[k][hh], L);
-            O = fmaf(w, s_o[k][hh][dim], O);
+        for (int k = 0; k < NW; k += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(&s_w[hh][k]);
+            const float4 l = *reinterpret_cast<const float4*>(&s_l[hh][k]);
+            L = fmaf(w.x, l.x, fmaf(w.y, l.y, fmaf(w.z, l.z, fmaf(w.w, l.w, L))));
+            O = fmaf(w.x, s_o[k][idx], fmaf(w.y, s_o[k + 1][idx], fmaf(w.z, s_o[k + 2][idx], fmaf(w.w, s_o[k + 3][idx], O))));
         }
+        const float M = s_ref[hh];
         if (nsplit == 1) {
             T* o = reinterpret_cast<T*>(p.out) + (ws_head0 + hh) * D + dim;
             *o = Elem<T>::from_float(O / L);
@@ -335,23 +375,28 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
             float bm[kBatch], bl[kBatch], bo[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
+                // part is uniform across a wave, so this branch is too: no
+                // load is issued for a split past the end
                 const int sidx = s0 + j * PARTS;
-                const bool ok = sidx < nsplit;
-                const int sc = ok ? sidx : s0;
-                bm[j] = load_coherent(mlh + 2 * sc);
-                bl[j] = load_coherent(mlh + 2 * sc + 1);
-                bo[j] = load_coherent(oh + (int64_t)sc * D);
-                if (!ok) bm[j] = -INFINITY;
+                if (sidx < nsplit) {
+                    bm[j] = load_coherent(mlh + 2 * sidx);
+                    bl[j] = load_coherent(mlh + 2 * sidx + 1);
+                    bo[j] = load_coherent(oh + (int64_t)sidx * D);
+                } else {
+                    bm[j] = -INFINITY;
+                    bl[j] = 0.f;
+                    bo[j] = 0.f;
+                }
             }
             float bM = M;
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) bM = fmaxf(bM, bm[j]);
-            const float a = M == -INFINITY ? 0.f : exp2f(M - bM);
+            const float a = M == -INFINITY ? 0.f : fast_exp2(M - bM);
             L *= a;
             O *= a;
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
-                const float w = bm[j] == -INFINITY ? 0.f : exp2f(bm[j] - bM);
+                const float w = bm[j] == -INFINITY ? 0.f : fast_exp2(bm[j] - bM);
                 L = fmaf(w, bl[j], L);
                 O = fmaf(w, bo[j], O);
             }
@@ -379,7 +424,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 #pragma unroll
             for (int k = 0; k < PARTS; ++k) {
                 const float mk = red[(k * 3) * PAIRS + pair];
-                const float w = mk == -INFINITY ? 0.f : exp2f(mk - M);
+                const float w = mk == -INFINITY ? 0.f : fast_exp2(mk - M);
                 L = fmaf(w, red[(k * 3 + 1) * PAIRS + pair], L);
                 O = fmaf(w, red[(k * 3 + 2) * PAIRS + pair], O);
             }
@@ -399,7 +444,8 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
 }
 
 // rows_per_split = NW * RPW * U: four waves for the two smallest sizes,
-// sixteen waves (short per-lane row chains, few splits) above.
+// sixteen for 16 RPW and 128 RPW, eight (longer per-lane row chains, a
+// cheaper combine across waves) for 32 RPW and 64 RPW.
 template <typename T, int D, int G>
 hipError_t dispatch_rows(int rows, const DecodeParams& p, hipStream_t stream) {
     constexpr int RPW = 64 / (D / Elem<T>::kPerVec);
@@ -407,8 +453,8 @@ hipError_t dispatch_rows(int rows, const DecodeParams& p, hipStream_t stream) {
     if (rows == r4) return launch_one<T, D, G, 4, 1>(p, stream);
     if (rows == 2 * r4) return launch_one<T, D, G, 4, 2>(p, stream);
     if (rows == r16) return launch_one<T, D, G, 16, 1>(p, stream);
-    if (rows == 2 * r16) return launch_one<T, D, G, 16, 2>(p, stream);
-    if (rows == 4 * r16) return launch_one<T, D, G, 16, 4>(p, stream);
+    if (rows == 2 * r16) return launch_one<T, D, G, 8, 4>(p, stream);
+    if (rows == 4 * r16) return launch_one<T, D, G, 8, 8>(p, stream);
     if (rows == 8 * r16) return launch_one<T, D, G, 16, 8>(p, stream);
     return hipErrorInvalidValue;
 }

@@ -81,7 +81,7 @@ hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split,
 // Rows one wave covers per 16-byte load instruction for (dtype, head_dim).
 int decode_rows_per_load(int dtype, int head_dim);
 // Split sizes the decode kernel is built for: with r = decode_rows_per_load,
-// 4r and 8r (four waves) and 16r, 32r, 64r, 128r (sixteen waves), each >= 16.
+// 4r, 8r, 16r, 32r, 64r and 128r, each >= 16.
 bool decode_rows_valid(int dtype, int head_dim, int rows);
 
 // ------------------------------------------------------------ append
