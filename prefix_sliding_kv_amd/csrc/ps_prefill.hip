@@ -13,16 +13,18 @@
 // FlashAttention kernel; njhaofan.com article, section
 // "PrefixSliding如何丢掉中间Token？"), rebuilt for CDNA4.
 //
-// bf16 path (head_dim 128): a workgroup of 4 waves owns 128 query rows, the G
-// heads of one GQA group stacked over 128/G positions, so every K/V tile
+// bf16 path (head_dim 128): a workgroup of 8 waves owns 256 query rows, the
+// G heads of one GQA group stacked over 256/G positions, so every K/V tile
 // staged in LDS serves all heads that share it.  Per 64-key tile each wave
 // computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (a lane then holds 16
 // scores of a single query, so the online softmax needs one cross-lane step),
-// and O^T += V^T P^T with the same instruction, reading V from a transposed
-// LDS copy written while staging.  The next tile's global loads are issued
-// before the current tile's math (register prefetch, two LDS buffers, one
-// barrier per tile).  fp32 path: a plain debug kernel with the same tile
-// walk and classification.
+// and O^T += V^T P^T with the same instruction, reading the V^T operand from
+// the row-major V tile with the transposing LDS read (ds_read_b64_tr_b16).
+// K and V tiles go from global memory straight into a 4-stage LDS ring
+// (buffer_load ... lds), three tiles ahead of the one being computed, one
+// barrier per tile.  The tile walk is kept in scalar registers and touches
+// LDS only at range boundaries.  fp32 path: a plain debug kernel with the
+// same tile walk and classification.
 #include "ps_internal.h"
 
 namespace ps {
@@ -110,26 +112,27 @@ __device__ inline int xcd_remap(int id, int n) {
     return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
 }
 
-constexpr int kKStride = 128 * 2;       // bytes per K row in LDS; 16-byte chunks xor-swizzled by row & 15
-constexpr int kVStride = kBN * 2;       // bytes per transposed V row (one head dimension), unpadded
-constexpr int kKBytes = kBN * kKStride;
-constexpr int kVBytes = 128 * kVStride;
-constexpr int kStageBytes = kKBytes + kVBytes;
+constexpr int kWaves = 8;                // waves per workgroup (2 per SIMD, one workgroup per CU)
+constexpr int kThreads = kWaves * 64;
+constexpr int kStages = 4;               // LDS ring of key tiles; prefetch distance kStages - 1
+constexpr int kRowBytes = 128 * 2;       // one K or V row (head_dim 128, bf16)
+constexpr int kTileBytes = kBN * kRowBytes;
+constexpr int kStageBytes = 2 * kTileBytes;  // K tile then V tile
 
-// Transposed V layout.  Row = head dimension, 64 keys of 2 bytes.  Keys are
-// stored in the order the P.V MFMA consumes them: the 8 keys lane half h
-// needs for k-step st (keys 16st + 8a + 4h + c, a, c in {0,1},{0..3}) sit in
-// columns 16st + 8h + 4a + c, i.e. key bits 2 and 3 swapped, so one 16-byte
-// read fetches them.  The 16-byte chunk of a row is xor-swizzled by
-// ((row >> 3) ^ row) & 7 so that both the staging writes and the operand
-// reads hit all LDS banks once.
-__device__ inline int vt_chunk_swz(int row) { return ((row >> 3) ^ row) & 7; }
-__device__ inline int swap01(int x) { return (x & ~3) | ((x & 1) << 1) | ((x >> 1) & 1); }
-// staging thread -> (dim group 0..15, key group 0..15) for V
-__device__ inline int v_dim_group(int t) { return (t & 7) | (((t >> 4) & 1) << 3); }
-__device__ inline int v_key_group(int t) { return (((t >> 3) & 1) << 1) | ((t >> 5) & 1) | ((t >> 6) << 2); }
-
+// Both tiles are row-major (row = key, 256 bytes) with 16-byte chunks
+// xor-swizzled by row so that the operand reads hit every LDS bank once:
+//  K: chunk c of row r at c ^ (r & 15)   (8 consecutive rows, same chunk, per
+//     16-byte read group);
+//  V: chunk c of row r at c ^ 2(r & 3)   (4 consecutive rows, two chunks, per
+//     16-lane transposing read).
 __device__ inline int k_chunk_swz(int row) { return row & 15; }
+__device__ inline int v_chunk_swz(int row) { return 2 * (row & 3); }
+
+// Buffer resource (V#) over [base, base + bytes): loads at offsets past the
+// end return zero, so partial tiles need no per-lane checks.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
 
 // Bits [lo, hi) of a 32-bit word, with lo and hi clamped to [0, 32].
 __device__ inline uint32_t range_bits(int lo, int hi) {
@@ -139,62 +142,90 @@ __device__ inline uint32_t range_bits(int lo, int hi) {
     return (uint32_t)((((uint64_t)1 << hi) - 1) ^ (((uint64_t)1 << lo) - 1));
 }
 
-struct TileRegs {
-    Vec16 v[4];
+__device__ inline int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ inline const char* uniform_ptr(const char* p) {
+    const uint64_t u = (uint64_t)p;
+    return (const char*)(((uint64_t)(uint32_t)uniform_int((int)(u >> 32)) << 32) | (uint32_t)uniform_int((int)(uint32_t)u));
+}
+__device__ inline int64_t uniform_i64(int64_t x) {
+    const uint64_t u = (uint64_t)x;
+    return (int64_t)(((uint64_t)(uint32_t)uniform_int((int)(u >> 32)) << 32) | (uint32_t)uniform_int((int)(uint32_t)u));
+}
+
+// Workgroup barrier between key tiles.  Each wave has already waited for its
+// own direct-to-LDS loads of the next tile (vmcnt) and for its LDS reads of
+// the current one (their results are consumed), so a bare s_barrier orders
+// everything that matters; __syncthreads would add a release fence that
+// waits for every direct-to-LDS load still in flight, prefetches included.
+__device__ inline void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// A position in the tile walk: range r, tile t of its run, end of the range,
+// and the run's geometry.  Everything is uniform across a wave and lives in
+// scalar registers; the walk and run tables in LDS are read only when the
+// cursor enters a new range.
+struct Cursor {
+    int r, t, end;
+    const char* k;
+    const char* v;
+    int64_t pos0;
+    int n, rs;
 };
 
-// Buffer resource (V#) over [base, base + bytes): loads at offsets past the
-// end return zero, so partial tiles need no per-lane checks.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+__device__ inline void cursor_enter(Cursor& c, int r, const TileWalk& w, const RunView* views) {
+    c.r = r;
+    c.t = uniform_int(w.begin[r]);
+    c.end = uniform_int(w.end[r]);
+    const RunView& v = views[uniform_int(w.run[r])];
+    c.k = uniform_ptr(v.k);
+    c.v = uniform_ptr(v.v);
+    c.pos0 = uniform_i64(v.pos0);
+    c.n = uniform_int(v.n);
+    c.rs = uniform_int(v.row_bytes);
 }
 
-// Stage one 64-key tile: K goes straight from global memory into LDS
-// (buffer_load ... lds, 16 bytes per lane at LDS base + lane * 16; each lane
-// picks the global chunk that belongs at its swizzled LDS position), V is
-// loaded to registers for the transposed store.  Both use a buffer resource
-// limited to the run's rows, so rows past the end read as zero (those keys are
-// masked out of the softmax; their zero V rows contribute nothing).
-__device__ inline void load_tile_bf16(const RunView& run, int tile, int tid, char* stage, TileRegs& t) {
-    const int row0 = tile * kBN;
-    const int rs = run.row_bytes;
-    const int nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(run.k + (int64_t)row0 * rs, nrows * rs);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(run.v + (int64_t)row0 * rs, nrows * rs);
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+// Step to the next tile; returns true when the cursor entered a new range.
+__device__ inline bool cursor_next(Cursor& c, int n_ranges, const TileWalk& w, const RunView* views) {
+    if (++c.t < c.end || c.r + 1 >= n_ranges) return false;
+    cursor_enter(c, c.r + 1, w, views);
+    return true;
+}
+
+// Per-lane byte offsets, within a tile, of this lane's 16-byte pieces of the
+// direct-to-LDS loads (two K and two V instructions per wave and tile; wave w
+// fills rows 8w .. 8w + 7).  They depend on the run's row stride only.
+struct LaneOffsets {
+    int k[2], v[2];
+};
+__device__ inline void lane_offsets(LaneOffsets& o, int rs, int lane, int wave) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = 16 * wave + 4 * i + (lane >> 4);
-        const int chunk = (lane & 15) ^ k_chunk_swz(row);
+    for (int i = 0; i < 2; ++i) {
+        const int row = 8 * wave + 4 * i + (lane >> 4);
+        o.k[i] = row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4);
+        o.v[i] = row * rs + (((lane & 15) ^ v_chunk_swz(row)) << 4);
+    }
+}
+
+// Stage the cursor's tile: K and V go straight from global memory into LDS
+// (buffer_load ... lds: 16 bytes per lane, landing at LDS base + lane * 16;
+// each lane loads the global chunk that belongs at its swizzled position).
+// The buffer resources cover only the run's rows of this tile, so rows past
+// the run's end read as zero (those keys are masked; zero V rows add nothing).
+__device__ inline void load_tile_bf16(const Cursor& c, const LaneOffsets& lo, int wave, char* stage) {
+    const int row0 = c.t * kBN;
+    const int nrows = c.n - row0 < kBN ? c.n - row0 : kBN;
+    const int64_t off = (int64_t)row0 * c.rs;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r4 = 8 * wave + 4 * i;      // first of the 4 rows this instruction fills
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            kr, (__attribute__((address_space(3))) void*)(stage + (16 * wave + 4 * i) * kKStride), 16,
-            row * rs + chunk * 16, 0, 0, 0);
-    }
-    const int vpiece = v_dim_group(tid), vrow = 4 * v_key_group(tid);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const i32x4 x = __builtin_amdgcn_raw_buffer_load_b128(vr, (vrow + i) * rs + vpiece * 16, 0, 0);
-        __builtin_memcpy(&t.v[i], &x, 16);
+            kr, (__attribute__((address_space(3))) void*)(stage + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void*)(stage + kTileBytes + r4 * kRowBytes), 16, lo.v[i], 0, 0, 0);
     }
 }
-
-__device__ inline void store_tile_bf16(char* stage, int tid, const TileRegs& t) {
-    char* vs = stage + kKBytes;
-    // transpose: this thread holds keys 4kg..4kg+3 of dims 8dg..8dg+7
-    const int dg = v_dim_group(tid);
-    const int col = 4 * swap01(v_key_group(tid));  // permuted key column of the 4 keys
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1;
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        Vec8 o;
-        o.w[0] = __builtin_amdgcn_perm(t.v[1].w[w], t.v[0].w[w], sel);
-        o.w[1] = __builtin_amdgcn_perm(t.v[3].w[w], t.v[2].w[w], sel);
-        const int row = 8 * dg + e;
-        *reinterpret_cast<Vec8*>(vs + row * kVStride + (((col >> 3) ^ vt_chunk_swz(row)) << 4) + (col & 7) * 2) = o;
-    }
-}
+constexpr int kLoadsPerTile = 4;  // vector memory instructions per thread per staged tile
 
 __device__ inline bf16x8 as_bf16x8(const Vec16& v) {
     bf16x8 r;
@@ -211,21 +242,21 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
     return u;
 }
 
-// Scheduling recipe for a region with N LDS operand reads each feeding QB
-// MFMAs: issue 4 reads, then alternate one MFMA group with one read, then the
+// Scheduling recipe for a region with N LDS operand reads each feeding one
+// MFMA: issue 4 reads, then alternate one MFMA with one read, then the
 // remaining MFMAs, so four reads are always in flight ahead of their use.
-template <int N, int QB>
+template <int N, int RPM>
 __device__ inline void pipeline_reads_and_mfma() {
     constexpr int kAhead = 4;
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read(s)
 #pragma unroll
     for (int i = 0; i < N - kAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read(s)
     }
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);
+    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
 }
 
 // Sum of the 8 bf16 values of a packed P operand, in fp32 (v_dot2 with ones):
@@ -243,17 +274,46 @@ __device__ inline float sum_bf16x8(const Vec16& v) {
     return acc;
 }
 
-// A workgroup of 4 waves owns 128*QB query rows: the G heads of a GQA group
-// stacked over 128*QB/G positions.  Each wave owns QB blocks of 32 rows, so
-// every K or V operand it reads from LDS feeds QB MFMAs; K and V operands of
-// a 32-key block are read into registers before the MFMAs that use them.
-template <int G, int QB>
-__global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) prefill_bf16_kernel(PrefillParams p) {
+__device__ inline uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// V^T operands of k-step ST (keys 16 ST .. 16 ST + 15) for the four dim
+// blocks, from the row-major V tile.  ds_read_b64_tr_b16 works on 16-lane
+// groups: group lane k reads 4 bf16 at its own address and lane i of the
+// group receives element i % 4 from each of group lanes i / 4, 4 + i / 4,
+// 8 + i / 4 and 12 + i / 4.  Group lane k reads key row base + k / 4 at
+// dims 32m + 16(q % 2) + 4(k % 4) (q = lane / 16), so lane i ends up with one
+// head dim (32m + lane % 32) of four consecutive keys; the reads at rows
+// +0 and +8 fill the two halves of the 8-key operand.  vaddr[m] already holds
+// the swizzled LDS address of row 4h + k / 4 (h = lane / 32) for dim block m;
+// the k-step and half become immediate offsets.  (The compiler cannot tell
+// these reads from the direct-to-LDS loads in flight and waits for those
+// first; the ring's depth still hides most of their latency.)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int ST>
+__device__ inline void read_vt(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, Vec16 (&va)[4]) {
+    const uint32_t ad[4] = {a0, a1, a2, a3};
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(ad[m] + ST * 16 * kRowBytes));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(ad[m] + ST * 16 * kRowBytes + 8 * kRowBytes));
+        __builtin_memcpy(&va[m].w[0], &lo, 8);
+        __builtin_memcpy(&va[m].w[2], &hi, 8);
+    }
+}
+
+// One workgroup of 8 waves per CU owns 256 query rows: the G heads of a GQA
+// group stacked over 256/G positions; wave w owns rows 32w .. 32w + 31, so
+// every key tile staged in LDS serves all heads of the group.
+template <int G>
+__global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams p) {
     constexpr int D = 128;
-    constexpr int QP = 128 * QB / G;  // positions per query tile
+    constexpr int QP = 32 * kWaves / G;  // positions per query tile
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
     // Workgroups are dealt to the 8 XCDs round-robin by linear id; give each
     // XCD a contiguous run of (sequence, kv head, q tile) work so the
@@ -270,23 +330,19 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) prefill_bf16_kernel(Pref
     const float c = p.scale_log2;                              // > 0 (checked on the host)
     const int w32 = p.W > (1 << 30) ? (1 << 30) : (int)p.W;    // a window beyond every position is the same
 
-    // this lane's query in each block: stacked row 32*(QB*wave + qb) + col
-    int head[QB];
-    int64_t my_t[QB], my_i[QB];
-    bool q_ok[QB];
-    Vec16 qreg[QB][8];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const int row = 32 * (QB * wave + qb) + col;
-        head[qb] = g * G + row / QP;
-        my_t[qb] = t0 + row % QP;
-        q_ok[qb] = my_t[qb] < p.seq_len;
-        my_i[qb] = p.start_pos + my_t[qb];
+    // this lane's query: stacked row 32*wave + col
+    const int qrow = 32 * wave + col;
+    const int head = g * G + qrow / QP;
+    const int64_t my_t = t0 + qrow % QP;
+    const bool q_ok = my_t < p.seq_len;
+    const int64_t my_i = p.start_pos + my_t;
+    Vec16 qreg[8];
+    {
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
-                             (((int64_t)b * p.seq_len + (q_ok[qb] ? my_t[qb] : 0)) * p.hq + head[qb]) * D;
+                             (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
-            qreg[qb][ks] = q_ok[qb] ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
+            qreg[ks] = q_ok ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
     }
 
     __shared__ TileWalk walk;
@@ -308,77 +364,98 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) prefill_bf16_kernel(Pref
     int total = 0;
     for (int r = 0; r < walk.n_ranges; ++r) total += walk.end[r] - walk.begin[r];
 
-    f32x16 o[QB][4];
+    // per-lane LDS offsets of the transposing V reads (row 4h + k/4 of the
+    // 16-lane group, dims 32m + 16(q%2) + 4(k%4)); rows differing by a
+    // multiple of 4 share the swizzle, so the k-step and half add constants
+    uint32_t vt_off[4];
+    {
+        const int q = lane >> 4, gp = lane & 15;
+        const int row = 4 * h + (gp >> 2);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) o[qb][m][r] = 0.f;
-    float m_run[QB], l_run[QB];
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        m_run[qb] = -INFINITY;
-        l_run[qb] = 0.f;
+        for (int m = 0; m < 4; ++m) {
+            const int dim = 32 * m + 16 * (q & 1) + 4 * (gp & 3);
+            vt_off[m] = row * kRowBytes + ((((dim >> 3) ^ v_chunk_swz(row)) << 4) | ((dim & 7) << 1));
+        }
     }
 
-    int cr = 0, ct = walk.n_ranges ? walk.begin[0] : 0;  // cursor (range, tile)
-    TileRegs regs;
+    f32x16 o[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+
+    // Tile pipeline: a ring of kStages LDS stages, one tile each.  While
+    // tile f is computed, tiles f + 1 .. f + 3 are resident or in flight.  At
+    // the end of iteration f every wave waits until its own loads of tile
+    // f + 1 landed and meets the others at the barrier; the stage of tile f
+    // is then free and receives tile f + 4.  Two cursors walk the tiles: one
+    // for the tile being computed, one for the next tile to stage.
+    Cursor cc, pc;
+    LaneOffsets lo;
     if (total > 0) {
-        load_tile_bf16(views[walk.run[0]], ct, tid, smem, regs);
-        store_tile_bf16(smem, tid, regs);
+        cursor_enter(cc, 0, walk, views);
+        cursor_enter(pc, 0, walk, views);
+        lane_offsets(lo, pc.rs, lane, wave);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS K loads landed
-    __syncthreads();
+    auto stage_next = [&](char* stage) {
+        load_tile_bf16(pc, lo, wave, stage);
+        if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets(lo, pc.rs, lane, wave);
+    };
+    auto sync_point = [&](int f) {
+        const int ahead = (total - 1 < f + 3 ? total - 1 : f + 3) - (f + 1);  // tiles issued beyond f + 1
+        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        tile_barrier();
+        if (f + kStages < total) stage_next(smem + (f % kStages) * kStageBytes);
+    };
+
+    // prologue: tiles 0 .. 3 in flight, wait for tile 0
+#pragma unroll
+    for (int f = 0; f < kStages; ++f)
+        if (f < total) stage_next(smem + f * kStageBytes);
+    static_assert(kStages == 4 && kLoadsPerTile == 4, "vmcnt immediates assume 4 stages of 4 loads");
+    if (total > 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else if (total > 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else if (total > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    tile_barrier();
 
     for (int f = 0; f < total; ++f) {
-        const int run_idx = walk.run[cr];
-        const int tile = ct;
-        // advance the cursor and prefetch the next tile
-        if (++ct >= walk.end[cr]) {
-            ++cr;
-            if (cr < walk.n_ranges) ct = walk.begin[cr];
-        }
-        const bool has_next = f + 1 < total;
-        if (has_next) load_tile_bf16(views[walk.run[cr]], ct, tid, smem + ((f + 1) & 1) * kStageBytes, regs);
-
-        const int row0 = tile * kBN;
-        const int run_n = views[run_idx].n;
-        const int nrows = run_n - row0 < kBN ? run_n - row0 : kBN;
-        const int64_t j0 = views[run_idx].pos0 + row0;
+        const int row0 = cc.t * kBN;
+        const int nrows = cc.n - row0 < kBN ? cc.n - row0 : kBN;
+        const int64_t j0 = cc.pos0 + row0;
         const int64_t j1 = j0 + nrows - 1;
         const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j1, p.P, p.W);
 
-        const char* stage = smem + (f & 1) * kStageBytes;
-        const char* ks_lds = stage;
-        const char* vs_lds = stage + kKBytes;
+        const char* ks_lds = smem + (f % kStages) * kStageBytes;
+        const char* vs_lds = ks_lds + kTileBytes;
         __builtin_amdgcn_sched_barrier(0);
 
-        // S^T = K Q^T (raw scores, unscaled).  The 16 K operands of the tile
-        // are read from LDS once and feed QB MFMAs each; the schedule keeps
-        // four reads in flight ahead of the MFMAs.
-        f32x16 s[QB][2];
+        // S^T = K Q^T (raw scores, unscaled); k-step outer so the two
+        // accumulators alternate; four K operand reads stay in flight
+        f32x16 s[2];
         {
             Vec16 ka[2][8];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
-                const int krow = 32 * mb + col;
+            for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-                    ka[mb][kk] = *reinterpret_cast<const Vec16*>(ks_lds + krow * kKStride + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
-            }
+                for (int mb = 0; mb < 2; ++mb) {
+                    const int krow = 32 * mb + col;
+                    ka[mb][kk] = *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
+                }
             const f32x16 zero = {};
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        s[qb][mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[mb][kk]), as_bf16x8(qreg[qb][kk]),
-                                                                            kk == 0 ? zero : s[qb][mb], 0, 0, 0);
-            pipeline_reads_and_mfma<16, QB>();
+                for (int mb = 0; mb < 2; ++mb)
+                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[mb][kk]), as_bf16x8(qreg[kk]),
+                                                                     kk == 0 ? zero : s[mb], 0, 0, 0);
+            pipeline_reads_and_mfma<16, 1>();
         }
         __builtin_amdgcn_sched_barrier(0);
+
         // Elementwise mask, straddling tiles only.  For this lane's query the
         // visible keys of the tile (tile-relative index kr) form at most two
         // intervals: [0, min(pj, hic + 1)) -- the prefix -- and
@@ -389,109 +466,99 @@ __global__ void __launch_bounds__(256, QB == 1 ? 2 : 1) prefill_bf16_kernel(Pref
         if (cls == kMasked) {
             const int64_t pj64 = p.P - j0;
             const int pj = pj64 > (1 << 30) ? (1 << 30) : (pj64 < -(1 << 30) ? -(1 << 30) : (int)pj64);
+            const int rel = (int)(my_i - j0);
+            const int hic = rel < nrows - 1 ? rel : nrows - 1;
+            const int a_hi = pj < hic + 1 ? pj : hic + 1;
+            const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
 #pragma unroll
-            for (int qb = 0; qb < QB; ++qb) {
-                const int rel = (int)(my_i[qb] - j0);
-                const int hic = rel < nrows - 1 ? rel : nrows - 1;
-                const int a_hi = pj < hic + 1 ? pj : hic + 1;
-                const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
+            for (int mb = 0; mb < 2; ++mb) {
+                const uint32_t bits = range_bits(0, a_hi - 32 * mb) | range_bits(b_lo - 32 * mb, hic + 1 - 32 * mb);
+                const uint32_t bits_h = bits >> (4 * h);  // this lane half's keys start at bit 4h
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const uint32_t bits = range_bits(0, a_hi - 32 * mb) | range_bits(b_lo - 32 * mb, hic + 1 - 32 * mb);
-                    const uint32_t bits_h = bits >> (4 * h);  // this lane half's keys start at bit 4h
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int keep = __builtin_amdgcn_sbfe((int)bits_h, 8 * (r >> 2) + (r & 3), 1);  // 0 or -1
-                        const uint32_t km = (uint32_t)keep;
-                        s[qb][mb][r] = __uint_as_float((km & __float_as_uint(s[qb][mb][r])) | (~km & 0xFF800000u));
-                    }
+                for (int r = 0; r < 16; ++r) {
+                    const uint32_t km = (uint32_t)__builtin_amdgcn_sbfe((int)bits_h, 8 * (r >> 2) + (r & 3), 1);
+                    s[mb][r] = __uint_as_float((km & __float_as_uint(s[mb][r])) | (~km & 0xFF800000u));
                 }
             }
         }
         // online softmax in raw-score units; exp2((s - m) * c) as one FMA + exp
-        Vec16 pb[QB][4];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
+        Vec16 pb[4];
+        {
             float tmax = -INFINITY;
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[qb][mb][r]);
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             // The exponent reference only moves when some row's maximum
             // exceeds it by more than 8 (log2 units): until then terms stay
             // below 2^8, and since l and O share the reference the result is
             // the same.
-            if (__any(tmax * c > m_run[qb] * c + 8.f)) {
-                const float m_new = fmaxf(m_run[qb], tmax);
-                const float alpha = m_run[qb] == -INFINITY ? 0.f : fast_exp2((m_run[qb] - m_new) * c);
-                l_run[qb] *= alpha;
+            if (__any(tmax * c > m_run * c + 8.f)) {
+                const float m_new = fmaxf(m_run, tmax);
+                const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c);
+                l_run *= alpha;
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) o[qb][m][r] *= alpha;
-                m_run[qb] = m_new;
+                    for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
+                m_run = m_new;
             }
-            const float mc = m_run[qb] == -INFINITY ? 0.f : m_run[qb] * c;
+            const float mc = m_run == -INFINITY ? 0.f : m_run * c;
             // P^T as B operand: k-step st covers keys 16 st .. 16 st + 15
 #pragma unroll
             for (int st = 0; st < 4; ++st) {
                 const int mb = st >> 1, base = 8 * (st & 1);
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    pb[qb][st].w[w] = pack_bf16x2(fast_exp2(fmaf(s[qb][mb][base + 2 * w], c, -mc)),
-                                                  fast_exp2(fmaf(s[qb][mb][base + 2 * w + 1], c, -mc)));
-                l_run[qb] += sum_bf16x8(pb[qb][st]);
+                    pb[st].w[w] = pack_bf16x2(fast_exp2(fmaf(s[mb][base + 2 * w], c, -mc)),
+                                              fast_exp2(fmaf(s[mb][base + 2 * w + 1], c, -mc)));
+                l_run += sum_bf16x8(pb[st]);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        // O^T += V^T P^T: the 16 V operands are read once and feed QB MFMAs
-        // each, with the same read-ahead schedule.
-        {
-            Vec16 va[4][4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int dim = 32 * m + col;
-                const char* vrow = vs_lds + dim * kVStride;
-                const int swz = vt_chunk_swz(dim);
-#pragma unroll
-                for (int st = 0; st < 4; ++st) va[m][st] = *reinterpret_cast<const Vec16*>(vrow + (((2 * st + h) ^ swz) << 4));
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int st = 0; st < 4; ++st)
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        o[qb][m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m][st]), as_bf16x8(pb[qb][st]),
-                                                                           o[qb][m], 0, 0, 0);
-            pipeline_reads_and_mfma<16, QB>();
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        if (has_next) store_tile_bf16(smem + ((f + 1) & 1) * kStageBytes, tid, regs);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // direct-to-LDS K loads landed
-        __syncthreads();
+        // O^T += V^T P^T.  The A operand (V^T: row = head dim, 8 keys in the
+        // order of P's k-step) comes from the row-major V tile with two
+        // transposing reads per dim block (see read_vt).
+        {
+            const uint32_t vb = lds_addr(vs_lds);
+            Vec16 va[4];
+            read_vt<0>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[0]), o[m], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            read_vt<1>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[1]), o[m], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            read_vt<2>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[2]), o[m], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            read_vt<3>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[3]), o[m], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sync_point(f);
+        cursor_next(cc, walk.n_ranges, walk, views);
     }
 
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (!q_ok) return;
+    const float inv = 1.f / l_tot;
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b * p.seq_len + my_t) * p.hq + head) * D;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float l_tot = l_run[qb] + __shfl_xor(l_run[qb], 32, 64);
-        if (!q_ok[qb]) continue;
-        const float inv = 1.f / l_tot;
-        uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + (((int64_t)b * p.seq_len + my_t[qb]) * p.hq + head[qb]) * D;
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                Vec8 w;
-                w.w[0] = pack_bf16x2(o[qb][m][4 * cc] * inv, o[qb][m][4 * cc + 1] * inv);
-                w.w[1] = pack_bf16x2(o[qb][m][4 * cc + 2] * inv, o[qb][m][4 * cc + 3] * inv);
-                *reinterpret_cast<Vec8*>(op + 32 * m + 8 * cc + 4 * h) = w;
-            }
-        if (p.lse && h == 0)
-            p.lse[((int64_t)b * p.seq_len + my_t[qb]) * p.hq + head[qb]] = (m_run[qb] * c + log2f(l_tot)) * kLn2;
-    }
+        for (int cc = 0; cc < 4; ++cc) {
+            Vec8 w;
+            w.w[0] = pack_bf16x2(o[m][4 * cc] * inv, o[m][4 * cc + 1] * inv);
+            w.w[1] = pack_bf16x2(o[m][4 * cc + 2] * inv, o[m][4 * cc + 3] * inv);
+            *reinterpret_cast<Vec8*>(op + 32 * m + 8 * cc + 4 * h) = w;
+        }
+    if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run * c + log2f(l_tot)) * kLn2;
 }
 
 // ----------------------------------------------------------------- fp32 debug
@@ -583,24 +650,30 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
     if (p.seq_len == 0) return hipSuccess;
     if (dtype == PS_BF16) {
         if (head_dim != 128) return hipErrorInvalidValue;
-        constexpr int QB = 1;
-        const int qp = 128 * QB / group;
+        const int qp = 32 * kWaves / group;
         dim3 grid((unsigned)(((p.seq_len + qp - 1) / qp) * p.hkv * p.batch));
-        const size_t lds = 2 * kStageBytes;
+        const size_t lds = (size_t)kStages * kStageBytes;
         const void* fn = nullptr;
         switch (group) {
-            case 1: fn = (const void*)prefill_bf16_kernel<1, QB>; break;
-            case 2: fn = (const void*)prefill_bf16_kernel<2, QB>; break;
-            case 4: fn = (const void*)prefill_bf16_kernel<4, QB>; break;
-            case 8: fn = (const void*)prefill_bf16_kernel<8, QB>; break;
+            case 1: fn = (const void*)prefill_bf16_kernel<1>; break;
+            case 2: fn = (const void*)prefill_bf16_kernel<2>; break;
+            case 4: fn = (const void*)prefill_bf16_kernel<4>; break;
+            case 8: fn = (const void*)prefill_bf16_kernel<8>; break;
             default: return hipErrorInvalidValue;
         }
-        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        // raise the dynamic LDS limit once per kernel (a host call, not per launch)
+        static bool lds_set[4] = {false, false, false, false};
+        const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+        if (!lds_set[gi]) {
+            const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+            lds_set[gi] = true;
+        }
         switch (group) {
-            case 1: hipLaunchKernelGGL((prefill_bf16_kernel<1, QB>), grid, dim3(256), lds, stream, p); break;
-            case 2: hipLaunchKernelGGL((prefill_bf16_kernel<2, QB>), grid, dim3(256), lds, stream, p); break;
-            case 4: hipLaunchKernelGGL((prefill_bf16_kernel<4, QB>), grid, dim3(256), lds, stream, p); break;
-            case 8: hipLaunchKernelGGL((prefill_bf16_kernel<8, QB>), grid, dim3(256), lds, stream, p); break;
+            case 1: hipLaunchKernelGGL(prefill_bf16_kernel<1>, grid, dim3(kThreads), lds, stream, p); break;
+            case 2: hipLaunchKernelGGL(prefill_bf16_kernel<2>, grid, dim3(kThreads), lds, stream, p); break;
+            case 4: hipLaunchKernelGGL(prefill_bf16_kernel<4>, grid, dim3(kThreads), lds, stream, p); break;
+            case 8: hipLaunchKernelGGL(prefill_bf16_kernel<8>, grid, dim3(kThreads), lds, stream, p); break;
         }
         return hipGetLastError();
     }
