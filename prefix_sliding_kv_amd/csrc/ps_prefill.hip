@@ -303,6 +303,15 @@ __device__ inline void read_vt(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a
     }
 }
 
+// tile_class for positions below 2^31, in 32-bit arithmetic: P and W at most
+// 2^31 - 1 and i0 >= 0 keep i0 - W and i1 - W in range.
+__device__ inline int tile_class32(int i0, int i1, int j0, int j1, int P, int W) {
+    if (j0 > i1 || (j0 >= P && j1 <= i0 - W)) return kSkip;
+    const int lo = j0 > P ? j0 : P;
+    if (j1 <= i0 && (j1 < P || lo > i1 - W)) return kFull;
+    return kMasked;
+}
+
 // One workgroup of 8 waves per CU owns 256 query rows: the G heads of a GQA
 // group stacked over 256/G positions; wave w owns rows 32w .. 32w + 31, so
 // every key tile staged in LDS serves all heads of the group.
@@ -323,19 +332,23 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     const int work = xcd_remap((int)blockIdx.x, n_qt * p.hkv * p.batch);
     const int qt = work % n_qt, g = (work / n_qt) % p.hkv, b = work / (n_qt * p.hkv);
 
-    const int64_t t0 = (int64_t)qt * QP;       // first chunk row of the tile
-    const int64_t t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
-    const int64_t i0 = p.start_pos + t0;
-    const int64_t i1 = p.start_pos + t_last;
+    // Positions are below 2^31 (the host rejects larger ones), so they are
+    // handled in 32 bits; P and W are clamped to 2^31 - 1, which changes no
+    // visibility decision for such positions.
+    const int t0 = qt * QP;                    // first chunk row of the tile
+    const int t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
+    const int i0 = (int)p.start_pos + t0;
+    const int i1 = (int)p.start_pos + t_last;
+    const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
+    const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
     const float c = p.scale_log2;                              // > 0 (checked on the host)
-    const int w32 = p.W > (1 << 30) ? (1 << 30) : (int)p.W;    // a window beyond every position is the same
 
     // this lane's query: stacked row 32*wave + col
     const int qrow = 32 * wave + col;
     const int head = g * G + qrow / QP;
-    const int64_t my_t = t0 + qrow % QP;
+    const int my_t = t0 + qrow % QP;
     const bool q_ok = my_t < p.seq_len;
-    const int64_t my_i = p.start_pos + my_t;
+    const int my_i = (int)p.start_pos + my_t;
     Vec16 qreg[8];
     {
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
@@ -348,7 +361,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     __shared__ TileWalk walk;
     __shared__ RunView views[kMaxRuns];
     if (tid == 0) {
-        plan_walk(p, i0, i1, walk);
+        plan_walk(p, (int64_t)i0, (int64_t)i1, walk);
         for (int r = 0; r < p.n_runs; ++r) {
             const KeyRun& run = p.runs[r];
             const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
@@ -425,36 +438,42 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     for (int f = 0; f < total; ++f) {
         const int row0 = cc.t * kBN;
         const int nrows = cc.n - row0 < kBN ? cc.n - row0 : kBN;
-        const int64_t j0 = cc.pos0 + row0;
-        const int64_t j1 = j0 + nrows - 1;
-        const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j1, p.P, p.W);
+        const int j0 = (int)cc.pos0 + row0;
+        const int j1 = j0 + nrows - 1;
+        const int cls = nrows < kBN ? kMasked : tile_class32(i0, i1, j0, j1, P32, w32);
 
         const char* ks_lds = smem + (f % kStages) * kStageBytes;
         const char* vs_lds = ks_lds + kTileBytes;
         __builtin_amdgcn_sched_barrier(0);
 
-        // S^T = K Q^T (raw scores, unscaled); k-step outer so the two
-        // accumulators alternate; four K operand reads stay in flight
+        // S^T = K Q^T (raw scores, unscaled).  k-step outer so the two
+        // accumulators alternate; the K operands of k-step kk + 2 are requested
+        // while k-step kk multiplies, and a scheduling fence after each k-step
+        // keeps that order (left alone, the compiler serialises the reads).
         f32x16 s[2];
         {
-            Vec16 ka[2][8];
+            auto kread = [&](int kk, int mb) {
+                const int krow = 32 * mb + col;
+                return *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
+            };
+            Vec16 ka[3][2];
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-                for (int mb = 0; mb < 2; ++mb) {
-                    const int krow = 32 * mb + col;
-                    ka[mb][kk] = *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
-                }
+                for (int mb = 0; mb < 2; ++mb) ka[kk][mb] = kread(kk, mb);
             const f32x16 zero = {};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
+            for (int kk = 0; kk < 8; ++kk) {
+                if (kk + 2 < 8) {
+#pragma unroll
+                    for (int mb = 0; mb < 2; ++mb) ka[(kk + 2) % 3][mb] = kread(kk + 2, mb);
+                }
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
-                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[mb][kk]), as_bf16x8(qreg[kk]),
+                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kk % 3][mb]), as_bf16x8(qreg[kk]),
                                                                      kk == 0 ? zero : s[mb], 0, 0, 0);
-            pipeline_reads_and_mfma<16, 1>();
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);
 
         // Elementwise mask, straddling tiles only.  For this lane's query the
         // visible keys of the tile (tile-relative index kr) form at most two
@@ -464,9 +483,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         // one 32-bit bitmap per 32-key block, and each score is kept or set to
         // -inf with a bit extract and a bitfield select (no per-element compares).
         if (cls == kMasked) {
-            const int64_t pj64 = p.P - j0;
-            const int pj = pj64 > (1 << 30) ? (1 << 30) : (pj64 < -(1 << 30) ? -(1 << 30) : (int)pj64);
-            const int rel = (int)(my_i - j0);
+            const int pj = P32 - j0;
+            const int rel = my_i - j0;
             const int hic = rel < nrows - 1 ? rel : nrows - 1;
             const int a_hi = pj < hic + 1 ? pj : hic + 1;
             const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
