@@ -16,6 +16,9 @@ Printed as one JSON line (rank 0, N=1):
   prefill      chunked prefill (28 layers, P=1024, W=8192, 4096 queries at
                98304..102399) and trainer forward (B=8, T=8192, P=256,
                W=2048): TFLOP/s on exact visible pairs and on unskipped tiles
+  baselines    full attention (W >= L) and a vanilla sliding window (P = 0)
+               through the same decode kernel at 8K / 32K / 128K, beside
+               Prefix Sliding (attention-only tok/s)
 """
 from __future__ import annotations
 
@@ -49,6 +52,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurements")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-baselines", action="store_true",
+                    help="skip the full-attention / vanilla-sliding-window comparison")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -176,6 +181,62 @@ def decode_bench(args, torch, ps, synth, np):
     cache.close()
     return dict(eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok, mean_launch_us=mean_launch_us,
                 flat=flat)
+
+
+def baselines_bench(torch, ps):
+    """Full attention (W >= L) and a vanilla sliding window (P = 0) through
+    the same decode kernel, beside Prefix Sliding: the shape of the pages'
+    comparison (attention only, 28 layers, batch 1, one captured graph per
+    cache, query at position L - 1).  Cache contents are random: the time
+    does not depend on them."""
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    rows = torch.zeros(1, dtype=torch.int32, device="cuda")
+    q = torch.randn(LAYERS, 1, HQ, D, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    lengths = (8192, 32768, 131072)
+
+    def rate(pcap, Pn, Wn, L):
+        cache = ps.Cache(LAYERS, 1, HQ, HKV, D, pcap, Wn, ps.PS_BF16)
+        for layer in range(LAYERS):
+            k, v = cache.kv(layer)
+            k.normal_()
+            v.normal_()
+        plen = torch.full((1,), Pn, dtype=torch.int32, device="cuda")
+        pos_t = torch.full((1,), L - 1, dtype=torch.int64, device="cuda")
+        batch = ps.SeqBatch(rows, plen, pos_t)
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            for layer in range(LAYERS):  # one eager pass before capture
+                ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None, scale, gs)
+            with torch.cuda.graph(g, stream=gs):
+                for layer in range(LAYERS):
+                    ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None, scale, gs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        reps = 10
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        del g
+        cache.close()
+        return round(1e3 / ms, 1)
+
+    res = {"workload": "decode attention only, 28 layers, batch 1, Hq=16, Hkv=8, d=128, query at L-1",
+           "full_attention": {}, "vanilla_sliding_window_w4096": {}, "prefix_sliding_p100_w4096": {}}
+    for L in lengths:
+        res["full_attention"][str(L)] = rate(0, 0, L, L)
+        res["vanilla_sliding_window_w4096"][str(L)] = rate(0, 0, W, L)
+        res["prefix_sliding_p100_w4096"][str(L)] = rate(P, P, W, L)
+    log(f"baselines tok/s: {res}")
+    return res
 
 
 def tile_flops(ps, q_lo, q_hi, key_hi, P, Wn, hq, d, tile=64):
@@ -353,6 +414,7 @@ def main():
     step_ms = dec["graph_ms"] if dec["graph_ok"] else dec["eager_ms"]
     value = 1e3 / step_ms
     pre = {} if args.no_prefill else prefill_bench(torch, ps, synth, np)
+    base_cmp = {} if args.no_baselines else baselines_bench(torch, ps)
     cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
     line = {
         "metric": METRIC,
@@ -380,6 +442,7 @@ def main():
         "eager_tok_s": round(1e3 / dec["eager_ms"], 1),
         "flat_cost_tok_s": dec["flat"],
         "prefill": pre,
+        "baselines": base_cmp,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
