@@ -19,6 +19,8 @@ Printed as one JSON line (rank 0, N=1):
   baselines    full attention (W >= L) and a vanilla sliding window (P = 0)
                through the same decode kernel at 8K / 32K / 128K, beside
                Prefix Sliding (attention-only tok/s)
+  batched_decode  64 ragged sequences (P ~ U[64,512], L ~ U[4K,128K]), one
+               token each per layer: tok/s and achieved HBM GB/s
 """
 from __future__ import annotations
 
@@ -239,6 +241,63 @@ def baselines_bench(torch, ps):
     return res
 
 
+def batched_bench(torch, ps, np):
+    """Batched ragged decode: 64 sequences, P_s ~ U[64, 512], length
+    L_s ~ U[4K, 128K] with four sequences not yet sliding (seeded), W = 4096,
+    28 layers, one decode token per sequence per layer (attention only, one
+    captured graph).  Cache contents are random: the time does not depend on
+    them.  Bytes = sum over sequences of 2*Hkv*d*min(L_s, P_s + W)*2 per layer."""
+    n, pcap = 64, 512
+    rng = np.random.default_rng(1000)
+    Ps = rng.integers(64, pcap + 1, size=n)
+    Ls = rng.integers(4096, TRACE + 1, size=n)
+    for s in range(4):
+        Ls[s] = rng.integers(4096, Ps[s] + W)
+    cache = ps.Cache(LAYERS, n, HQ, HKV, D, pcap, W, ps.PS_BF16)
+    for layer in range(LAYERS):
+        k, v = cache.kv(layer)
+        k.normal_()
+        v.normal_()
+    rows = torch.arange(n, dtype=torch.int32, device="cuda")
+    plen = torch.tensor(Ps, dtype=torch.int32, device="cuda")
+    pos_t = torch.tensor(Ls - 1, dtype=torch.int64, device="cuda")
+    batch = ps.SeqBatch(rows, plen, pos_t)
+    q = torch.randn(LAYERS, n, HQ, D, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    scale = 1.0 / math.sqrt(D)
+    stream = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        for layer in range(LAYERS):
+            ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None, scale, gs)
+        with torch.cuda.graph(g, stream=gs):
+            for layer in range(LAYERS):
+                ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None, scale, gs)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    nbytes = LAYERS * sum(2 * HKV * D * min(int(L), int(Pp) + W) * 2 for L, Pp in zip(Ls, Ps))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    res = {"workload": "64 sequences, P ~ U[64,512], L ~ U[4K,128K] (4 not yet sliding), W=4096, 28 layers, "
+                       "attention only",
+           "ms_per_step": round(ms, 4), "tok_s": round(n * 1e3 / ms, 1), "bytes_per_step": nbytes,
+           "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    log(f"batched ragged decode: {res}")
+    del g
+    cache.close()
+    return res
+
+
 def tile_flops(ps, q_lo, q_hi, key_hi, P, Wn, hq, d, tile=64):
     """Flops of unskipped 64x64 (query position, key position) tiles."""
     n = 0
@@ -415,6 +474,7 @@ def main():
     value = 1e3 / step_ms
     pre = {} if args.no_prefill else prefill_bench(torch, ps, synth, np)
     base_cmp = {} if args.no_baselines else baselines_bench(torch, ps)
+    batched = {} if args.no_baselines else batched_bench(torch, ps, np)
     cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
     line = {
         "metric": METRIC,
@@ -443,6 +503,7 @@ def main():
         "flat_cost_tok_s": dec["flat"],
         "prefill": pre,
         "baselines": base_cmp,
+        "batched_decode": batched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
