@@ -62,7 +62,7 @@ bool batch_ok(const ps_cache* c, const ps_seq_batch* b) {
 // smallest valid one.
 int auto_decode_rows(const ps_cache* c, int n_seqs) {
     const int r = ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
-    const int cand[] = {128 * r, 64 * r, 32 * r, 16 * r, 8 * r, 4 * r};
+    const int cand[] = {64 * r, 32 * r, 16 * r, 8 * r, 4 * r};
     int smallest = 0;
     for (int rows : cand) {
         if (!ps::decode_rows_valid(c->desc.dtype, c->desc.head_dim, rows)) continue;
@@ -106,6 +106,9 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     p.n_seqs = batch->n;
     const int rows = c->decode_rows > 0 ? c->decode_rows : auto_decode_rows(c, batch->n);
     const int group = c->desc.n_q_heads / c->desc.n_kv_heads;
+    // several workgroups per CU: the kernel marks its K/V loads non-temporal
+    const int64_t n_wg = (int64_t)batch->n * c->desc.n_kv_heads * ((c->rows_per_head + rows - 1) / rows);
+    p.stream_nt = n_wg >= 1024;
     return hip_status(ps::launch_decode(c->desc.dtype, c->desc.head_dim, group, rows, p, (hipStream_t)stream));
 }
 

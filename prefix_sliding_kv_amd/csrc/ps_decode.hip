@@ -107,6 +107,23 @@ __device__ inline float group_sum(float x) {
 }
 
 __device__ inline Vec16 load16(const void* p) { return *reinterpret_cast<const Vec16*>(p); }
+// The same load, optionally with the non-temporal hint (data read once, not
+// worth keeping in the caches).
+template <bool NT>
+__device__ inline Vec16 load16_stream(const void* p) {
+    if constexpr (NT) {
+        typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+        Vec16 r;
+        r.w[0] = x[0];
+        r.w[1] = x[1];
+        r.w[2] = x[2];
+        r.w[3] = x[3];
+        return r;
+    } else {
+        return load16(p);
+    }
+}
 
 // Split partials cross workgroups that may sit on different XCDs (separate
 // L2s): they are written and read with agent-scope atomic accesses, which
@@ -157,7 +174,7 @@ __device__ inline float rowgroup_max(float x) {
     return x;
 }
 
-template <typename T, int D, int G, int NW, int U>
+template <typename T, int D, int G, int NW, int U, bool NTL>
 __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     constexpr int NT = NW * 64;
     constexpr int VEC = Elem<T>::kPerVec;
@@ -223,8 +240,8 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         const bool is_new = fused && phys == new_phys;
         const T* kp = is_new ? knew_row : kbase + phys * D;
         const T* vp = is_new ? vnew_row : vbase + phys * D;
-        kr[u] = load16(kp + sub * VEC);
-        vr[u] = load16(vp + sub * VEC);
+        kr[u] = load16_stream<NTL>(kp + sub * VEC);
+        vr[u] = load16_stream<NTL>(vp + sub * VEC);
     }
 
     // Scores (log2 units): q.k over this lane's slice, summed over the row's
@@ -435,11 +452,11 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     }
 }
 
-template <typename T, int D, int G, int NW, int U>
+template <typename T, int D, int G, int NW, int U, bool NTL = false>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
     constexpr int R = NW * (64 / (D / Elem<T>::kPerVec)) * U;
     const dim3 grid((unsigned)((p.rows_per_head + R - 1) / R), (unsigned)p.hkv, (unsigned)p.n_seqs);
-    hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U>), grid, dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U, NTL>), grid, dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -454,7 +471,13 @@ hipError_t dispatch_rows(int rows, const DecodeParams& p, hipStream_t stream) {
     if (rows == 2 * r4) return launch_one<T, D, G, 4, 2>(p, stream);
     if (rows == r16) return launch_one<T, D, G, 16, 1>(p, stream);
     if (rows == 2 * r16) return launch_one<T, D, G, 8, 4>(p, stream);
-    if (rows == 4 * r16) return launch_one<T, D, G, 8, 8>(p, stream);
+    if (rows == 4 * r16) {
+        // many workgroups (several per CU) stream far more than the caches
+        // hold: mark the K/V loads non-temporal (a single sequence's few
+        // workgroups are latency-bound and measured faster without the hint)
+        if (p.stream_nt) return launch_one<T, D, G, 8, 8, true>(p, stream);
+        return launch_one<T, D, G, 8, 8>(p, stream);
+    }
     if (rows == 8 * r16) return launch_one<T, D, G, 16, 8>(p, stream);
     return hipErrorInvalidValue;
 }

@@ -73,6 +73,7 @@ struct DecodeParams {
     uint32_t* tickets;
     int32_t s_max;
     int32_t n_seqs;
+    int32_t stream_nt;     // nonzero: K/V loads carry the non-temporal hint
 };
 
 // Launch decode attention; rows_per_split chosen by the caller (host).
