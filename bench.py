@@ -298,13 +298,14 @@ def batched_bench(torch, ps, np):
     return res
 
 
-def tile_flops(ps, q_lo, q_hi, key_hi, P, Wn, hq, d, tile=64):
-    """Flops of unskipped 64x64 (query position, key position) tiles."""
+def tile_flops(ps, q_lo, q_hi, key_hi, P, Wn, hq, d, tile_q=128, tile_k=128):
+    """Flops of unskipped (query position, key position) tiles of the bf16
+    kernel's shape for GQA group 2: 128 positions (256 query rows) by 128 keys."""
     n = 0
-    for i0 in range(q_lo, q_hi, tile):
-        i1 = min(i0 + tile, q_hi) - 1
-        for j0 in range(0, key_hi, tile):
-            j1 = min(j0 + tile, key_hi) - 1
+    for i0 in range(q_lo, q_hi, tile_q):
+        i1 = min(i0 + tile_q, q_hi) - 1
+        for j0 in range(0, key_hi, tile_k):
+            j1 = min(j0 + tile_k, key_hi) - 1
             if ps.ps_tile_class(i0, i1, j0, j1, P, Wn) != 0:
                 n += (i1 - i0 + 1) * (j1 - j0 + 1)
     return 4.0 * d * hq * n

@@ -15,23 +15,24 @@
 //
 // bf16 path (head_dim 128): a workgroup of 8 waves owns 256 query rows, the
 // G heads of one GQA group stacked over 256/G positions, so every K/V tile
-// staged in LDS serves all heads that share it.  Per 64-key tile each wave
+// staged in LDS serves all heads that share it.  Per 128-key tile each wave
 // computes S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (a lane then holds 16
-// scores of a single query, so the online softmax needs one cross-lane step),
-// and O^T += V^T P^T with the same instruction, reading the V^T operand from
-// the row-major V tile with the transposing LDS read (ds_read_b64_tr_b16).
-// K and V tiles go from global memory straight into a 4-stage LDS ring
-// (buffer_load ... lds), three tiles ahead of the one being computed, one
-// barrier per tile.  The tile walk is kept in scalar registers and touches
-// LDS only at range boundaries.  fp32 path: a plain debug kernel with the
-// same tile walk and classification.
+// scores of a single query per 32-key block, so the online softmax needs one
+// cross-lane step), and O^T += V^T P^T with the same instruction, reading the
+// V^T operand from the row-major V tile with the transposing LDS read
+// (ds_read_b64_tr_b16); the exponentials of each 16-key step are made right
+// before its MFMAs.  K and V tiles go from global memory straight into two
+// LDS stages (buffer_load ... lds), the next tile loading while the current
+// one is computed, one barrier per tile.  The tile walk is kept in scalar
+// registers and touches LDS only at range boundaries.  fp32 path: a plain
+// debug kernel with 64-key tiles, the same walk and classification.
 #include "ps_internal.h"
 
 namespace ps {
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kBN = 64;  // keys per tile
+constexpr int kBN = 64;  // keys per tile of the fp32 debug kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -71,6 +72,7 @@ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x 
 // (every row has a term equal to 1 at its running reference).
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <int TILE>
 __device__ inline void plan_walk(const PrefillParams& p, int64_t i0, int64_t i1, TileWalk& w) {
     w.n_ranges = 0;
     for (int r = 0; r < p.n_runs; ++r) {
@@ -82,9 +84,9 @@ __device__ inline void plan_walk(const PrefillParams& p, int64_t i0, int64_t i1,
         // window part: positions in [i0 - W + 1, i1]
         const int64_t loB = clamp64(i0 - p.W + 1 - run.pos0, 0, n);
         const int64_t hiB = clamp64(i1 + 1 - run.pos0, 0, n);
-        const int endA = (int)((hiA + kBN - 1) / kBN);
-        int begB = (int)(loB / kBN);
-        const int endB = hiB > loB ? (int)((hiB + kBN - 1) / kBN) : 0;
+        const int endA = (int)((hiA + TILE - 1) / TILE);
+        int begB = (int)(loB / TILE);
+        const int endB = hiB > loB ? (int)((hiB + TILE - 1) / TILE) : 0;
         if (endA > 0) {
             w.run[w.n_ranges] = r;
             w.begin[w.n_ranges] = 0;
@@ -114,9 +116,10 @@ __device__ inline int xcd_remap(int id, int n) {
 
 constexpr int kWaves = 8;                // waves per workgroup (2 per SIMD, one workgroup per CU)
 constexpr int kThreads = kWaves * 64;
-constexpr int kStages = 4;               // LDS ring of key tiles; prefetch distance kStages - 1
+constexpr int kBNB = 128;                // keys per tile of the bf16 kernel
+constexpr int kStages = 2;               // LDS ring of key tiles
 constexpr int kRowBytes = 128 * 2;       // one K or V row (head_dim 128, bf16)
-constexpr int kTileBytes = kBN * kRowBytes;
+constexpr int kTileBytes = kBNB * kRowBytes;
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile then V tile
 
 // Both tiles are row-major (row = key, 256 bytes) with 16-byte chunks
@@ -191,15 +194,16 @@ __device__ inline bool cursor_next(Cursor& c, int n_ranges, const TileWalk& w, c
 }
 
 // Per-lane byte offsets, within a tile, of this lane's 16-byte pieces of the
-// direct-to-LDS loads (two K and two V instructions per wave and tile; wave w
-// fills rows 8w .. 8w + 7).  They depend on the run's row stride only.
+// direct-to-LDS loads (four K and four V instructions per wave and tile; wave
+// w fills rows 16w .. 16w + 15).  They depend on the run's row stride only.
+constexpr int kLoadsPerWave = kBNB / 8 / 4;  // 4-row instructions per wave for K (and for V)
 struct LaneOffsets {
-    int k[2], v[2];
+    int k[kLoadsPerWave], v[kLoadsPerWave];
 };
 __device__ inline void lane_offsets(LaneOffsets& o, int rs, int lane, int wave) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int row = 8 * wave + 4 * i + (lane >> 4);
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int row = (kBNB / 8) * wave + 4 * i + (lane >> 4);
         o.k[i] = row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4);
         o.v[i] = row * rs + (((lane & 15) ^ v_chunk_swz(row)) << 4);
     }
@@ -211,21 +215,21 @@ __device__ inline void lane_offsets(LaneOffsets& o, int rs, int lane, int wave) 
 // The buffer resources cover only the run's rows of this tile, so rows past
 // the run's end read as zero (those keys are masked; zero V rows add nothing).
 __device__ inline void load_tile_bf16(const Cursor& c, const LaneOffsets& lo, int wave, char* stage) {
-    const int row0 = c.t * kBN;
-    const int nrows = c.n - row0 < kBN ? c.n - row0 : kBN;
+    const int row0 = c.t * kBNB;
+    const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
     const int64_t off = (int64_t)row0 * c.rs;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int r4 = 8 * wave + 4 * i;      // first of the 4 rows this instruction fills
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int r4 = (kBNB / 8) * wave + 4 * i;  // first of the 4 rows this instruction fills
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kr, (__attribute__((address_space(3))) void*)(stage + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             vr, (__attribute__((address_space(3))) void*)(stage + kTileBytes + r4 * kRowBytes), 16, lo.v[i], 0, 0, 0);
     }
 }
-constexpr int kLoadsPerTile = 4;  // vector memory instructions per thread per staged tile
+constexpr int kLoadsPerTile = 2 * kLoadsPerWave;  // vector memory instructions per thread per staged tile
 
 __device__ inline bf16x8 as_bf16x8(const Vec16& v) {
     bf16x8 r;
@@ -291,13 +295,12 @@ __device__ inline uint32_t lds_addr(const char* p) {
 // these reads from the direct-to-LDS loads in flight and waits for those
 // first; the ring's depth still hides most of their latency.)
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-template <int ST>
-__device__ inline void read_vt(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, Vec16 (&va)[4]) {
+__device__ inline void read_vt(int st, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, Vec16 (&va)[4]) {
     const uint32_t ad[4] = {a0, a1, a2, a3};
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(ad[m] + ST * 16 * kRowBytes));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(ad[m] + ST * 16 * kRowBytes + 8 * kRowBytes));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(ad[m] + st * 16 * kRowBytes));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(uintptr_t)(ad[m] + st * 16 * kRowBytes + 8 * kRowBytes));
         __builtin_memcpy(&va[m].w[0], &lo, 8);
         __builtin_memcpy(&va[m].w[2], &hi, 8);
     }
@@ -361,7 +364,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     __shared__ TileWalk walk;
     __shared__ RunView views[kMaxRuns];
     if (tid == 0) {
-        plan_walk(p, (int64_t)i0, (int64_t)i1, walk);
+        plan_walk<kBNB>(p, (int64_t)i0, (int64_t)i1, walk);
         for (int r = 0; r < p.n_runs; ++r) {
             const KeyRun& run = p.runs[r];
             const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
@@ -398,12 +401,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
     float m_run = -INFINITY, l_run = 0.f;
 
-    // Tile pipeline: a ring of kStages LDS stages, one tile each.  While
-    // tile f is computed, tiles f + 1 .. f + 3 are resident or in flight.  At
-    // the end of iteration f every wave waits until its own loads of tile
-    // f + 1 landed and meets the others at the barrier; the stage of tile f
-    // is then free and receives tile f + 4.  Two cursors walk the tiles: one
-    // for the tile being computed, one for the next tile to stage.
+    // Tile pipeline: two LDS stages of one 128-key tile each.  While tile f is
+    // computed, tile f + 1 is resident or in flight.  At the end of iteration
+    // f every wave waits until its own loads of tile f + 1 landed and meets
+    // the others at the barrier; the stage of tile f is then free and
+    // receives tile f + 2.  Two cursors walk the tiles: one for the tile being
+    // computed, one for the next tile to stage.
     Cursor cc, pc;
     LaneOffsets lo;
     if (total > 0) {
@@ -415,65 +418,44 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         load_tile_bf16(pc, lo, wave, stage);
         if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets(lo, pc.rs, lane, wave);
     };
-    auto sync_point = [&](int f) {
-        const int ahead = (total - 1 < f + 3 ? total - 1 : f + 3) - (f + 1);  // tiles issued beyond f + 1
-        if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-        else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        tile_barrier();
-        if (f + kStages < total) stage_next(smem + (f % kStages) * kStageBytes);
-    };
+    static_assert(kStages == 2 && kLoadsPerTile == 8, "vmcnt immediates assume 2 stages of 8 loads");
 
-    // prologue: tiles 0 .. 3 in flight, wait for tile 0
-#pragma unroll
-    for (int f = 0; f < kStages; ++f)
-        if (f < total) stage_next(smem + f * kStageBytes);
-    static_assert(kStages == 4 && kLoadsPerTile == 4, "vmcnt immediates assume 4 stages of 4 loads");
-    if (total > 3) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-    else if (total > 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (total > 1) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // prologue: tiles 0 and 1 in flight, wait for tile 0
+    if (total > 0) stage_next(smem);
+    if (total > 1) {
+        stage_next(smem + kStageBytes);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
     tile_barrier();
 
+    constexpr int kMB = kBNB / 32;  // 32-key score blocks per tile
+    constexpr int kST = kBNB / 16;  // 16-key k-steps of P.V per tile
     for (int f = 0; f < total; ++f) {
-        const int row0 = cc.t * kBN;
-        const int nrows = cc.n - row0 < kBN ? cc.n - row0 : kBN;
+        const int row0 = cc.t * kBNB;
+        const int nrows = cc.n - row0 < kBNB ? cc.n - row0 : kBNB;
         const int j0 = (int)cc.pos0 + row0;
         const int j1 = j0 + nrows - 1;
-        const int cls = nrows < kBN ? kMasked : tile_class32(i0, i1, j0, j1, P32, w32);
-
-        const char* ks_lds = smem + (f % kStages) * kStageBytes;
-        const char* vs_lds = ks_lds + kTileBytes;
+        const int cls = nrows < kBNB ? kMasked : tile_class32(i0, i1, j0, j1, P32, w32);
+        const char* ks_lds = smem + (f & 1) * kStageBytes;
         __builtin_amdgcn_sched_barrier(0);
 
-        // S^T = K Q^T (raw scores, unscaled).  k-step outer so the two
-        // accumulators alternate; the K operands of k-step kk + 2 are requested
-        // while k-step kk multiplies, and a scheduling fence after each k-step
-        // keeps that order (left alone, the compiler serialises the reads).
-        f32x16 s[2];
+        // S^T = K Q^T (raw scores, unscaled), one 32-key block per accumulator
+        f32x16 s[kMB];
         {
-            auto kread = [&](int kk, int mb) {
-                const int krow = 32 * mb + col;
-                return *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
-            };
-            Vec16 ka[3][2];
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb) ka[kk][mb] = kread(kk, mb);
             const f32x16 zero = {};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) {
-                if (kk + 2 < 8) {
+            for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-                    for (int mb = 0; mb < 2; ++mb) ka[(kk + 2) % 3][mb] = kread(kk + 2, mb);
-                }
-#pragma unroll
-                for (int mb = 0; mb < 2; ++mb)
-                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[kk % 3][mb]), as_bf16x8(qreg[kk]),
+                for (int mb = 0; mb < kMB; ++mb) {
+                    const int krow = 32 * mb + col;
+                    const Vec16 ka = *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
+                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qreg[kk]),
                                                                      kk == 0 ? zero : s[mb], 0, 0, 0);
-            }
+                }
         }
+        __builtin_amdgcn_sched_barrier(0);
 
         // Elementwise mask, straddling tiles only.  For this lane's query the
         // visible keys of the tile (tile-relative index kr) form at most two
@@ -489,7 +471,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
             const int a_hi = pj < hic + 1 ? pj : hic + 1;
             const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) {
+            for (int mb = 0; mb < kMB; ++mb) {
                 const uint32_t bits = range_bits(0, a_hi - 32 * mb) | range_bits(b_lo - 32 * mb, hic + 1 - 32 * mb);
                 const uint32_t bits_h = bits >> (4 * h);  // this lane half's keys start at bit 4h
 #pragma unroll
@@ -499,12 +481,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
                 }
             }
         }
-        // online softmax in raw-score units; exp2((s - m) * c) as one FMA + exp
-        Vec16 pb[4];
+        // online softmax in raw-score units: the reference first
         {
             float tmax = -INFINITY;
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
@@ -514,7 +495,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
             // the same.
             if (__any(tmax * c > m_run * c + 8.f)) {
                 const float m_new = fmaxf(m_run, tmax);
-                const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * c);
+                const float alpha = fast_exp2(m_run == -INFINITY ? -INFINITY : (m_run - m_new) * c);
                 l_run *= alpha;
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
@@ -522,44 +503,41 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
                     for (int r = 0; r < 16; ++r) o[m][r] *= alpha;
                 m_run = m_new;
             }
-            const float mc = m_run == -INFINITY ? 0.f : m_run * c;
-            // P^T as B operand: k-step st covers keys 16 st .. 16 st + 15
+        }
+        const float mc = m_run == -INFINITY ? 0.f : m_run * c;
+        __builtin_amdgcn_sched_barrier(0);
+
+        // O^T += V^T P^T, k-step by k-step.  P^T of k-step st (keys 16 st ..
+        // 16 st + 15, exp2((s - m) * c) packed to bf16) is made right before
+        // its four MFMAs, so the exponentials of one k-step run beside the
+        // MFMAs of the previous one.  The A operand (V^T: row = head dim, 8
+        // keys in the order of P's k-step) comes from the row-major V tile with
+        // two transposing reads per dim block (see read_vt).
+        {
+            const uint32_t vb = lds_addr(ks_lds + kTileBytes);
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int st = 0; st < kST; ++st) {
                 const int mb = st >> 1, base = 8 * (st & 1);
+                Vec16 pb;
 #pragma unroll
                 for (int w = 0; w < 4; ++w)
-                    pb[st].w[w] = pack_bf16x2(fast_exp2(fmaf(s[mb][base + 2 * w], c, -mc)),
-                                              fast_exp2(fmaf(s[mb][base + 2 * w + 1], c, -mc)));
-                l_run += sum_bf16x8(pb[st]);
+                    pb.w[w] = pack_bf16x2(fast_exp2(fmaf(s[mb][base + 2 * w], c, -mc)),
+                                          fast_exp2(fmaf(s[mb][base + 2 * w + 1], c, -mc)));
+                l_run += sum_bf16x8(pb);
+                Vec16 va[4];
+                read_vt(st, vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb), o[m], 0, 0, 0);
             }
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // O^T += V^T P^T.  The A operand (V^T: row = head dim, 8 keys in the
-        // order of P's k-step) comes from the row-major V tile with two
-        // transposing reads per dim block (see read_vt).
-        {
-            const uint32_t vb = lds_addr(vs_lds);
-            Vec16 va[4];
-            read_vt<0>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[0]), o[m], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            read_vt<1>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[1]), o[m], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            read_vt<2>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[2]), o[m], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            read_vt<3>(vb + vt_off[0], vb + vt_off[1], vb + vt_off[2], vb + vt_off[3], va);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) o[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[m]), as_bf16x8(pb[3]), o[m], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        sync_point(f);
+        // tile f + 1 must have landed before anyone reads it; then the stage
+        // of tile f takes tile f + 2
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        tile_barrier();
+        if (f + kStages < total) stage_next(smem + (f & 1) * kStageBytes);
         cursor_next(cc, walk.n_ranges, walk, views);
     }
 
@@ -607,7 +585,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     }
     float m_run = -INFINITY, l_run = 0.f;
 
-    if (tid == 0) plan_walk(p, i0, i1, walk);
+    if (tid == 0) plan_walk<kBN>(p, i0, i1, walk);
     __syncthreads();
     for (int rr = 0; rr < walk.n_ranges; ++rr) {
         const KeyRun& run = p.runs[walk.run[rr]];
