@@ -194,16 +194,20 @@ __device__ inline bool cursor_next(Cursor& c, int n_ranges, const TileWalk& w, c
 }
 
 // Per-lane byte offsets, within a tile, of this lane's 16-byte pieces of the
-// direct-to-LDS loads (four K and four V instructions per wave and tile; wave
-// w fills rows 16w .. 16w + 15).  They depend on the run's row stride only.
-constexpr int kLoadsPerWave = kBNB / 8 / 4;  // 4-row instructions per wave for K (and for V)
+// direct-to-LDS loads.  Only waves 0-3 stage tiles (eight K and eight V
+// instructions per wave and tile; wave w fills rows 32w .. 32w + 31): issuing
+// these loads stalls a wave for a while, and waves 4-7, which share the SIMDs
+// with 0-3, keep the MFMA pipes busy meanwhile.  The offsets depend on the
+// run's row stride only.
+constexpr int kLoadWaves = 4;
+constexpr int kLoadsPerWave = kBNB / kLoadWaves / 4;  // 4-row instructions per loading wave for K (and for V)
 struct LaneOffsets {
     int k[kLoadsPerWave], v[kLoadsPerWave];
 };
 __device__ inline void lane_offsets(LaneOffsets& o, int rs, int lane, int wave) {
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int row = (kBNB / 8) * wave + 4 * i + (lane >> 4);
+        const int row = (kBNB / kLoadWaves) * (wave & (kLoadWaves - 1)) + 4 * i + (lane >> 4);
         o.k[i] = row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4);
         o.v[i] = row * rs + (((lane & 15) ^ v_chunk_swz(row)) << 4);
     }
@@ -220,9 +224,10 @@ __device__ inline void load_tile_bf16(const Cursor& c, const LaneOffsets& lo, in
     const int64_t off = (int64_t)row0 * c.rs;
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
+    if (wave >= kLoadWaves) return;
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
-        const int r4 = (kBNB / 8) * wave + 4 * i;  // first of the 4 rows this instruction fills
+        const int r4 = (kBNB / kLoadWaves) * wave + 4 * i;  // first of the 4 rows this instruction fills
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             kr, (__attribute__((address_space(3))) void*)(stage + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -418,13 +423,13 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         load_tile_bf16(pc, lo, wave, stage);
         if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets(lo, pc.rs, lane, wave);
     };
-    static_assert(kStages == 2 && kLoadsPerTile == 8, "vmcnt immediates assume 2 stages of 8 loads");
+    static_assert(kStages == 2 && kLoadsPerTile == 16, "vmcnt immediates assume 2 stages of 16 loads");
 
     // prologue: tiles 0 and 1 in flight, wait for tile 0
     if (total > 0) stage_next(smem);
     if (total > 1) {
         stage_next(smem + kStageBytes);
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
     } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
