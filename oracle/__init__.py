@@ -61,6 +61,10 @@ def _load():
         lib.oracle_attention.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
                                          i64, vp, vp, vp, i64, i64, ctypes.c_double, vp, vp,
                                          ctypes.c_int]
+        lib.oracle_attention_bwd.restype = None
+        lib.oracle_attention_bwd.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
+                                             i64, vp, vp, vp, vp, i64, i64, ctypes.c_double,
+                                             vp, vp, vp, ctypes.c_int]
         _lib = lib
     return _lib
 
@@ -110,6 +114,40 @@ def attention(q, qpos, k, v, kpos, P: int, W: int, scale: float | None = None,
                              v.ctypes.data, kpos.ctypes.data, P, W, float(scale), out.ctypes.data,
                              lse.ctypes.data, int(threads))
     return out, lse
+
+
+def attention_bwd(q, qpos, k, v, kpos, dout, P: int, W: int, scale: float | None = None,
+                  threads: int = 1):
+    """Gradient of ``attention`` with respect to q, k and v.
+
+    Same conventions as ``attention``; ``dout`` [nq][hq][d] is the gradient of
+    the output.  Returns (dq [nq][hq][d], dk [nk][hkv][d], dv [nk][hkv][d]),
+    float64.  The trainer backpropagates through the masked attention
+    (agihunt.info summary, paragraph on RL; njhaofan.com article, passage on
+    truncated backpropagation); the formulas are the derivative of the
+    definition (see oracle.c).
+    """
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int64).reshape(-1))
+    kpos = np.ascontiguousarray(np.asarray(kpos, dtype=np.int64).reshape(-1))
+    nq, hq, d = q.shape
+    nk, hkv, dk_ = k.shape
+    if dk_ != d or v.shape != k.shape or dout.shape != q.shape or qpos.size != nq or kpos.size != nk:
+        raise ValueError("oracle.attention_bwd: inconsistent shapes")
+    if hq % hkv != 0:
+        raise ValueError("oracle.attention_bwd: Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.empty((nq, hq, d), dtype=np.float64)
+    dk = np.empty((nk, hkv, d), dtype=np.float64)
+    dv = np.empty((nk, hkv, d), dtype=np.float64)
+    _load().oracle_attention_bwd(nq, hq, hkv, d, q.ctypes.data, qpos.ctypes.data, nk, k.ctypes.data,
+                                 v.ctypes.data, kpos.ctypes.data, dout.ctypes.data, P, W, float(scale),
+                                 dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
+    return dq, dk, dv
 
 
 def lse_merge(parts):

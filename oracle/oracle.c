@@ -130,3 +130,88 @@ int oracle_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P,
     if (vis == tot) return 1;
     return 2;
 }
+
+/*
+ * Gradient of oracle_attention with respect to q, k and v, for the trainer
+ * side (the agihunt.info summary, paragraph on RL, and the njhaofan.com
+ * article, passage on truncated backpropagation: the trainer takes the last
+ * few windows of a rollout and backpropagates through the masked attention).
+ * The pages give no formula; this is the derivative of the definition above,
+ * written out.  For query (t, h), g = floor(h*hkv/hq), visible keys J,
+ * p_j = softmax_J(s)_j, upstream gradient dO = dout[t][h]:
+ *   dp_j = <dO, v[j][g]>
+ *   D    = sum_{j in J} p_j dp_j            (= <dO, out[t][h]>)
+ *   ds_j = p_j (dp_j - D)
+ *   dq[t][h]  += scale * sum_j ds_j k[j][g]
+ *   dk[j][g]  += scale * ds_j q[t][h]
+ *   dv[j][g]  += p_j dO
+ * Hidden keys get nothing (they are skipped).  Outputs are overwritten.
+ * Parallel over kv heads: every write of one thread stays in its kv head.
+ */
+void oracle_attention_bwd(int64_t nq, int hq, int hkv, int d,
+                          const float* q, const int64_t* qpos,
+                          int64_t nk, const float* k, const float* v, const int64_t* kpos,
+                          const float* dout, int64_t P, int64_t W, double scale,
+                          double* dq, double* dk, double* dv, int n_threads) {
+    for (int64_t x = 0; x < nq * hq * (int64_t)d; ++x) dq[x] = 0.0;
+    for (int64_t x = 0; x < nk * hkv * (int64_t)d; ++x) { dk[x] = 0.0; dv[x] = 0.0; }
+#pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
+    for (int g = 0; g < hkv; ++g) {
+        for (int64_t t = 0; t < nq; ++t)
+            for (int h = 0; h < hq; ++h) {
+                if ((int)(((int64_t)h * hkv) / hq) != g) continue;
+                const int64_t i = qpos[t];
+                const float* qr = q + (t * hq + h) * (int64_t)d;
+                const float* dor = dout + (t * hq + h) * (int64_t)d;
+                double* dqr = dq + (t * hq + h) * (int64_t)d;
+                /* scores and their maximum */
+                double m = -INFINITY;
+                int64_t nvis = 0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    if (!oracle_visible(i, kpos[j], P, W)) continue;
+                    const float* kr = k + (j * hkv + g) * (int64_t)d;
+                    double s = 0.0;
+                    for (int e = 0; e < d; ++e) s += (double)qr[e] * (double)kr[e];
+                    s *= scale;
+                    if (s > m) m = s;
+                    ++nvis;
+                }
+                if (nvis == 0) continue;
+                /* probabilities p_j and dp_j over the visible keys */
+                double l = 0.0, D = 0.0;
+                for (int64_t j = 0; j < nk; ++j) {
+                    if (!oracle_visible(i, kpos[j], P, W)) continue;
+                    const float* kr = k + (j * hkv + g) * (int64_t)d;
+                    double s = 0.0;
+                    for (int e = 0; e < d; ++e) s += (double)qr[e] * (double)kr[e];
+                    l += exp(s * scale - m);
+                }
+                for (int64_t j = 0; j < nk; ++j) {
+                    if (!oracle_visible(i, kpos[j], P, W)) continue;
+                    const float* kr = k + (j * hkv + g) * (int64_t)d;
+                    const float* vr = v + (j * hkv + g) * (int64_t)d;
+                    double s = 0.0, dpj = 0.0;
+                    for (int e = 0; e < d; ++e) s += (double)qr[e] * (double)kr[e];
+                    for (int e = 0; e < d; ++e) dpj += (double)dor[e] * (double)vr[e];
+                    D += exp(s * scale - m) / l * dpj;
+                }
+                for (int64_t j = 0; j < nk; ++j) {
+                    if (!oracle_visible(i, kpos[j], P, W)) continue;
+                    const float* kr = k + (j * hkv + g) * (int64_t)d;
+                    const float* vr = v + (j * hkv + g) * (int64_t)d;
+                    double* dkr = dk + (j * hkv + g) * (int64_t)d;
+                    double* dvr = dv + (j * hkv + g) * (int64_t)d;
+                    double s = 0.0, dpj = 0.0;
+                    for (int e = 0; e < d; ++e) s += (double)qr[e] * (double)kr[e];
+                    for (int e = 0; e < d; ++e) dpj += (double)dor[e] * (double)vr[e];
+                    const double pj = exp(s * scale - m) / l;
+                    const double dsj = pj * (dpj - D);
+                    for (int e = 0; e < d; ++e) {
+                        dqr[e] += scale * dsj * (double)kr[e];
+                        dkr[e] += scale * dsj * (double)qr[e];
+                        dvr[e] += pj * (double)dor[e];
+                    }
+                }
+            }
+    }
+}

@@ -328,3 +328,82 @@ def test_generator_bf16_is_round_to_nearest_of_float():
     # directly, which can only differ on float32 double-rounding ties
     assert np.mean(ref != b) < 1e-3
     np.testing.assert_allclose(b, f, rtol=2 ** -8, atol=0)
+
+
+# ------------------------------------------------------------ trainer backward
+def _grid(x, step=2.0 ** -10):
+    """Round to a grid so that +-step perturbations stay exact in float32."""
+    return np.round(np.asarray(x, np.float64) / step) * step
+
+
+@pytest.mark.parametrize("P,W,L,hq,hkv,d", [
+    (2, 3, 7, 2, 1, 4),     # prefix + window, GQA group 2
+    (0, 4, 6, 2, 2, 4),     # vanilla sliding window, one head per group
+    (3, 1, 6, 1, 1, 4),     # window of one: prefix + self
+])
+def test_attention_bwd_matches_finite_differences(P, W, L, hq, hkv, d):
+    """Central differences of the forward oracle with L = sum(dout * out)."""
+    pos, q, k, v = rand_qkv(11, L, hq, hkv, d)
+    q, k, v = _grid(q), _grid(k), _grid(v)
+    dout = _grid(synth.rows(12, synth.V, 0, 0, pos, hq, d, 0.0, synth.F32))
+    dq, dk, dv = oracle.attention_bwd(q, pos, k, v, pos, dout, P, W)
+    eps = 2.0 ** -10
+
+    def loss(qq, kk, vv):
+        out, _ = oracle.attention(qq, pos, kk, vv, pos, P, W)
+        return float(np.sum(out * dout))
+
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            hi, lo = arr.copy(), arr.copy()
+            hi[idx] += eps
+            lo[idx] -= eps
+            args_hi = {"q": (hi, k, v), "k": (q, hi, v), "v": (q, k, hi)}[name]
+            args_lo = {"q": (lo, k, v), "k": (q, lo, v), "v": (q, k, lo)}[name]
+            num[idx] = (loss(*args_hi) - loss(*args_lo)) / (2 * eps)
+        np.testing.assert_allclose(grad, num, rtol=0, atol=2e-5, err_msg=name)
+
+
+@pytest.mark.parametrize("P,W,L,hq,hkv,d", [
+    (5, 7, 30, 4, 2, 16),
+    (0, 30, 24, 2, 1, 8),   # W >= L, no prefix: plain causal
+    (12, 4, 40, 2, 2, 8),
+])
+def test_attention_bwd_matches_sdpa_autograd(P, W, L, hq, hkv, d):
+    """torch autograd through SDPA (float64, CPU) under the simulated mask."""
+    pos, q, k, v = rand_qkv(13, L, hq, hkv, d)
+    dout = synth.rows(14, synth.V, 0, 0, pos, hq, d, 0.0, synth.F32)
+    dq, dk, dv = oracle.attention_bwd(q, pos, k, v, pos, dout, P, W, threads=2)
+    rep = hq // hkv
+    qt = torch.from_numpy(np.asarray(q, np.float64)).permute(1, 0, 2).requires_grad_()
+    kt = torch.from_numpy(np.asarray(k, np.float64)).permute(1, 0, 2).requires_grad_()
+    vt = torch.from_numpy(np.asarray(v, np.float64)).permute(1, 0, 2).requires_grad_()
+    mask = torch.from_numpy(mask_from_simulation(L, P, W))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt.repeat_interleave(rep, 0), vt.repeat_interleave(rep, 0), attn_mask=mask)
+    o.backward(torch.from_numpy(np.asarray(dout, np.float64)).permute(1, 0, 2))
+    np.testing.assert_allclose(dq, qt.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, kt.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, vt.grad.permute(1, 0, 2).numpy(), rtol=0, atol=1e-11)
+
+
+def test_attention_bwd_sum_invariants():
+    """Softmax weights sum to one over the visible keys, so the value
+    gradients of a kv head sum to the output gradients of its query heads,
+    and the score gradients of every query sum to zero, so the key gradients
+    of a kv head sum to zero."""
+    P, W, L, hq, hkv, d = 4, 6, 33, 4, 2, 8
+    pos, q, k, v = rand_qkv(15, L, hq, hkv, d)
+    dout = synth.rows(16, synth.V, 0, 0, pos, hq, d, 0.0, synth.F32)
+    dq, dk, dv = oracle.attention_bwd(q, pos, k, v, pos, dout, P, W)
+    rep = hq // hkv
+    for g in range(hkv):
+        want = np.asarray(dout, np.float64)[:, g * rep:(g + 1) * rep, :].sum(axis=(0, 1))
+        np.testing.assert_allclose(dv[:, g, :].sum(axis=0), want, rtol=0, atol=1e-10)
+        np.testing.assert_allclose(dk[:, g, :].sum(axis=0), 0.0, rtol=0, atol=1e-10)
+    # a key no query can see (future of every query) gets no gradient
+    k2 = np.concatenate([k, k[:1]]); v2 = np.concatenate([v, v[:1] + 5.0])
+    kpos2 = np.concatenate([pos, [L + 10]])
+    _, dk2, dv2 = oracle.attention_bwd(q, pos, k2, v2, kpos2, dout, P, W)
+    assert np.all(dk2[-1] == 0.0) and np.all(dv2[-1] == 0.0)
