@@ -206,6 +206,55 @@ typedef struct {
 
 int ps_prefill_attn(const ps_prefill_args* args, void* stream);
 
+/* Trainer-side backward of ps_prefill_attn in trainer mode (cache == NULL):
+ * the gradients dq, dk, dv of the masked attention given the upstream
+ * gradient dout.  The trainer backpropagates through the last windows of a
+ * rollout (agihunt.info summary, paragraph on RL; njhaofan.com article,
+ * passage on truncated backpropagation); the pages give no formula, this is
+ * the derivative of the forward: with P the softmax over the visible keys,
+ * Delta_i = sum_d dout[i][d] out[i][d] and dS = P (dout V^T - Delta),
+ *   dq = scale dS K,   dk = scale dS^T Q,   dv = P^T dout,
+ * summed over the query heads of each kv head for dk and dv.  Visibility,
+ * positions and tile skipping are those of the forward.
+ *
+ * Layouts as in ps_prefill_attn trainer mode: q, out, dout, dq
+ * [B][T][n_q_heads][head_dim]; k, v, dk, dv [B][T][n_kv_heads][head_dim];
+ * lse [B][T][n_q_heads] natural log, as written by the forward of the same
+ * q, k, v (P is rebuilt from it); delta [B][T][n_q_heads] fp32 is a
+ * caller-owned workspace the call overwrites.  Every pointer is device memory
+ * the caller owns; dq, dk and dv are overwritten (no accumulation into them).
+ * bf16 only, head_dim 128, GQA group 1, 2, 4 or 8.  Stream-ordered: Delta,
+ * then dq, then dk/dv, on the given stream.
+ *
+ * Errors: PS_ERR_INVALID (NULL pointer, batch < 1, seq_len < 0, start_pos < 0,
+ * prefix_len < 0, window < 1, n_q_heads not a multiple of n_kv_heads, scale
+ * <= 0 or not finite), PS_ERR_UNSUPPORTED (dtype other than bf16, head_dim
+ * other than 128, another GQA group, positions reaching 2^31), PS_ERR_HIP. */
+typedef struct {
+    int32_t batch;          /* B >= 1 */
+    int32_t seq_len;        /* T >= 0 (0: nothing to do) */
+    int32_t n_q_heads;
+    int32_t n_kv_heads;
+    int32_t head_dim;       /* 128 */
+    int32_t dtype;          /* PS_BF16 */
+    int64_t start_pos;      /* position of token 0, >= 0 */
+    int64_t prefix_len;     /* P >= 0 */
+    int64_t window;         /* W >= 1 */
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* out;        /* forward output */
+    const float* lse;       /* forward log-sum-exp */
+    const void* dout;       /* gradient of out */
+    void* dq;
+    void* dk;
+    void* dv;
+    float* delta;           /* workspace [B][T][n_q_heads] fp32 */
+    float scale;            /* the forward's multiplier of q.k, > 0 */
+} ps_prefill_bwd_args;
+
+int ps_prefill_attn_bwd(const ps_prefill_bwd_args* args, void* stream);
+
 /* Class of a (query tile, key tile) pair, query positions [i0, i1] and key
  * positions [j0, j1] (both non-empty, contiguous): 0 SKIP (no visible pair),
  * 1 FULL (every pair visible), 2 MASKED.  The same closed form the prefill

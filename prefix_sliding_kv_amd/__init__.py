@@ -55,6 +55,16 @@ class _PrefillArgs(ctypes.Structure):
                 ("scale", ctypes.c_float)]
 
 
+class _PrefillBwdArgs(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq_len", ctypes.c_int32), ("n_q_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("start_pos", ctypes.c_int64), ("prefix_len", ctypes.c_int64), ("window", ctypes.c_int64),
+                ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+                ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dout", ctypes.c_void_p),
+                ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+                ("delta", ctypes.c_void_p), ("scale", ctypes.c_float)]
+
+
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
 _SIGS = {
     "ps_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheDesc)]),
@@ -69,6 +79,7 @@ _SIGS = {
     "ps_decode_step": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _vp, _vp, _vp, _vp, _vp,
                                       ctypes.c_float, _vp]),
     "ps_prefill_attn": (ctypes.c_int, [ctypes.POINTER(_PrefillArgs), _vp]),
+    "ps_prefill_attn_bwd": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), _vp]),
     "ps_tile_class": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "ps_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ps_version": (ctypes.c_char_p, []),
@@ -190,6 +201,20 @@ def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: in
                      rows.data_ptr() if rows is not None else 0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                      out.data_ptr(), lse.data_ptr() if lse is not None else 0, scale)
     _check(lib.ps_prefill_attn(ctypes.byref(a), _stream(stream)), "ps_prefill_attn")
+
+
+def ps_prefill_attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, *, start_pos: int,
+                        prefix_len: int, window: int, scale: float, stream=None) -> None:
+    """Trainer-mode backward: q/out/dout/dq [B][T][Hq][d], k/v/dk/dv [B][T][Hkv][d]
+    bf16 CUDA tensors, lse/delta [B][T][Hq] float32 (lse from the forward,
+    delta a workspace)."""
+    B, T, hq, d = q.shape
+    hkv = k.shape[2]
+    dtype = PS_BF16 if q.dtype == torch.bfloat16 else PS_F32
+    a = _PrefillBwdArgs(B, T, hq, hkv, d, dtype, start_pos, prefix_len, window, q.data_ptr(),
+                        k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), scale)
+    _check(lib.ps_prefill_attn_bwd(ctypes.byref(a), _stream(stream)), "ps_prefill_attn_bwd")
 
 
 class Cache:

@@ -288,6 +288,59 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     return hip_status(ps::launch_prefill(dtype, d, group, p, (hipStream_t)stream));
 }
 
+int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) {
+    if (!a) return PS_ERR_INVALID;
+    if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1)
+        return PS_ERR_INVALID;
+    if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
+    const int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim;
+    if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
+    if (a->dtype != PS_BF16 || d != 128) return PS_ERR_UNSUPPORTED;
+    const int group = hq / hkv;
+    if (group != 1 && group != 2 && group != 4 && group != 8) return PS_ERR_UNSUPPORTED;
+    if (a->start_pos + (int64_t)a->seq_len >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
+    // byte offsets of rows inside one sequence (plus one 64-row sub-tile past
+    // its end) are 32-bit in the kernels
+    if (((int64_t)a->seq_len + 64) * hq * d * 2 >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
+    if (a->seq_len == 0) return PS_OK;
+    if (!a->q || !a->k || !a->v || !a->out || !a->lse || !a->dout || !a->dq || !a->dk || !a->dv || !a->delta)
+        return PS_ERR_INVALID;
+    ps::BwdParams p{};
+    const int64_t T = a->seq_len;
+    ps::KeyRun& r = p.f.runs[0];
+    r.k = a->k;
+    r.v = a->v;
+    r.seq_stride = T * hkv * d;
+    r.head_stride = d;
+    r.row_stride = (int64_t)hkv * d;
+    r.pos0 = a->start_pos;
+    r.n = T;
+    r.rows = nullptr;
+    p.f.n_runs = 1;
+    p.f.batch = a->batch;
+    p.f.seq_len = a->seq_len;
+    p.f.hq = hq;
+    p.f.hkv = hkv;
+    p.f.start_pos = a->start_pos;
+    p.f.P = a->prefix_len;
+    p.f.W = a->window;
+    p.f.q = a->q;
+    p.f.out = const_cast<void*>(a->out);
+    p.f.lse = nullptr;
+    p.f.scale_log2 = a->scale * kLog2e;
+    p.dout = a->dout;
+    p.lse = a->lse;
+    p.delta_out = a->delta;
+    p.delta = a->delta;
+    p.dq = a->dq;
+    p.dk = a->dk;
+    p.dv = a->dv;
+    p.k = a->k;
+    p.v = a->v;
+    p.scale = a->scale;
+    return hip_status(ps::launch_prefill_bwd(group, p, (hipStream_t)stream));
+}
+
 int ps_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P, int64_t W) {
     if (i1 < i0 || j1 < j0 || P < 0 || W < 1) return -1;
     return ps::tile_class(i0, i1, j0, j1, P, W);

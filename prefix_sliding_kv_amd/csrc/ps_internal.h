@@ -132,4 +132,20 @@ struct PrefillParams {
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p,
                           hipStream_t stream);
 
+// Trainer-side backward (bf16, head_dim 128): Delta, dQ, then dK/dV on one stream.
+struct BwdParams {
+    PrefillParams f;       // trainer-mode walk: one key run (the chunk); f.q = Q, f.out = forward O
+    const void* dout;      // [B][T][Hq][d]
+    const float* lse;      // [B][T][Hq] natural log, from the forward
+    float* delta_out;      // [B][T][Hq] fp32 workspace: rowsum(dO * O), written first
+    const float* delta;    // the same buffer, read by the dQ and dK/dV kernels
+    void* dq;              // [B][T][Hq][d]
+    void* dk;              // [B][T][Hkv][d]
+    void* dv;
+    const void* k;         // [B][T][Hkv][d]
+    const void* v;
+    float scale;
+};
+hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream);
+
 }  // namespace ps

@@ -32,6 +32,7 @@ namespace ps {
 namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2eF = 1.4426950408889634f;
 constexpr int kBN = 64;  // keys per tile of the fp32 debug kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -645,6 +646,488 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     if (p.lse) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run + log2f(l_run)) * kLn2;
 }
 
+// ================================================================ backward
+// Trainer-side backward of the masked attention (the gradient of the forward
+// above; the agihunt.info summary, paragraph on RL, and the njhaofan.com
+// article, passage on truncated backpropagation, describe the trainer that
+// backpropagates through it).  With P = softmax over the visible keys,
+// Delta_i = rowsum(dO_i * O_i) and dS = P * (dP - Delta), dP = dO V^T:
+//   dQ = scale * dS K,   dK = scale * dS^T Q,   dV = P^T dO.
+// Three kernels: Delta (a row reduction), dQ (per query tile over its key
+// tiles, the forward's walk and staging) and dK/dV (per key block over the
+// query tiles that see it).  P is rebuilt from the forward's log-sum-exp, so
+// no running maximum is needed.  Tile classification is the forward's: SKIP
+// pairs cost nothing, FULL pairs run unmasked, MASKED pairs mask per element.
+
+// Delta[row] = sum_d dO[row][d] * O[row][d] over rows of 128 bf16; 16 lanes
+// per row, 8 elements per lane.
+__global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* out, const uint16_t* dout, float* delta,
+                                                        int64_t rows) {
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t row = gid >> 4;
+    const int part = (int)(gid & 15);
+    float acc = 0.f;
+    if (row < rows) {
+        const Vec16 a = *reinterpret_cast<const Vec16*>(out + row * 128 + part * 8);
+        const Vec16 b = *reinterpret_cast<const Vec16*>(dout + row * 128 + part * 8);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            acc = fmaf(__uint_as_float(a.w[w] << 16), __uint_as_float(b.w[w] << 16), acc);
+            acc = fmaf(__uint_as_float(a.w[w] & 0xFFFF0000u), __uint_as_float(b.w[w] & 0xFFFF0000u), acc);
+        }
+    }
+#pragma unroll
+    for (int o = 8; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 16);
+    if (row < rows && part == 0) delta[row] = acc;
+}
+
+// Per-lane byte offsets of the transposing operand reads from a row-major
+// tile whose 16-byte chunks are swizzled with k_chunk_swz (row & 15): the
+// same lane pattern as read_vt (row 4h + k/4 of the 16-lane group, dims
+// 32m + 16(q%2) + 4(k%4)), for the two 8-row halves of a 16-row step; the
+// step itself adds 16 rows, which keeps row & 15.
+__device__ inline void kswz_tr_offsets(int lane, uint32_t (&off)[2][4]) {
+    const int h = lane >> 5, q = lane >> 4, gp = lane & 15;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        const int row = 8 * half + 4 * h + (gp >> 2);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int dim = 32 * m + 16 * (q & 1) + 4 * (gp & 3);
+            off[half][m] = row * kRowBytes + ((((dim >> 3) ^ k_chunk_swz(row)) << 4) | ((dim & 7) << 1));
+        }
+    }
+}
+// Transposed operands of 16-row step ST (rows 16 ST .. 16 ST + 15) for the
+// four dim blocks, from a tile at LDS address base with the K swizzle.
+__device__ inline void read_t_kswz(int st, uint32_t base, const uint32_t (&off)[2][4], Vec16 (&va)[4]) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(uintptr_t)(base + off[0][m] + st * 16 * kRowBytes));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(uintptr_t)(base + off[1][m] + st * 16 * kRowBytes));
+        __builtin_memcpy(&va[m].w[0], &lo, 8);
+        __builtin_memcpy(&va[m].w[2], &hi, 8);
+    }
+}
+
+
+// Stage the cursor's tile for the dQ kernel: K and V rows both with the K
+// swizzle (K is read as rows for S^T and transposed for dQ; V as rows for dP^T).
+__device__ inline void load_tile_bwd(const Cursor& c, const LaneOffsets& lo, int wave, char* stage) {
+    const int row0 = c.t * kBNB;
+    const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
+    const int64_t off = (int64_t)row0 * c.rs;
+    const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
+    const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
+    if (wave >= kLoadWaves) return;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int r4 = (kBNB / kLoadWaves) * wave + 4 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            kr, (__attribute__((address_space(3))) void*)(stage + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            vr, (__attribute__((address_space(3))) void*)(stage + kTileBytes + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
+    }
+}
+
+// dQ: the forward's workgroup layout (8 waves, 256 stacked query rows, 128-key
+// tiles in a 2-stage ring).  Per tile and 64-key half: S^T = K Q^T and
+// dP^T = V dO^T (both with the key rows as the A operand), dS^T in registers,
+// then dQ^T += K^T dS^T with K^T from transposing reads.
+template <int G>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
+    constexpr int D = 128;
+    constexpr int QP = 32 * kWaves / G;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const PrefillParams& p = bp.f;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    const int n_qt = (p.seq_len + QP - 1) / QP;
+    const int work = xcd_remap((int)blockIdx.x, n_qt * p.hkv * p.batch);
+    const int qt = work % n_qt, g = (work / n_qt) % p.hkv, b = work / (n_qt * p.hkv);
+
+    const int t0 = qt * QP;
+    const int t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
+    const int i0 = (int)p.start_pos + t0;
+    const int i1 = (int)p.start_pos + t_last;
+    const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
+    const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
+    const float c = p.scale_log2;
+
+    const int qrow = 32 * wave + col;
+    const int head = g * G + qrow / QP;
+    const int my_t = t0 + qrow % QP;
+    const bool q_ok = my_t < p.seq_len;
+    const int my_i = (int)p.start_pos + my_t;
+    const int64_t row_el = ((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head;
+    Vec16 qreg[8], dreg[8];
+    {
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) + row_el * D;
+        const uint16_t* dp = reinterpret_cast<const uint16_t*>(bp.dout) + row_el * D;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            qreg[ks] = q_ok ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
+            dreg[ks] = q_ok ? *reinterpret_cast<const Vec16*>(dp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
+        }
+    }
+    // P = exp2(s c - lse log2 e); rows past the chunk get P = 0
+    const float lse2 = q_ok ? bp.lse[row_el] * kLog2eF : INFINITY;
+    const float dlt = q_ok ? bp.delta[row_el] : 0.f;
+
+    __shared__ TileWalk walk;
+    __shared__ RunView views[kMaxRuns];
+    if (tid == 0) {
+        plan_walk<kBNB>(p, (int64_t)i0, (int64_t)i1, walk);
+        for (int r = 0; r < p.n_runs; ++r) {
+            const KeyRun& run = p.runs[r];
+            const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
+            const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride;
+            views[r].k = static_cast<const char*>(run.k) + base_el * 2;
+            views[r].v = static_cast<const char*>(run.v) + base_el * 2;
+            views[r].pos0 = run.pos0;
+            views[r].n = (int)run.n;
+            views[r].row_bytes = (int)(run.row_stride * 2);
+        }
+    }
+    __syncthreads();
+    int total = 0;
+    for (int r = 0; r < walk.n_ranges; ++r) total += walk.end[r] - walk.begin[r];
+
+    uint32_t kt_off[2][4];
+    kswz_tr_offsets(lane, kt_off);
+
+    f32x16 dq[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[m][r] = 0.f;
+
+    Cursor cc, pc;
+    LaneOffsets lo;
+    if (total > 0) {
+        cursor_enter(cc, 0, walk, views);
+        cursor_enter(pc, 0, walk, views);
+        lane_offsets(lo, pc.rs, lane, wave);
+    }
+    auto stage_next = [&](char* stage) {
+        load_tile_bwd(pc, lo, wave, stage);
+        if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets(lo, pc.rs, lane, wave);
+    };
+    if (total > 0) stage_next(smem);
+    if (total > 1) {
+        stage_next(smem + kStageBytes);
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    tile_barrier();
+
+    for (int f = 0; f < total; ++f) {
+        const int row0 = cc.t * kBNB;
+        const int nrows = cc.n - row0 < kBNB ? cc.n - row0 : kBNB;
+        const int j0 = (int)cc.pos0 + row0;
+        const int j1 = j0 + nrows - 1;
+        const int cls = nrows < kBNB ? kMasked : tile_class32(i0, i1, j0, j1, P32, w32);
+        const char* ks_lds = smem + (f & 1) * kStageBytes;
+        const char* vs_lds = ks_lds + kTileBytes;
+        const uint32_t kb = lds_addr(ks_lds);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            f32x16 s[2], dp[2];
+            const f32x16 zero = {};
+#pragma unroll
+            for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int krow = 32 * (2 * half + mm) + col;
+                    const int off = krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4);
+                    const Vec16 ka = *reinterpret_cast<const Vec16*>(ks_lds + off);
+                    const Vec16 va = *reinterpret_cast<const Vec16*>(vs_lds + off);
+                    s[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qreg[kk]),
+                                                                     kk == 0 ? zero : s[mm], 0, 0, 0);
+                    dp[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va), as_bf16x8(dreg[kk]),
+                                                                      kk == 0 ? zero : dp[mm], 0, 0, 0);
+                }
+            if (cls == kMasked) {
+                const int pj = P32 - j0;
+                const int rel = my_i - j0;
+                const int hic = rel < nrows - 1 ? rel : nrows - 1;
+                const int a_hi = pj < hic + 1 ? pj : hic + 1;
+                const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
+#pragma unroll
+                for (int mm = 0; mm < 2; ++mm) {
+                    const int mb = 2 * half + mm;
+                    const uint32_t bits = range_bits(0, a_hi - 32 * mb) | range_bits(b_lo - 32 * mb, hic + 1 - 32 * mb);
+                    const uint32_t bits_h = bits >> (4 * h);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const uint32_t km = (uint32_t)__builtin_amdgcn_sbfe((int)bits_h, 8 * (r >> 2) + (r & 3), 1);
+                        s[mm][r] = __uint_as_float((km & __float_as_uint(s[mm][r])) | (~km & 0xFF800000u));
+                    }
+                }
+            }
+            // dS^T = P^T (dP^T - Delta), packed to bf16 per 16-key step, and
+            // dQ^T += K^T dS^T
+#pragma unroll
+            for (int sl = 0; sl < 4; ++sl) {
+                const int mm = sl >> 1, base = 8 * (sl & 1);
+                Vec16 ds;
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int r0 = base + 2 * w;
+                    const float p0 = fast_exp2(fmaf(s[mm][r0], c, -lse2));
+                    const float p1 = fast_exp2(fmaf(s[mm][r0 + 1], c, -lse2));
+                    ds.w[w] = pack_bf16x2(p0 * (dp[mm][r0] - dlt), p1 * (dp[mm][r0 + 1] - dlt));
+                }
+                Vec16 ka[4];
+                read_t_kswz(4 * half + sl, kb, kt_off, ka);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    dq[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[m]), as_bf16x8(ds), dq[m], 0, 0, 0);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        tile_barrier();
+        if (f + kStages < total) stage_next(smem + (f & 1) * kStageBytes);
+        cursor_next(cc, walk.n_ranges, walk, views);
+    }
+
+    if (!q_ok) return;
+    uint16_t* op = reinterpret_cast<uint16_t*>(bp.dq) + row_el * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int cc4 = 0; cc4 < 4; ++cc4) {
+            Vec8 w;
+            w.w[0] = pack_bf16x2(dq[m][4 * cc4] * bp.scale, dq[m][4 * cc4 + 1] * bp.scale);
+            w.w[1] = pack_bf16x2(dq[m][4 * cc4 + 2] * bp.scale, dq[m][4 * cc4 + 3] * bp.scale);
+            *reinterpret_cast<Vec8*>(op + 32 * m + 8 * cc4 + 4 * h) = w;
+        }
+}
+
+// dK / dV: one workgroup of 8 waves per (sequence, kv head, block of 256
+// keys).  Wave w owns keys 32w .. 32w + 31 of the block: their K rows stay in
+// registers (B operand of S = Q K^T), their dK^T and dV^T accumulate in
+// registers; the block's V rows sit in LDS (B operand of dP = dO V^T).  The
+// query positions that can see the block are walked in sub-tiles of 64
+// stacked rows (the G heads of the group over 64/G positions); Q, dO, lse and
+// Delta of a sub-tile are staged into one of two LDS buffers while the other
+// is computed.  Per sub-tile each wave runs its two 32-row halves: S, P, dP,
+// dS with the key on the lane and the query on the register, then
+// dV^T += dO^T P and dK^T += Q^T dS with dO^T, Q^T from transposing reads.
+constexpr int kKB = 256;                                  // keys per block
+constexpr int kSubRows = 64;                              // stacked query rows per sub-tile
+constexpr int kSubRowBytes = kSubRows * kRowBytes;        // 16 KB of Q (or dO) rows
+constexpr int kSubStage = 2 * kSubRowBytes + 2 * kSubRows * 4;  // Q, dO, lse, Delta
+constexpr int kVBlock = kKB * kRowBytes;                  // 64 KB
+constexpr size_t kDkdvLds = (size_t)kVBlock + 2 * kSubStage;
+
+__device__ inline void dma_row16(const __amdgpu_buffer_rsrc_t& r, int voff, char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+__device__ inline void dma_row4(const __amdgpu_buffer_rsrc_t& r, int voff, char* lds) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
+template <int G>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
+    constexpr int D = 128;
+    constexpr int QS = kSubRows / G;  // positions per sub-tile
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const PrefillParams& p = bp.f;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    const int T = p.seq_len, hq = p.hq, hkv = p.hkv;
+    const int n_kb = (T + kKB - 1) / kKB;
+    const int work = xcd_remap((int)blockIdx.x, n_kb * hkv * p.batch);
+    const int kb = work % n_kb, g = (work / n_kb) % hkv, b = work / (n_kb * hkv);
+    const int S0 = (int)p.start_pos;
+    const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
+    const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
+    const float c = p.scale_log2;
+
+    const int kt0 = kb * kKB;                          // first key (chunk row) of the block
+    const int nk = T - kt0 < kKB ? T - kt0 : kKB;
+    const int wk0 = kt0 + 32 * wave;                   // this wave's first key
+    const int wk_n = T - wk0 < 32 ? (T - wk0 > 0 ? T - wk0 : 0) : 32;
+    const int jw0 = S0 + wk0, jw1 = jw0 + wk_n - 1;
+
+    // K rows of this wave's keys (lane: key col, dims 16 kk + 8h .. + 7)
+    Vec16 kreg[8];
+    {
+        const bool ok = col < wk_n;
+        const uint16_t* kp = reinterpret_cast<const uint16_t*>(bp.k) +
+                             (((int64_t)b * T + (ok ? wk0 + col : 0)) * hkv + g) * D;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+            kreg[kk] = ok ? *reinterpret_cast<const Vec16*>(kp + 8 * h + 16 * kk) : Vec16{{0, 0, 0, 0}};
+    }
+
+    char* vblk = smem;
+    char* stage0 = smem + kVBlock;
+    // V rows of the block into LDS (K swizzle); rows past the chunk read as zero
+    {
+        const int rs = hkv * D * 2;
+        const __amdgpu_buffer_rsrc_t vr = make_rsrc(
+            static_cast<const char*>(bp.v) + (((int64_t)b * T + kt0) * hkv + g) * D * 2, nk * rs);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 32 * wave + 4 * i + (lane >> 4);
+            dma_row16(vr, row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4), vblk + (32 * wave + 4 * i) * kRowBytes);
+        }
+    }
+
+    // query positions (chunk-relative) that can see a key of the block
+    const int t_lo = kt0;
+    const int64_t t_hi_w = (int64_t)kt0 + nk - 1 + w32 - 1;  // last query of the block's window
+    const int t_hi = (S0 + kt0 < P32 || t_hi_w >= T - 1) ? T - 1 : (int)t_hi_w;
+    const int s_first = t_lo / QS, s_last = t_hi / QS;
+    const int n_sub = s_last - s_first + 1;
+
+    // staging of sub-tile n: stacked row r = head offset r / QS, position
+    // t = (s_first + n) QS + r % QS; wave w stages rows 8w .. 8w + 7 of Q and
+    // dO; waves 0 and 1 stage the 64 lse and Delta values
+    const int64_t qseq = (int64_t)b * T * hq;  // row index of (b, t = 0, head 0)
+    const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const char*>(p.q) + qseq * D * 2, T * hq * D * 2);
+    const __amdgpu_buffer_rsrc_t dr = make_rsrc(static_cast<const char*>(bp.dout) + qseq * D * 2, T * hq * D * 2);
+    const __amdgpu_buffer_rsrc_t lr = make_rsrc(bp.lse + qseq, T * hq * 4);
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(bp.delta + qseq, T * hq * 4);
+    auto stage_sub = [&](int n, char* st) {
+        const int ts = (s_first + n) * QS;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int row = 8 * wave + 4 * i + (lane >> 4);
+            const int t = ts + row % QS, head = g * G + row / QS;
+            const int off = (t * hq + head) * D * 2 + (((lane & 15) ^ k_chunk_swz(row)) << 4);
+            dma_row16(qr, off, st + (8 * wave + 4 * i) * kRowBytes);
+            dma_row16(dr, off, st + kSubRowBytes + (8 * wave + 4 * i) * kRowBytes);
+        }
+        if (wave < 2) {
+            const int t = ts + lane % QS, head = g * G + lane / QS;
+            dma_row4(wave == 0 ? lr : xr, (t * hq + head) * 4, st + 2 * kSubRowBytes + wave * kSubRows * 4);
+        }
+    };
+    if (n_sub > 0) stage_sub(0, stage0);
+    if (n_sub > 1) {
+        stage_sub(1, stage0 + kSubStage);
+        if (wave < 2) asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) asm volatile("" ::"v"(kreg[kk].w[0]));
+    tile_barrier();
+
+    uint32_t tr_off[2][4];
+    kswz_tr_offsets(lane, tr_off);
+    f32x16 dkacc[4], dvacc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkacc[m][r] = dvacc[m][r] = 0.f;
+
+    for (int n = 0; n < n_sub; ++n) {
+        const char* st = stage0 + (n & 1) * kSubStage;
+        const char* qs = st;
+        const char* ds_ = st + kSubRowBytes;
+        const float* lse_s = reinterpret_cast<const float*>(st + 2 * kSubRowBytes);
+        const float* dlt_s = lse_s + kSubRows;
+        const int ts = (s_first + n) * QS;
+        if (wk_n > 0) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                // positions of this half's 32 stacked rows
+                const int iw0 = S0 + ts + (G == 1 ? 32 * half : 0);
+                const int iw1 = iw0 + (QS < 32 ? QS : 32) - 1;
+                const int cls = tile_class32(iw0, iw1, jw0, jw1, P32, w32);
+                if (cls == kSkip) continue;
+                f32x16 s = {}, dp = {};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const int qrow = 32 * half + col;
+                    const int off = qrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(qrow)) << 4);
+                    const Vec16 qa = *reinterpret_cast<const Vec16*>(qs + off);
+                    const Vec16 da = *reinterpret_cast<const Vec16*>(ds_ + off);
+                    const int vrow = 32 * wave + col;
+                    const Vec16 vb = *reinterpret_cast<const Vec16*>(
+                        vblk + vrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(vrow)) << 4));
+                    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kreg[kk]), s, 0, 0, 0);
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), as_bf16x8(vb), dp, 0, 0, 0);
+                }
+                // register r holds query row 8(r/4) + 4h + r%4 of the half, key col
+                const int my_j = jw0 + col;
+                Vec16 pb[2], sb[2];
+#pragma unroll
+                for (int st2 = 0; st2 < 2; ++st2) {
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        float pv[2], dv2[2];
+#pragma unroll
+                        for (int e = 0; e < 2; ++e) {
+                            const int r = 8 * st2 + 2 * w + e;
+                            const int qr_ = 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
+                            float sv = s[r];
+                            if (cls == kMasked) {
+                                const int i = S0 + ts + qr_ % QS;
+                                const bool vis = my_j <= i && (my_j < P32 || my_j > i - w32) && col < wk_n;
+                                sv = vis ? sv : -INFINITY;
+                            }
+                            const float pr = fast_exp2(fmaf(sv, c, -lse_s[qr_] * kLog2eF));
+                            pv[e] = pr;
+                            dv2[e] = pr * (dp[r] - dlt_s[qr_]);
+                        }
+                        pb[st2].w[w] = pack_bf16x2(pv[0], pv[1]);
+                        sb[st2].w[w] = pack_bf16x2(dv2[0], dv2[1]);
+                    }
+                }
+                const uint32_t qb_ = lds_addr(qs) + 32 * half * kRowBytes;
+                const uint32_t db_ = lds_addr(ds_) + 32 * half * kRowBytes;
+#pragma unroll
+                for (int st2 = 0; st2 < 2; ++st2) {
+                    Vec16 ta[4];
+                    read_t_kswz(st2, db_, tr_off, ta);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        dvacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ta[m]), as_bf16x8(pb[st2]), dvacc[m], 0, 0, 0);
+                    read_t_kswz(st2, qb_, tr_off, ta);
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        dkacc[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ta[m]), as_bf16x8(sb[st2]), dkacc[m], 0, 0, 0);
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        tile_barrier();
+        if (n + 2 < n_sub) stage_sub(n + 2, stage0 + (n & 1) * kSubStage);
+    }
+
+    if (col >= wk_n) return;
+    const int64_t kel = (((int64_t)b * T + wk0 + col) * hkv + g) * D;
+    uint16_t* dkp = reinterpret_cast<uint16_t*>(bp.dk) + kel;
+    uint16_t* dvp = reinterpret_cast<uint16_t*>(bp.dv) + kel;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int cc4 = 0; cc4 < 4; ++cc4) {
+            Vec8 wk, wv;
+            wk.w[0] = pack_bf16x2(dkacc[m][4 * cc4] * bp.scale, dkacc[m][4 * cc4 + 1] * bp.scale);
+            wk.w[1] = pack_bf16x2(dkacc[m][4 * cc4 + 2] * bp.scale, dkacc[m][4 * cc4 + 3] * bp.scale);
+            wv.w[0] = pack_bf16x2(dvacc[m][4 * cc4], dvacc[m][4 * cc4 + 1]);
+            wv.w[1] = pack_bf16x2(dvacc[m][4 * cc4 + 2], dvacc[m][4 * cc4 + 3]);
+            *reinterpret_cast<Vec8*>(dkp + 32 * m + 8 * cc4 + 4 * h) = wk;
+            *reinterpret_cast<Vec8*>(dvp + 32 * m + 8 * cc4 + 4 * h) = wv;
+        }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p, hipStream_t stream) {
@@ -685,6 +1168,46 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
         hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, stream, p);
     else
         return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream) {
+    const int64_t rows = (int64_t)p.f.batch * p.f.seq_len * p.f.hq;
+    if (rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(p.f.out), static_cast<const uint16_t*>(p.dout), p.delta_out, rows);
+    const int qp = 32 * kWaves / group;
+    const dim3 grid_q((unsigned)(((p.f.seq_len + qp - 1) / qp) * p.f.hkv * p.f.batch));
+    const dim3 grid_k((unsigned)(((p.f.seq_len + kKB - 1) / kKB) * p.f.hkv * p.f.batch));
+    const size_t lds_q = (size_t)kStages * kStageBytes;
+    static bool lds_set[8] = {false, false, false, false, false, false, false, false};
+    const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+    const void* fq = nullptr;
+    const void* fk = nullptr;
+    switch (group) {
+        case 1: fq = (const void*)bwd_dq_kernel<1>; fk = (const void*)bwd_dkdv_kernel<1>; break;
+        case 2: fq = (const void*)bwd_dq_kernel<2>; fk = (const void*)bwd_dkdv_kernel<2>; break;
+        case 4: fq = (const void*)bwd_dq_kernel<4>; fk = (const void*)bwd_dkdv_kernel<4>; break;
+        case 8: fq = (const void*)bwd_dq_kernel<8>; fk = (const void*)bwd_dkdv_kernel<8>; break;
+        default: return hipErrorInvalidValue;
+    }
+    if (!lds_set[gi]) {
+        hipError_t e = hipFuncSetAttribute(fq, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_q);
+        if (e != hipSuccess) return e;
+        e = hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkdvLds);
+        if (e != hipSuccess) return e;
+        lds_set[gi] = true;
+    }
+    switch (group) {
+        case 1: hipLaunchKernelGGL(bwd_dq_kernel<1>, grid_q, dim3(kThreads), lds_q, stream, p);
+                hipLaunchKernelGGL(bwd_dkdv_kernel<1>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
+        case 2: hipLaunchKernelGGL(bwd_dq_kernel<2>, grid_q, dim3(kThreads), lds_q, stream, p);
+                hipLaunchKernelGGL(bwd_dkdv_kernel<2>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
+        case 4: hipLaunchKernelGGL(bwd_dq_kernel<4>, grid_q, dim3(kThreads), lds_q, stream, p);
+                hipLaunchKernelGGL(bwd_dkdv_kernel<4>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
+        case 8: hipLaunchKernelGGL(bwd_dq_kernel<8>, grid_q, dim3(kThreads), lds_q, stream, p);
+                hipLaunchKernelGGL(bwd_dkdv_kernel<8>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
+    }
     return hipGetLastError();
 }
 

@@ -133,3 +133,32 @@ def test_prefill_validation():
     assert call(scale=0.0) == ps.PS_ERR_INVALID
     assert call(scale=-0.1) == ps.PS_ERR_INVALID
     assert call(start_pos=2**31 - 2, seq_len=4) == ps.PS_ERR_UNSUPPORTED  # positions are 32-bit in the kernel
+
+
+def _bwd_args(**kw):
+    a = dict(batch=1, seq_len=16, n_q_heads=4, n_kv_heads=2, head_dim=128, dtype=ps.PS_BF16, start_pos=0,
+             prefix_len=4, window=8, q=1, k=1, v=1, out=1, lse=1, dout=1, dq=1, dk=1, dv=1, delta=1,
+             scale=0.1)
+    a.update(kw)
+    return ps._PrefillBwdArgs(**a)
+
+
+def test_prefill_bwd_rejects_bad_arguments_before_any_launch():
+    call = lambda **kw: ps.lib.ps_prefill_attn_bwd(ctypes.byref(_bwd_args(**kw)), None)
+    assert ps.lib.ps_prefill_attn_bwd(None, None) == ps.PS_ERR_INVALID
+    assert call(batch=0) == ps.PS_ERR_INVALID
+    assert call(seq_len=-1) == ps.PS_ERR_INVALID
+    assert call(window=0) == ps.PS_ERR_INVALID
+    assert call(prefix_len=-1) == ps.PS_ERR_INVALID
+    assert call(start_pos=-1) == ps.PS_ERR_INVALID
+    assert call(n_q_heads=3) == ps.PS_ERR_INVALID
+    assert call(scale=0.0) == ps.PS_ERR_INVALID
+    assert call(scale=float("nan")) == ps.PS_ERR_INVALID
+    assert call(dtype=ps.PS_F32) == ps.PS_ERR_UNSUPPORTED
+    assert call(head_dim=64) == ps.PS_ERR_UNSUPPORTED
+    assert call(n_q_heads=6, n_kv_heads=2) == ps.PS_ERR_UNSUPPORTED
+    assert call(start_pos=(1 << 31) - 8) == ps.PS_ERR_UNSUPPORTED
+    assert call(dv=0) == ps.PS_ERR_INVALID
+    assert call(delta=0) == ps.PS_ERR_INVALID
+    # nothing to do: no pointer is touched
+    assert call(seq_len=0, q=0, k=0, v=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0, delta=0) == ps.PS_OK

@@ -1,0 +1,81 @@
+"""GPU parity of the trainer-side backward (dq, dk, dv of the masked
+attention, bf16 MFMA path) against the CPU oracle's float64 gradient.
+
+The backward takes the forward's output and log-sum-exp from the GPU forward
+of the same inputs and an upstream gradient dout drawn from the seeded
+generator.  Tolerance: the bf16 operands of the four products (P, dS, and the
+bf16 inputs and outputs) carry a relative rounding of 2^-9, so every gradient
+is compared element by element with max-abs error <= 2e-2 * max(1, max|ref|)
+of its tensor, and its Frobenius error must stay below 1e-2 * max(1, |ref|).  A
+dropped or leaked key, a wrong head or a missing scale moves some element by
+far more than that (the "peaky" cases spread scores over tens of units)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_harness import DT_BF16, as_f32, dev_to_f32, gen, note, to_dev
+
+pytestmark = pytest.mark.gpu
+ps = pytest.importorskip("prefix_sliding_kv_amd")
+
+
+def bwd_inputs(seed, B, start, T, hq, hkv, d, scale):
+    pos = np.arange(start, start + T)
+    q = np.stack([gen(seed, synth.Q, 0, b, pos, hq, d, 1e4, DT_BF16, scale) for b in range(B)])
+    k = np.stack([gen(seed, synth.K, 0, b, pos, hkv, d, 1e4, DT_BF16, scale) for b in range(B)])
+    v = np.stack([gen(seed, synth.V, 0, b, pos, hkv, d, 0.0, DT_BF16) for b in range(B)])
+    do = np.stack([gen(seed + 1, synth.V, 1, b, pos, hq, d, 0.0, DT_BF16) for b in range(B)])
+    return pos, q, k, v, do
+
+
+def run_bwd(q, k, v, do, P, W, start):
+    B, T, hq, d = q.shape
+    hkv = k.shape[2]
+    sc = 1.0 / math.sqrt(d)
+    qd, kd, vd, dod = to_dev(q), to_dev(k), to_dev(v), to_dev(do)
+    out = torch.empty_like(qd)
+    lse = torch.empty(B, T, hq, device="cuda")
+    ps.ps_prefill_attn(qd, kd, vd, out, start_pos=start, prefix_len=P, window=W, scale=sc, lse=lse)
+    dq, dk, dv = torch.empty_like(qd), torch.empty_like(kd), torch.empty_like(vd)
+    delta = torch.empty(B, T, hq, device="cuda")
+    ps.ps_prefill_attn_bwd(qd, kd, vd, out, lse, dod, dq, dk, dv, delta, start_pos=start, prefix_len=P,
+                           window=W, scale=sc)
+    torch.cuda.synchronize()
+    return dev_to_f32(dq), dev_to_f32(dk), dev_to_f32(dv), dev_to_f32(delta), dev_to_f32(out)
+
+
+def check(name, got, ref):
+    mx = max(1.0, float(np.max(np.abs(ref))))
+    err = float(np.max(np.abs(got - ref)))
+    fro = float(np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1.0))
+    assert err <= 2e-2 * mx and fro <= 1e-2, (name, err, mx, fro)
+
+
+@pytest.mark.parametrize("hq,hkv,B,T,P,W,start,scale", [
+    (4, 2, 2, 300, 20, 70, 0, 1.0),      # several tiles and a ragged tail, G=2
+    (4, 2, 1, 333, 17, 100, 0, 3.0),     # peaky: mask errors show
+    (2, 2, 1, 260, 0, 33, 0, 3.0),       # G=1, vanilla sliding window
+    (8, 2, 1, 200, 5, 64, 0, 3.0),       # G=4
+    (16, 2, 1, 150, 9, 40, 0, 3.0),      # G=8
+    (2, 1, 1, 190, 3, 1, 0, 3.0),        # W=1: prefix + self
+    (2, 1, 1, 300, 400, 8, 0, 1.0),      # P > T: plain causal
+    (4, 2, 1, 290, 30, 50, 1000, 3.0),   # chunk not starting at 0
+    (2, 1, 1, 1, 0, 5, 0, 1.0),          # single token
+])
+def test_trainer_backward_small(hq, hkv, B, T, P, W, start, scale):
+    note(f"backward hq={hq} hkv={hkv} B={B} T={T} P={P} W={W} start={start} s={scale}")
+    d = 128
+    pos, q, k, v, do = bwd_inputs(21, B, start, T, hq, hkv, d, scale)
+    dq, dk, dv, delta, out = run_bwd(q, k, v, do, P, W, start)
+    for b in range(B):
+        rq, rk, rv = oracle.attention_bwd(as_f32(q[b]), pos, as_f32(k[b]), as_f32(v[b]), pos, as_f32(do[b]),
+                                          P, W, 1.0 / math.sqrt(d), threads=16)
+        check("dq", dq[b], rq)
+        check("dk", dk[b], rk)
+        check("dv", dv[b], rv)
+        # Delta is rowsum(dout * out) of the bf16 forward output
+        np.testing.assert_allclose(delta[b], np.sum(as_f32(do[b]) * out[b], axis=-1), rtol=0, atol=1e-3)
