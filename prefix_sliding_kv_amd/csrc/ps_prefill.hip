@@ -659,6 +659,29 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
 // no running maximum is needed.  Tile classification is the forward's: SKIP
 // pairs cost nothing, FULL pairs run unmasked, MASKED pairs mask per element.
 
+// Direct-to-LDS loads written as asm: 16 (or 4) bytes per lane from
+// rsrc + voff land at LDS address m0 + 16 (4) * lane.  The compiler does not
+// see them, so it does not make every later LDS read wait for them; the
+// kernels order them against the reads of their buffer themselves (vmcnt
+// before the barrier that hands the buffer over).  Compiler-visible global
+// loads issued before them are waited for explicitly before the loops.
+__device__ inline i32x4 rsrc_words(const void* base, int bytes) {
+    i32x4 r;
+    r[0] = (int)(uint32_t)(uintptr_t)base;
+    r[1] = (int)(((uintptr_t)base >> 32) & 0xFFFF);
+    r[2] = bytes;
+    r[3] = 0x00020000;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    return r;
+}
+__device__ inline void dma16_asm(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+__device__ inline void dma4_asm(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+
 // Delta[row] = sum_d dO[row][d] * O[row][d] over rows of 128 bf16; 16 lanes
 // per row, 8 elements per lane.
 __global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* out, const uint16_t* dout, float* delta,
@@ -719,16 +742,15 @@ __device__ inline void load_tile_bwd(const Cursor& c, const LaneOffsets& lo, int
     const int row0 = c.t * kBNB;
     const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
     const int64_t off = (int64_t)row0 * c.rs;
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
     if (wave >= kLoadWaves) return;
+    const i32x4 kr = rsrc_words(c.k + off, nrows * c.rs);
+    const i32x4 vr = rsrc_words(c.v + off, nrows * c.rs);
+    const uint32_t sb = lds_addr(stage);
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
         const int r4 = (kBNB / kLoadWaves) * wave + 4 * i;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            kr, (__attribute__((address_space(3))) void*)(stage + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            vr, (__attribute__((address_space(3))) void*)(stage + kTileBytes + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
+        dma16_asm(kr, lo.k[i], sb + r4 * kRowBytes);
+        dma16_asm(vr, lo.k[i], sb + kTileBytes + r4 * kRowBytes);
     }
 }
 
@@ -777,6 +799,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
     // P = exp2(s c - lse log2 e); rows past the chunk get P = 0
     const float lse2 = q_ok ? bp.lse[row_el] * kLog2eF : INFINITY;
     const float dlt = q_ok ? bp.delta[row_el] : 0.f;
+    // the compiler cannot see the asm tile loads: make these loads complete
+    // here rather than at their first use inside the tile loop
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks].w[0]), "v"(dreg[ks].w[0]));
+    asm volatile("" ::"v"(lse2), "v"(dlt));
 
     __shared__ TileWalk walk;
     __shared__ RunView views[kMaxRuns];
@@ -927,13 +954,6 @@ constexpr int kSubStage = 2 * kSubRowBytes + 2 * kSubRows * 4;  // Q, dO, lse, D
 constexpr int kVBlock = kKB * kRowBytes;                  // 64 KB
 constexpr size_t kDkdvLds = (size_t)kVBlock + 2 * kSubStage;
 
-__device__ inline void dma_row16(const __amdgpu_buffer_rsrc_t& r, int voff, char* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
-}
-__device__ inline void dma_row4(const __amdgpu_buffer_rsrc_t& r, int voff, char* lds) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
-}
-
 template <int G>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
     constexpr int D = 128;
@@ -975,12 +995,13 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
     // V rows of the block into LDS (K swizzle); rows past the chunk read as zero
     {
         const int rs = hkv * D * 2;
-        const __amdgpu_buffer_rsrc_t vr = make_rsrc(
-            static_cast<const char*>(bp.v) + (((int64_t)b * T + kt0) * hkv + g) * D * 2, nk * rs);
+        const i32x4 vr = rsrc_words(static_cast<const char*>(bp.v) + (((int64_t)b * T + kt0) * hkv + g) * D * 2,
+                                    nk * rs);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 32 * wave + 4 * i + (lane >> 4);
-            dma_row16(vr, row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4), vblk + (32 * wave + 4 * i) * kRowBytes);
+            dma16_asm(vr, row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4),
+                      lds_addr(vblk) + (32 * wave + 4 * i) * kRowBytes);
         }
     }
 
@@ -995,23 +1016,23 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
     // t = (s_first + n) QS + r % QS; wave w stages rows 8w .. 8w + 7 of Q and
     // dO; waves 0 and 1 stage the 64 lse and Delta values
     const int64_t qseq = (int64_t)b * T * hq;  // row index of (b, t = 0, head 0)
-    const __amdgpu_buffer_rsrc_t qr = make_rsrc(static_cast<const char*>(p.q) + qseq * D * 2, T * hq * D * 2);
-    const __amdgpu_buffer_rsrc_t dr = make_rsrc(static_cast<const char*>(bp.dout) + qseq * D * 2, T * hq * D * 2);
-    const __amdgpu_buffer_rsrc_t lr = make_rsrc(bp.lse + qseq, T * hq * 4);
-    const __amdgpu_buffer_rsrc_t xr = make_rsrc(bp.delta + qseq, T * hq * 4);
+    const i32x4 qr = rsrc_words(static_cast<const char*>(p.q) + qseq * D * 2, T * hq * D * 2);
+    const i32x4 dr = rsrc_words(static_cast<const char*>(bp.dout) + qseq * D * 2, T * hq * D * 2);
+    const i32x4 xr = rsrc_words(wave == 0 ? (const void*)(bp.lse + qseq) : (const void*)(bp.delta + qseq), T * hq * 4);
     auto stage_sub = [&](int n, char* st) {
         const int ts = (s_first + n) * QS;
+        const uint32_t sb = lds_addr(st);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int row = 8 * wave + 4 * i + (lane >> 4);
             const int t = ts + row % QS, head = g * G + row / QS;
             const int off = (t * hq + head) * D * 2 + (((lane & 15) ^ k_chunk_swz(row)) << 4);
-            dma_row16(qr, off, st + (8 * wave + 4 * i) * kRowBytes);
-            dma_row16(dr, off, st + kSubRowBytes + (8 * wave + 4 * i) * kRowBytes);
+            dma16_asm(qr, off, sb + (8 * wave + 4 * i) * kRowBytes);
+            dma16_asm(dr, off, sb + kSubRowBytes + (8 * wave + 4 * i) * kRowBytes);
         }
         if (wave < 2) {
             const int t = ts + lane % QS, head = g * G + lane / QS;
-            dma_row4(wave == 0 ? lr : xr, (t * hq + head) * 4, st + 2 * kSubRowBytes + wave * kSubRows * 4);
+            dma4_asm(xr, (t * hq + head) * 4, sb + 2 * kSubRowBytes + wave * kSubRows * 4);
         }
     };
     if (n_sub > 0) stage_sub(0, stage0);
@@ -1049,45 +1070,59 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                 const int iw1 = iw0 + (QS < 32 ? QS : 32) - 1;
                 const int cls = tile_class32(iw0, iw1, jw0, jw1, P32, w32);
                 if (cls == kSkip) continue;
-                f32x16 s = {}, dp = {};
+                const int qrow = 32 * half + col;
+                const int vrow = 32 * wave + col;
+                // S = Q K^T; register r holds query row 8(r/4) + 4h + r%4 of the
+                // half, the lane's key col
+                f32x16 s = {};
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
-                    const int qrow = 32 * half + col;
-                    const int off = qrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(qrow)) << 4);
-                    const Vec16 qa = *reinterpret_cast<const Vec16*>(qs + off);
-                    const Vec16 da = *reinterpret_cast<const Vec16*>(ds_ + off);
-                    const int vrow = 32 * wave + col;
-                    const Vec16 vb = *reinterpret_cast<const Vec16*>(
-                        vblk + vrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(vrow)) << 4));
+                    const Vec16 qa = *reinterpret_cast<const Vec16*>(
+                        qs + qrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(qrow)) << 4));
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kreg[kk]), s, 0, 0, 0);
-                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), as_bf16x8(vb), dp, 0, 0, 0);
                 }
-                // register r holds query row 8(r/4) + 4h + r%4 of the half, key col
+                // P from the forward's log-sum-exp (fp32, kept for dS) and its bf16 operand
                 const int my_j = jw0 + col;
+                float pf[16];
                 Vec16 pb[2], sb[2];
 #pragma unroll
-                for (int st2 = 0; st2 < 2; ++st2) {
+                for (int r = 0; r < 16; ++r) {
+                    const int qr_ = 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
+                    float sv = s[r];
+                    if (cls == kMasked) {
+                        const int i = S0 + ts + qr_ % QS;
+                        const bool vis = my_j <= i && (my_j < P32 || my_j > i - w32) && col < wk_n;
+                        sv = vis ? sv : -INFINITY;
+                    }
+                    pf[r] = fast_exp2(fmaf(sv, c, -lse_s[qr_] * kLog2eF));
+                }
+#pragma unroll
+                for (int st2 = 0; st2 < 2; ++st2)
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) pb[st2].w[w] = pack_bf16x2(pf[8 * st2 + 2 * w], pf[8 * st2 + 2 * w + 1]);
+                // dP = dO V^T, then dS = P (dP - Delta)
+                f32x16 dp = {};
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) {
+                    const Vec16 da = *reinterpret_cast<const Vec16*>(
+                        ds_ + qrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(qrow)) << 4));
+                    const Vec16 vb = *reinterpret_cast<const Vec16*>(
+                        vblk + vrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(vrow)) << 4));
+                    dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), as_bf16x8(vb), dp, 0, 0, 0);
+                }
+#pragma unroll
+                for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
-                        float pv[2], dv2[2];
+                        float dv2[2];
 #pragma unroll
                         for (int e = 0; e < 2; ++e) {
                             const int r = 8 * st2 + 2 * w + e;
                             const int qr_ = 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
-                            float sv = s[r];
-                            if (cls == kMasked) {
-                                const int i = S0 + ts + qr_ % QS;
-                                const bool vis = my_j <= i && (my_j < P32 || my_j > i - w32) && col < wk_n;
-                                sv = vis ? sv : -INFINITY;
-                            }
-                            const float pr = fast_exp2(fmaf(sv, c, -lse_s[qr_] * kLog2eF));
-                            pv[e] = pr;
-                            dv2[e] = pr * (dp[r] - dlt_s[qr_]);
+                            dv2[e] = pf[r] * (dp[r] - dlt_s[qr_]);
                         }
-                        pb[st2].w[w] = pack_bf16x2(pv[0], pv[1]);
                         sb[st2].w[w] = pack_bf16x2(dv2[0], dv2[1]);
                     }
-                }
                 const uint32_t qb_ = lds_addr(qs) + 32 * half * kRowBytes;
                 const uint32_t db_ = lds_addr(ds_) + 32 * half * kRowBytes;
 #pragma unroll
