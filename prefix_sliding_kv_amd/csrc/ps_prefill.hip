@@ -966,10 +966,33 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
     const int h = lane >> 5, col = lane & 31;
     const int T = p.seq_len, hq = p.hq, hkv = p.hkv;
     const int n_kb = (T + kKB - 1) / kKB;
-    const int work = xcd_remap((int)blockIdx.x, n_kb * hkv * p.batch);
-    const int kb = work % n_kb, g = (work / n_kb) % hkv, b = work / (n_kb * hkv);
     const int S0 = (int)p.start_pos;
     const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
+    // Key blocks holding prefix keys are seen by every later query, so they
+    // take the longest: they get the first workgroup ids (dispatched first),
+    // padded to a multiple of the XCD count; the other blocks follow, dealt
+    // to the XCDs in contiguous runs of (sequence, kv head, block).
+    int kb, g, b;
+    {
+        const int n_bg = hkv * p.batch;
+        const int pre_pos = P32 - S0;  // prefix positions inside the chunk
+        const int kb_pre = pre_pos <= 0 ? 0 : ((pre_pos < T ? pre_pos : T) + kKB - 1) / kKB;
+        const int n_pre = kb_pre * n_bg;
+        const int n_pre_pad = (n_pre + kXcds - 1) / kXcds * kXcds;
+        const int id = (int)blockIdx.x;
+        if (id < n_pre_pad) {
+            if (id >= n_pre) return;
+            kb = id % kb_pre;
+            g = (id / kb_pre) % hkv;
+            b = id / (kb_pre * hkv);
+        } else {
+            const int n_rest_kb = n_kb - kb_pre;
+            const int work = xcd_remap(id - n_pre_pad, n_rest_kb * n_bg);
+            kb = kb_pre + work % n_rest_kb;
+            g = (work / n_rest_kb) % hkv;
+            b = work / (n_rest_kb * hkv);
+        }
+    }
     const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
     const float c = p.scale_log2;
 
@@ -1213,7 +1236,13 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
                        static_cast<const uint16_t*>(p.f.out), static_cast<const uint16_t*>(p.dout), p.delta_out, rows);
     const int qp = 32 * kWaves / group;
     const dim3 grid_q((unsigned)(((p.f.seq_len + qp - 1) / qp) * p.f.hkv * p.f.batch));
-    const dim3 grid_k((unsigned)(((p.f.seq_len + kKB - 1) / kKB) * p.f.hkv * p.f.batch));
+    // dK/dV grid: blocks holding prefix keys first (padded to a multiple of 8)
+    const int64_t n_kb = (p.f.seq_len + kKB - 1) / kKB;
+    const int64_t pre_pos = p.f.P - p.f.start_pos;
+    const int64_t kb_pre = pre_pos <= 0 ? 0 : ((pre_pos < p.f.seq_len ? pre_pos : p.f.seq_len) + kKB - 1) / kKB;
+    const int64_t n_bg = (int64_t)p.f.hkv * p.f.batch;
+    const int64_t n_pre_pad = (kb_pre * n_bg + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid_k((unsigned)(n_pre_pad + (n_kb - kb_pre) * n_bg));
     const size_t lds_q = (size_t)kStages * kStageBytes;
     static bool lds_set[8] = {false, false, false, false, false, false, false, false};
     const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
