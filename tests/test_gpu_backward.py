@@ -79,3 +79,46 @@ def test_trainer_backward_small(hq, hkv, B, T, P, W, start, scale):
         check("dv", dv[b], rv)
         # Delta is rowsum(dout * out) of the bf16 forward output
         np.testing.assert_allclose(delta[b], np.sum(as_f32(do[b]) * out[b], axis=-1), rtol=0, atol=1e-3)
+
+
+def test_trainer_backward_qwen_config():
+    """Batch 8, 8192 tokens, P=256, W=2048, Hq=16, Hkv=8, d=128, bf16 (the
+    trainer shape the benchmark times): dq on sampled queries of every batch
+    element, dk and dv on sampled keys (prefix, window and last positions) of
+    two batch elements, every gradient finite.  A key's gradient sums over
+    every query that sees it; the oracle runs those queries in chunks on
+    threads and the chunk results are added."""
+    from concurrent.futures import ThreadPoolExecutor
+    B, T, hq, hkv, d, P, W = 8, 8192, 16, 8, 128, 256, 2048
+    note("backward qwen config")
+    pos, q, k, v, do = bwd_inputs(0, B, 0, T, hq, hkv, d, 1.0)
+    dq, dk, dv, _, _ = run_bwd(q, k, v, do, P, W, 0)
+    assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    sc = 1.0 / math.sqrt(d)
+    rng = np.random.default_rng(2)
+    for b in range(B):
+        sample = np.unique(np.concatenate([[0, 255, 256, 2047, 2048, 6144, T - 1], rng.integers(0, T, 8)]))
+        rq, _, _ = oracle.attention_bwd(as_f32(q[b][sample]), pos[sample], as_f32(k[b]), as_f32(v[b]), pos,
+                                        as_f32(do[b][sample]), P, W, sc, threads=16)
+        check("dq", dq[b][sample], rq)
+    pool = ThreadPoolExecutor(16)
+    rep = hq // hkv
+    for b, g in ((0, 3), (7, 6)):
+        for j in (5, 255, 3000, T - 1):
+            i_hi = T - 1 if j < P else min(T - 1, j + W - 1)
+            qi = np.arange(j, i_hi + 1)
+            chunks = np.array_split(qi, 16)
+            hs = slice(g * rep, (g + 1) * rep)
+            kk, vv = as_f32(k[b][: i_hi + 1, g:g + 1]), as_f32(v[b][: i_hi + 1, g:g + 1])
+
+            def part(ch):
+                _, pk, pv = oracle.attention_bwd(as_f32(q[b][ch, hs]), pos[ch], kk, vv, pos[: i_hi + 1],
+                                                 as_f32(do[b][ch, hs]), P, W, sc)
+                return pk[j, 0], pv[j, 0]
+
+            parts = list(pool.map(part, [c for c in chunks if len(c)]))
+            rk = np.sum([p_[0] for p_ in parts], axis=0)
+            rv = np.sum([p_[1] for p_ in parts], axis=0)
+            check("dk", dk[b][j, g], rk)
+            check("dv", dv[b][j, g], rv)
+    pool.shutdown()
