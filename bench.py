@@ -393,6 +393,31 @@ def prefill_bench(torch, ps, synth, np):
                       "tflops_tiles": round(ft / ms / 1e9, 1),
                       "frac_mfma_tiles": round(ft / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"trainer forward: {res['trainer']}")
+
+    # trainer backward of the same forward: Delta, dQ, dK/dV
+    lse = torch.empty(B, T, HQ, device="cuda")
+    ps.ps_prefill_attn(q, k, v, out, start_pos=0, prefix_len=Pt, window=Wt, scale=scale, lse=lse, stream=stream)
+    do = torch.stack([bf16_dev(torch, synth.rows(1, synth.V, 1, b, pos, HQ, D)) for b in range(B)])
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(B, T, HQ, device="cuda")
+    run3 = lambda: ps.ps_prefill_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, start_pos=0, prefix_len=Pt,
+                                          window=Wt, scale=scale, stream=stream)
+    run3()
+    torch.cuda.synchronize()
+    reps = 5
+    e0.record(stream)
+    for _ in range(reps):
+        run3()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    # five products of the size of one forward product per visible pair:
+    # S (recomputed), dP, dV, dK, dQ
+    fb = exact_flops(0, T, Pt, Wt, HQ, D) * B * 2.5
+    res["trainer_backward"] = {"workload": "backward of the trainer forward above (dq, dk, dv)",
+                               "ms": round(ms, 3), "tflops_exact": round(fb / ms / 1e9, 1),
+                               "frac_mfma_exact": round(fb / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"trainer backward: {res['trainer_backward']}")
     return res
 
 
