@@ -197,7 +197,7 @@ def baselines_bench(torch, ps):
     q = torch.randn(LAYERS, 1, HQ, D, device="cuda").to(torch.bfloat16)
     out = torch.empty_like(q)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    lengths = (8192, 32768, 131072)
+    lengths = (2048, 4096, 8192, 16384, 32768, 65536, 131072)
 
     def rate(pcap, Pn, Wn, L):
         cache = ps.Cache(LAYERS, 1, HQ, HKV, D, pcap, Wn, ps.PS_BF16)
