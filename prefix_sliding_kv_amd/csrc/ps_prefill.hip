@@ -704,9 +704,17 @@ __global__ void __launch_bounds__(256) bwd_delta_kernel(const uint16_t* out, con
     if (row < rows && part == 0) delta[row] = acc;
 }
 
-// Per-lane byte offsets of the transposing operand reads from a row-major
-// tile whose 16-byte chunks are swizzled with k_chunk_swz (row & 15): the
-// same lane pattern as read_vt (row 4h + k/4 of the 16-lane group, dims
+// Tiles the backward reads both as rows (16-byte operand reads: 16 lanes
+// read one chunk of 16 consecutive rows) and transposed (ds_read_b64_tr_b16:
+// 16 lanes read chunks c and c + 1 of 4 consecutive rows, c even) swizzle
+// chunk c of row r to c ^ b_chunk_swz(r), the two 2-bit halves of r & 15
+// swapped: a bijection on every 16 rows (row reads hit 16 distinct chunks),
+// whose upper three bits take 4 distinct values over 4 consecutive rows
+// (transposing reads hit 8 distinct chunks).  Both are conflict-free.
+__device__ inline int b_chunk_swz(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+
+// Per-lane byte offsets of the transposing operand reads from such a tile:
+// the same lane pattern as read_vt (row 4h + k/4 of the 16-lane group, dims
 // 32m + 16(q%2) + 4(k%4)), for the two 8-row halves of a 16-row step; the
 // step itself adds 16 rows, which keeps row & 15.
 __device__ inline void kswz_tr_offsets(int lane, uint32_t (&off)[2][4]) {
@@ -717,12 +725,12 @@ __device__ inline void kswz_tr_offsets(int lane, uint32_t (&off)[2][4]) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const int dim = 32 * m + 16 * (q & 1) + 4 * (gp & 3);
-            off[half][m] = row * kRowBytes + ((((dim >> 3) ^ k_chunk_swz(row)) << 4) | ((dim & 7) << 1));
+            off[half][m] = row * kRowBytes + ((((dim >> 3) ^ b_chunk_swz(row)) << 4) | ((dim & 7) << 1));
         }
     }
 }
 // Transposed operands of 16-row step ST (rows 16 ST .. 16 ST + 15) for the
-// four dim blocks, from a tile at LDS address base with the K swizzle.
+// four dim blocks, from a tile at LDS address base with the b_chunk_swz swizzle.
 __device__ inline void read_t_kswz(int st, uint32_t base, const uint32_t (&off)[2][4], Vec16 (&va)[4]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -736,8 +744,19 @@ __device__ inline void read_t_kswz(int st, uint32_t base, const uint32_t (&off)[
 }
 
 
-// Stage the cursor's tile for the dQ kernel: K and V rows both with the K
-// swizzle (K is read as rows for S^T and transposed for dQ; V as rows for dP^T).
+// Per-lane byte offsets of the dQ kernel's tile loads (waves 0-3, rows 32w ..
+// 32w + 31), chunks placed with b_chunk_swz.
+__device__ inline void lane_offsets_bwd(LaneOffsets& o, int rs, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i) {
+        const int row = (kBNB / kLoadWaves) * (wave & (kLoadWaves - 1)) + 4 * i + (lane >> 4);
+        o.k[i] = o.v[i] = row * rs + (((lane & 15) ^ b_chunk_swz(row)) << 4);
+    }
+}
+
+// Stage the cursor's tile for the dQ kernel: K and V rows both with
+// b_chunk_swz (K is read as rows for S^T and transposed for dQ; V as rows
+// for dP^T).
 __device__ inline void load_tile_bwd(const Cursor& c, const LaneOffsets& lo, int wave, char* stage) {
     const int row0 = c.t * kBNB;
     const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
@@ -838,11 +857,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
     if (total > 0) {
         cursor_enter(cc, 0, walk, views);
         cursor_enter(pc, 0, walk, views);
-        lane_offsets(lo, pc.rs, lane, wave);
+        lane_offsets_bwd(lo, pc.rs, lane, wave);
     }
     auto stage_next = [&](char* stage) {
         load_tile_bwd(pc, lo, wave, stage);
-        if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets(lo, pc.rs, lane, wave);
+        if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets_bwd(lo, pc.rs, lane, wave);
     };
     if (total > 0) stage_next(smem);
     if (total > 1) {
@@ -871,7 +890,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
 #pragma unroll
                 for (int mm = 0; mm < 2; ++mm) {
                     const int krow = 32 * (2 * half + mm) + col;
-                    const int off = krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4);
+                    const int off = krow * kRowBytes + (((2 * kk + h) ^ b_chunk_swz(krow)) << 4);
                     const Vec16 ka = *reinterpret_cast<const Vec16*>(ks_lds + off);
                     const Vec16 va = *reinterpret_cast<const Vec16*>(vs_lds + off);
                     s[mm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qreg[kk]),
@@ -1023,7 +1042,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 32 * wave + 4 * i + (lane >> 4);
-            dma16_asm(vr, row * rs + (((lane & 15) ^ k_chunk_swz(row)) << 4),
+            dma16_asm(vr, row * rs + (((lane & 15) ^ b_chunk_swz(row)) << 4),
                       lds_addr(vblk) + (32 * wave + 4 * i) * kRowBytes);
         }
     }
@@ -1049,7 +1068,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
         for (int i = 0; i < 2; ++i) {
             const int row = 8 * wave + 4 * i + (lane >> 4);
             const int t = ts + row % QS, head = g * G + row / QS;
-            const int off = (t * hq + head) * D * 2 + (((lane & 15) ^ k_chunk_swz(row)) << 4);
+            const int off = (t * hq + head) * D * 2 + (((lane & 15) ^ b_chunk_swz(row)) << 4);
             dma16_asm(qr, off, sb + (8 * wave + 4 * i) * kRowBytes);
             dma16_asm(dr, off, sb + kSubRowBytes + (8 * wave + 4 * i) * kRowBytes);
         }
@@ -1101,7 +1120,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const Vec16 qa = *reinterpret_cast<const Vec16*>(
-                        qs + qrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(qrow)) << 4));
+                        qs + qrow * kRowBytes + (((2 * kk + h) ^ b_chunk_swz(qrow)) << 4));
                     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(qa), as_bf16x8(kreg[kk]), s, 0, 0, 0);
                 }
                 // P from the forward's log-sum-exp (fp32, kept for dS) and its bf16 operand
@@ -1128,9 +1147,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) {
                     const Vec16 da = *reinterpret_cast<const Vec16*>(
-                        ds_ + qrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(qrow)) << 4));
+                        ds_ + qrow * kRowBytes + (((2 * kk + h) ^ b_chunk_swz(qrow)) << 4));
                     const Vec16 vb = *reinterpret_cast<const Vec16*>(
-                        vblk + vrow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(vrow)) << 4));
+                        vblk + vrow * kRowBytes + (((2 * kk + h) ^ b_chunk_swz(vrow)) << 4));
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), as_bf16x8(vb), dp, 0, 0, 0);
                 }
 #pragma unroll
