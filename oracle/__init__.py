@@ -65,6 +65,8 @@ def _load():
         lib.oracle_attention_bwd.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
                                              i64, vp, vp, vp, vp, i64, i64, ctypes.c_double,
                                              vp, vp, vp, ctypes.c_int]
+        lib.oracle_rope_turn.restype = None
+        lib.oracle_rope_turn.argtypes = [i64, ctypes.c_int, vp, vp, ctypes.c_double, vp]
         _lib = lib
     return _lib
 
@@ -148,6 +150,20 @@ def attention_bwd(q, qpos, k, v, kpos, dout, P: int, W: int, scale: float | None
                                  v.ctypes.data, kpos.ctypes.data, dout.ctypes.data, P, W, float(scale),
                                  dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
     return dq, dk, dv
+
+
+def rope_turn(x, delta, base: float):
+    """Turn rows x [..., d] (float32-exact) by ``delta`` positions of rotary
+    encoding (scalar or one per row of the leading dims); float64 result.
+    Reset PE re-encodes retained keys at their new positions this way
+    (agihunt.info summary, paragraph on position encodings)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    d = x.shape[-1]
+    flat = x.reshape(-1, d)
+    dl = np.ascontiguousarray(np.broadcast_to(np.asarray(delta, dtype=np.int64), x.shape[:-1]).reshape(-1))
+    out = np.empty(flat.shape, dtype=np.float64)
+    _load().oracle_rope_turn(flat.shape[0], d, flat.ctypes.data, dl.ctypes.data, float(base), out.ctypes.data)
+    return out.reshape(x.shape)
 
 
 def lse_merge(parts):

@@ -215,3 +215,29 @@ void oracle_attention_bwd(int64_t nq, int hq, int hkv, int d,
             }
     }
 }
+
+/*
+ * Rotary turn of rows by a number of positions: the re-encoding Reset PE
+ * performs on retained keys when it gives them new positions (agihunt.info
+ * summary, paragraph on position encodings; njhaofan.com article, passage
+ * comparing ContinuePE and ResetPE).  Rotary encoding turns the half-split
+ * pair (x_e, x_{e+d/2}), e < d/2, by the angle pos * base^(-2e/d), so moving
+ * a key from position p to p + delta turns each pair by delta * base^(-2e/d):
+ *   out_e       = x_e cos(t) - x_{e+d/2} sin(t)
+ *   out_{e+d/2} = x_e sin(t) + x_{e+d/2} cos(t),   t = delta * base^(-2e/d).
+ *  x     [n][d] float32 rows;  delta [n] positions per row;  out [n][d] double.
+ */
+void oracle_rope_turn(int64_t n, int d, const float* x, const int64_t* delta, double base, double* out) {
+    const int half = d / 2;
+    for (int64_t r = 0; r < n; ++r) {
+        const float* xr = x + r * (int64_t)d;
+        double* o = out + r * (int64_t)d;
+        for (int e = 0; e < half; ++e) {
+            const double t = (double)delta[r] * pow(base, -2.0 * e / (double)d);
+            const double c = cos(t), s = sin(t);
+            const double x0 = xr[e], x1 = xr[e + half];
+            o[e] = x0 * c - x1 * s;
+            o[e + half] = x0 * s + x1 * c;
+        }
+    }
+}

@@ -407,3 +407,35 @@ def test_attention_bwd_sum_invariants():
     kpos2 = np.concatenate([pos, [L + 10]])
     _, dk2, dv2 = oracle.attention_bwd(q, pos, k2, v2, kpos2, dout, P, W)
     assert np.all(dk2[-1] == 0.0) and np.all(dv2[-1] == 0.0)
+
+
+# ------------------------------------------------------------------ Reset PE
+@pytest.mark.parametrize("d,base", [(128, 1e6), (128, 1e4), (64, 1e4)])
+def test_rope_turn_matches_generator_rotation(d, base):
+    """The generator rotates each drawn key at its own position (its own
+    implementation of rotary encoding); turning the unrotated draw of the
+    same position by that position from 0 must give the generator's key."""
+    pos = np.array([0, 1, 17, 4195, 5000, 131071])
+    z = synth.rows(3, synth.K, 0, 0, pos, 4, d, 0.0, synth.F32)
+    want = synth.rows(3, synth.K, 0, 0, pos, 4, d, base, synth.F32)
+    got = oracle.rope_turn(z, pos[:, None], base)
+    np.testing.assert_allclose(got, want, rtol=0, atol=2e-6)
+    # turns compose: p then delta equals p + delta
+    two = oracle.rope_turn(got.astype(np.float32), -1, base)
+    one = oracle.rope_turn(z, pos[:, None] - 1, base)
+    np.testing.assert_allclose(two, one, rtol=0, atol=2e-6)
+
+
+def test_rope_turn_inverse_and_pair_norms():
+    x = synth.rows(4, synth.V, 0, 0, np.arange(6), 2, 128, 0.0, synth.F32)
+    there = oracle.rope_turn(x, 37, 1e6)
+    back = oracle.rope_turn(there.astype(np.float32), -37, 1e6)
+    np.testing.assert_allclose(back, x, rtol=0, atol=1e-6)
+    x64 = x.astype(np.float64)
+    n0 = x64[..., :64] ** 2 + x64[..., 64:] ** 2
+    n1 = there[..., :64] ** 2 + there[..., 64:] ** 2
+    np.testing.assert_allclose(n1, n0, rtol=1e-12, atol=1e-12)
+    # delta 0 is the identity, per-row deltas apply row by row
+    np.testing.assert_array_equal(oracle.rope_turn(x, 0, 1e6), x)
+    per = oracle.rope_turn(x, np.array([[1, 2]] * 6), 1e6)
+    np.testing.assert_allclose(per[:, 1], oracle.rope_turn(x[:, 1], 2, 1e6), rtol=0, atol=0)
