@@ -156,6 +156,26 @@ int ps_decode_step(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, co
                    const void* k_new, const void* v_new, void* out, float* lse, float scale,
                    void* stream);
 
+/* Reset PE support: turn the rotary encoding of every key the window holds
+ * by delta positions, in place.  Under Reset PE the retained tokens are given
+ * new positions and their rotary-encoded keys are recomputed (agihunt.info
+ * summary, paragraph on position encodings; njhaofan.com article, passage
+ * comparing ContinuePE and ResetPE, which the pages reject as the costlier
+ * option).  Rotary encoding turns each half-split pair (x_e, x_{e+d/2}),
+ * e < d/2, by pos * rope_base^(-2e/d); turns compose, so a key stored rotated
+ * at position p becomes the key rotated at p + delta.  For sequence s the
+ * window is the ring rows holding the tokens [max(P_s, pos_s - W), pos_s)
+ * (the cache as left by appending every token < pos_s; batch->pos is read as
+ * that bound, batch->prefix_len as P_s).  Prefix rows and V rows are not
+ * touched.  The turn is computed from double-precision sines and cosines and
+ * applied in fp32 with one rounding per call, so repeated calls on a bf16
+ * cache accumulate rounding like any in-place update.
+ *
+ * Errors: PS_ERR_INVALID (NULL cache or batch, layer out of range, rope_base
+ * <= 1 or not finite, n outside [1, max_seqs]), PS_ERR_HIP. */
+int ps_kv_rerotate(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, int64_t delta, float rope_base,
+                   void* stream);
+
 /* Chunked prefill (cache != NULL) or trainer-side forward (cache == NULL).
  *
  * Every sequence of the batch has the same prefix length P and its chunk

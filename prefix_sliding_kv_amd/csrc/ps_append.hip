@@ -14,6 +14,8 @@
 // the reads and the writes are coalesced.
 #include "ps_internal.h"
 
+#include <hip/hip_bf16.h>
+
 namespace ps {
 namespace {
 
@@ -52,6 +54,56 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_
     }
 }
 
+// Re-rotation of the window's keys by a position change (Reset PE: retained
+// tokens are given new positions and their rotary-encoded keys recomputed --
+// agihunt.info summary, paragraph on position encodings; njhaofan.com
+// article, the passage comparing ContinuePE and ResetPE).  Rotary encoding
+// turns the half-split pair (x_e, x_{e+d/2}) by pos * base^(-2e/d); rotations
+// compose, so a key stored rotated at p becomes the key rotated at p + delta
+// by one more turn of delta * base^(-2e/d).  One lane owns the pair chunks
+// e = 8j .. 8j + 7 and their partners (j = lane % (d/16)); its cosines and
+// sines are computed once, in double precision, and the rotation runs in fp32
+// with one rounding to the cache type.  Memory-bound: every window key row is
+// read and written once; V rows and prefix rows are not touched.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
+    constexpr int LPR = D / 16;          // lanes per row (each: 8 pairs)
+    constexpr int RPW = 256 / LPR;       // rows per workgroup pass
+    const int j = threadIdx.x % LPR;
+    const int rsub = threadIdx.x / LPR;
+    const int g = blockIdx.y, b = blockIdx.z;
+    const int64_t P = p.plen[b];
+    const int64_t pos = p.pos[b];
+    const int64_t lo = pos - p.window > P ? pos - p.window : P;
+    const int64_t count = pos - lo;      // window tokens [lo, pos)
+    if ((int64_t)blockIdx.x * RPW >= count) return;
+    float cs[8], sn[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = 8 * j + i;
+        const double ang = (double)p.delta * pow((double)p.base, -2.0 * e / (double)D);
+        cs[i] = (float)cos(ang);
+        sn[i] = (float)sin(ang);
+    }
+    T* head = static_cast<T*>(p.kc) + ((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head * D;
+    for (int64_t k = (int64_t)blockIdx.x * RPW + rsub; k < count; k += (int64_t)gridDim.x * RPW) {
+        const int64_t t = lo + k;
+        const int64_t slot = (t - P) % p.window;
+        T* row = head + (p.pcap + slot) * D;
+        T a[8], c[8];
+        __builtin_memcpy(a, row + 8 * j, sizeof(a));
+        __builtin_memcpy(c, row + 8 * j + D / 2, sizeof(c));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x0 = (float)a[i], x1 = (float)c[i];
+            a[i] = (T)(x0 * cs[i] - x1 * sn[i]);
+            c[i] = (T)(x0 * sn[i] + x1 * cs[i]);
+        }
+        __builtin_memcpy(row + 8 * j, a, sizeof(a));
+        __builtin_memcpy(row + 8 * j + D / 2, c, sizeof(c));
+    }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = value;
@@ -75,6 +127,21 @@ hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t st
     size_t blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_rerotate(int dtype, int head_dim, const RerotateParams& p, hipStream_t stream) {
+    // one pass of 256 threads covers 256 / (d / 16) rows; the grid covers the
+    // whole window of the longest possible sequence
+    const int rpw = 256 / (head_dim / 16);
+    const dim3 grid((unsigned)((p.window + rpw - 1) / rpw), (unsigned)p.hkv, (unsigned)p.n_seqs);
+    if (dtype == PS_BF16) {
+        if (head_dim == 128) hipLaunchKernelGGL((rerotate_kernel<__hip_bfloat16, 128>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((rerotate_kernel<__hip_bfloat16, 64>), grid, dim3(256), 0, stream, p);
+    } else {
+        if (head_dim == 128) hipLaunchKernelGGL((rerotate_kernel<float, 128>), grid, dim3(256), 0, stream, p);
+        else hipLaunchKernelGGL((rerotate_kernel<float, 64>), grid, dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

@@ -196,6 +196,27 @@ int ps_kv_append_evict(ps_cache* c, int32_t layer, const ps_seq_batch* batch, in
     return hip_status(ps::launch_append(c->desc.dtype, c->desc.head_dim, p, (hipStream_t)stream));
 }
 
+int ps_kv_rerotate(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int64_t delta, float rope_base,
+                   void* stream) {
+    if (!c || !batch_ok(c, batch)) return PS_ERR_INVALID;
+    if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
+    if (!isfinite(rope_base) || !(rope_base > 1.f)) return PS_ERR_INVALID;
+    if (delta == 0) return PS_OK;
+    ps::RerotateParams p{};
+    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
+    p.hkv = c->desc.n_kv_heads;
+    p.pcap = c->desc.prefix_cap;
+    p.window = c->desc.window;
+    p.rows_per_head = c->rows_per_head;
+    p.rows = batch->rows;
+    p.plen = batch->prefix_len;
+    p.pos = batch->pos;
+    p.n_seqs = batch->n;
+    p.delta = delta;
+    p.base = rope_base;
+    return hip_status(ps::launch_rerotate(c->desc.dtype, c->desc.head_dim, p, (hipStream_t)stream));
+}
+
 int ps_decode_attn(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const void* q, void* out, float* lse,
                    float scale, void* stream) {
     return decode_common(c, layer, batch, q, nullptr, nullptr, out, lse, scale, stream);

@@ -101,6 +101,21 @@ struct AppendParams {
 };
 hipError_t launch_append(int dtype, int head_dim, const AppendParams& p, hipStream_t stream);
 
+// Reset-PE re-rotation of the window keys of a batch by delta positions.
+struct RerotateParams {
+    void* kc;              // layer's K region
+    int32_t hkv;
+    int32_t pcap, window;
+    int64_t rows_per_head;
+    const int32_t* rows;
+    const int32_t* plen;
+    const int64_t* pos;    // window = tokens [max(P, pos - W), pos)
+    int32_t n_seqs;
+    int64_t delta;
+    float base;
+};
+hipError_t launch_rerotate(int dtype, int head_dim, const RerotateParams& p, hipStream_t stream);
+
 // Zero-fill of a u32 array with a kernel (safe inside captured graphs).
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t value, hipStream_t stream);
 

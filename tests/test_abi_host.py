@@ -162,3 +162,9 @@ def test_prefill_bwd_rejects_bad_arguments_before_any_launch():
     assert call(delta=0) == ps.PS_ERR_INVALID
     # nothing to do: no pointer is touched
     assert call(seq_len=0, q=0, k=0, v=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0, delta=0) == ps.PS_OK
+
+
+def test_rerotate_rejects_null_cache_before_any_launch():
+    b = ps._SeqBatch(1, None, None, None)
+    assert ps.lib.ps_kv_rerotate(None, 0, ctypes.byref(b), 1, 1e4, None) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_kv_rerotate(None, 0, None, 1, 1e4, None) == ps.PS_ERR_INVALID
