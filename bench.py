@@ -180,9 +180,44 @@ def decode_bench(args, torch, ps, synth, np):
         torch.cuda.synchronize()
         flat[str(L)] = round(1e3 / (t_start.elapsed_time(t_end) / reps), 1)
     log(f"flat cost tok/s by trace length (graph, attention only): {flat}")
+
+    # Reset PE (the variant the pages rejected as costlier): before each
+    # layer's decode step every retained window key is turned back by one
+    # position, in place, so the window keeps positions P .. P+W-1.  Same
+    # caches and step as the graph above, one extra launch per layer.
+    g3 = torch.cuda.CUDAGraph()
+    pos_t.fill_(TRACE - 1)
+    with torch.cuda.stream(gstream):
+        def step_reset():
+            for layer in range(LAYERS):
+                ps.ps_kv_rerotate(cache.handle, layer, batch, -1, 1e6, gstream)
+                ps.ps_decode_step(cache.handle, layer, batch, q_all[layer][s_fixed:s_fixed + 1],
+                                  k_all[layer][s_fixed:s_fixed + 1], v_all[layer][s_fixed:s_fixed + 1],
+                                  out[layer], None, scale, gstream)
+        step_reset()
+        pos_t.add_(1)
+        with torch.cuda.graph(g3, stream=gstream):
+            step_reset()
+            pos_t.add_(1)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        g3.replay()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for _ in range(args.steps):
+        g3.replay()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    reset_ms = t_start.elapsed_time(t_end) / args.steps
+    reset = {"workload": "decode step as above plus, per layer, the in-place turn of all W window keys by "
+                         "-1 position (Reset PE)",
+             "tok_s": round(1e3 / reset_ms, 1), "ms_per_step": round(reset_ms, 4),
+             "extra_us_per_layer": round((reset_ms - graph_ms) * 1e3 / LAYERS, 2),
+             "turn_bytes_per_layer": W * HKV * D * 2 * 2}
+    log(f"reset PE: {reset}")
     cache.close()
     return dict(eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok, mean_launch_us=mean_launch_us,
-                flat=flat)
+                flat=flat, reset_pe=reset)
 
 
 def baselines_bench(torch, ps):
@@ -527,6 +562,7 @@ def main():
         "step_hbm_frac": round(bytes_per_launch * LAYERS / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "eager_tok_s": round(1e3 / dec["eager_ms"], 1),
         "flat_cost_tok_s": dec["flat"],
+        "reset_pe": dec["reset_pe"],
         "prefill": pre,
         "baselines": base_cmp,
         "batched_decode": batched,

@@ -60,11 +60,11 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_
 // article, the passage comparing ContinuePE and ResetPE).  Rotary encoding
 // turns the half-split pair (x_e, x_{e+d/2}) by pos * base^(-2e/d); rotations
 // compose, so a key stored rotated at p becomes the key rotated at p + delta
-// by one more turn of delta * base^(-2e/d).  One lane owns the pair chunks
-// e = 8j .. 8j + 7 and their partners (j = lane % (d/16)); its cosines and
-// sines are computed once, in double precision, and the rotation runs in fp32
-// with one rounding to the cache type.  Memory-bound: every window key row is
-// read and written once; V rows and prefix rows are not touched.
+// by one more turn of delta * base^(-2e/d).  The host computes the d/2
+// cosines and sines in double precision; one lane owns the pair chunks
+// e = 8j .. 8j + 7 and their partners (j = lane % (d/16)) and turns them in
+// fp32 with one rounding to the cache type.  Memory-bound: every window key
+// row is read and written once; V rows and prefix rows are not touched.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
     constexpr int LPR = D / 16;          // lanes per row (each: 8 pairs)
@@ -80,10 +80,8 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
     float cs[8], sn[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int e = 8 * j + i;
-        const double ang = (double)p.delta * pow((double)p.base, -2.0 * e / (double)D);
-        cs[i] = (float)cos(ang);
-        sn[i] = (float)sin(ang);
+        cs[i] = p.cs[8 * j + i];
+        sn[i] = p.sn[8 * j + i];
     }
     T* head = static_cast<T*>(p.kc) + ((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head * D;
     for (int64_t k = (int64_t)blockIdx.x * RPW + rsub; k < count; k += (int64_t)gridDim.x * RPW) {

@@ -212,8 +212,12 @@ int ps_kv_rerotate(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int64_
     p.plen = batch->prefix_len;
     p.pos = batch->pos;
     p.n_seqs = batch->n;
-    p.delta = delta;
-    p.base = rope_base;
+    const int d = c->desc.head_dim;
+    for (int e = 0; e < d / 2; ++e) {
+        const double t = (double)delta * pow((double)rope_base, -2.0 * e / (double)d);
+        p.cs[e] = (float)cos(t);
+        p.sn[e] = (float)sin(t);
+    }
     return hip_status(ps::launch_rerotate(c->desc.dtype, c->desc.head_dim, p, (hipStream_t)stream));
 }
 

@@ -111,8 +111,7 @@ struct RerotateParams {
     const int32_t* plen;
     const int64_t* pos;    // window = tokens [max(P, pos - W), pos)
     int32_t n_seqs;
-    int64_t delta;
-    float base;
+    float cs[64], sn[64];  // cos, sin of the turn of pair e (e < d/2), from the host in double
 };
 hipError_t launch_rerotate(int dtype, int head_dim, const RerotateParams& p, hipStream_t stream);
 
