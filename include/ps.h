@@ -156,6 +156,19 @@ int ps_decode_step(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, co
                    const void* k_new, const void* v_new, void* out, float* lse, float scale,
                    void* stream);
 
+/* ps_kv_append_evict with the rotary position encoding of the new keys fused
+ * in: k_new arrives unrotated and each key is turned at its own position
+ * (Continue PE -- position IDs keep climbing, so a key is encoded once, on
+ * its way into the cache, and never again: agihunt.info summary, paragraph on
+ * position encodings).  The half-split pair (x_e, x_{e+d/2}), e < d/2, turns
+ * by pos * rope_base^(-2e/d); the angle is formed in double precision and
+ * reduced before its fp32 sine and cosine are taken, the turn runs in fp32
+ * with one rounding to the cache type.  V rows are copied unchanged.  Slots,
+ * eviction, layouts and errors as ps_kv_append_evict, plus PS_ERR_INVALID for
+ * rope_base <= 1 or not finite. */
+int ps_kv_append_rope(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, int32_t n_new,
+                      const void* k_new, const void* v_new, float rope_base, void* stream);
+
 /* Reset PE support: turn the rotary encoding of every key the window holds
  * by delta positions, in place.  Under Reset PE the retained tokens are given
  * new positions and their rotary-encoded keys are recomputed (agihunt.info

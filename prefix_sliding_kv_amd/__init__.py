@@ -74,6 +74,8 @@ _SIGS = {
     "ps_cache_kv": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
     "ps_cache_set_decode_split": (ctypes.c_int, [_vp, _i32]),
     "ps_kv_append_evict": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, _vp]),
+    "ps_kv_append_rope": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, ctypes.c_float,
+                                         _vp]),
     "ps_kv_rerotate": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i64, ctypes.c_float, _vp]),
     "ps_decode_attn": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _vp, _vp, _vp,
                                       ctypes.c_float, _vp]),
@@ -175,6 +177,12 @@ def ps_kv_append_evict(handle: int, layer: int, batch: SeqBatch, n_new: int, k_n
                        stream=None) -> None:
     _check(lib.ps_kv_append_evict(ctypes.c_void_p(handle), layer, ctypes.byref(batch._c), n_new,
                                   _ptr(k_new), _ptr(v_new), _stream(stream)), "ps_kv_append_evict")
+
+
+def ps_kv_append_rope(handle: int, layer: int, batch: SeqBatch, n_new: int, k_new, v_new, rope_base: float,
+                      stream=None) -> None:
+    _check(lib.ps_kv_append_rope(ctypes.c_void_p(handle), layer, ctypes.byref(batch._c), n_new, _ptr(k_new),
+                                 _ptr(v_new), float(rope_base), _stream(stream)), "ps_kv_append_rope")
 
 
 def ps_kv_rerotate(handle: int, layer: int, batch: SeqBatch, delta: int, rope_base: float, stream=None) -> None:

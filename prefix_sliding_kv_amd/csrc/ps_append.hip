@@ -54,6 +54,67 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_
     }
 }
 
+// Append with the rotary encoding fused in: the new keys arrive unrotated and
+// each is turned at its own position (Continue PE: the position of a token
+// never changes, so its key is encoded once, on the way into the cache --
+// agihunt.info summary, paragraph on position encodings).  The half-split
+// pair (x_e, x_{e+d/2}) turns by pos * base^(-2e/d): the angle is formed in
+// double precision from the host's frequency table, reduced to [-pi, pi],
+// and its sine and cosine taken in fp32; the turn runs in fp32 with one
+// rounding.  One thread owns 8 pairs of one row (16 bytes of each half of K,
+// and the same bytes of V); slots as in append_kernel.
+template <typename T, int D>
+__global__ void __launch_bounds__(256) append_rope_kernel(AppendParams p, RopeFreqs f) {
+    constexpr int LPR = D / 16;
+    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.hkv * LPR;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
+        const int j = (int)(idx % LPR);
+        int64_t rest = idx / LPR;
+        const int g = (int)(rest % p.hkv);
+        rest /= p.hkv;
+        const int t = (int)(rest % p.n_new);
+        const int b = (int)(rest / p.n_new);
+
+        const int64_t P = p.plen[b];
+        const int64_t pos = p.pos[b] + t;
+        const int64_t last = p.pos[b] + p.n_new - 1;
+        int64_t phys;
+        if (pos < P) {
+            phys = pos;
+        } else {
+            if (pos <= last - p.window) continue;  // overwritten later in this same call
+            phys = p.pcap + (pos - P) % p.window;
+        }
+        const int64_t src = (((int64_t)b * p.n_new + t) * p.hkv + g) * D;
+        const int64_t dst = (((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head + phys) * D;
+        const T* ks = static_cast<const T*>(p.knew) + src;
+        const T* vs = static_cast<const T*>(p.vnew) + src;
+        T* kd = static_cast<T*>(p.kc) + dst;
+        T* vd = static_cast<T*>(p.vc) + dst;
+        T a[8], c[8];
+        __builtin_memcpy(a, ks + 8 * j, sizeof(a));
+        __builtin_memcpy(c, ks + 8 * j + D / 2, sizeof(c));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const double th = (double)pos * f.inv_freq[8 * j + i];
+            const float r = (float)(th - 6.283185307179586 * rint(th * 0.15915494309189535));
+            float sn, cs;
+            sincosf(r, &sn, &cs);
+            const float x0 = (float)a[i], x1 = (float)c[i];
+            a[i] = (T)(x0 * cs - x1 * sn);
+            c[i] = (T)(x0 * sn + x1 * cs);
+        }
+        __builtin_memcpy(kd + 8 * j, a, sizeof(a));
+        __builtin_memcpy(kd + 8 * j + D / 2, c, sizeof(c));
+        T va[8], vc[8];
+        __builtin_memcpy(va, vs + 8 * j, sizeof(va));
+        __builtin_memcpy(vc, vs + 8 * j + D / 2, sizeof(vc));
+        __builtin_memcpy(vd + 8 * j, va, sizeof(va));
+        __builtin_memcpy(vd + 8 * j + D / 2, vc, sizeof(vc));
+    }
+}
+
 // Re-rotation of the window's keys by a position change (Reset PE: retained
 // tokens are given new positions and their rotary-encoded keys recomputed --
 // agihunt.info summary, paragraph on position encodings; njhaofan.com
@@ -139,6 +200,23 @@ hipError_t launch_rerotate(int dtype, int head_dim, const RerotateParams& p, hip
     } else {
         if (head_dim == 128) hipLaunchKernelGGL((rerotate_kernel<float, 128>), grid, dim3(256), 0, stream, p);
         else hipLaunchKernelGGL((rerotate_kernel<float, 64>), grid, dim3(256), 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_append_rope(int dtype, int head_dim, const AppendParams& p, const RopeFreqs& f,
+                              hipStream_t stream) {
+    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.hkv * (head_dim / 16);
+    if (total == 0) return hipSuccess;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    const dim3 grid((unsigned)blocks);
+    if (dtype == PS_BF16) {
+        if (head_dim == 128) hipLaunchKernelGGL((append_rope_kernel<__hip_bfloat16, 128>), grid, dim3(256), 0, stream, p, f);
+        else hipLaunchKernelGGL((append_rope_kernel<__hip_bfloat16, 64>), grid, dim3(256), 0, stream, p, f);
+    } else {
+        if (head_dim == 128) hipLaunchKernelGGL((append_rope_kernel<float, 128>), grid, dim3(256), 0, stream, p, f);
+        else hipLaunchKernelGGL((append_rope_kernel<float, 64>), grid, dim3(256), 0, stream, p, f);
     }
     return hipGetLastError();
 }

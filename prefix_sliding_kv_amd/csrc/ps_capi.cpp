@@ -196,6 +196,33 @@ int ps_kv_append_evict(ps_cache* c, int32_t layer, const ps_seq_batch* batch, in
     return hip_status(ps::launch_append(c->desc.dtype, c->desc.head_dim, p, (hipStream_t)stream));
 }
 
+int ps_kv_append_rope(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int32_t n_new, const void* k_new,
+                      const void* v_new, float rope_base, void* stream) {
+    if (!c || !batch_ok(c, batch) || n_new < 0) return PS_ERR_INVALID;
+    if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
+    if (!isfinite(rope_base) || !(rope_base > 1.f)) return PS_ERR_INVALID;
+    if (n_new == 0) return PS_OK;
+    if (!k_new || !v_new) return PS_ERR_INVALID;
+    ps::AppendParams p{};
+    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
+    p.vc = c->v_region + (size_t)layer * c->layer_bytes;
+    p.hkv = c->desc.n_kv_heads;
+    p.pcap = c->desc.prefix_cap;
+    p.window = c->desc.window;
+    p.rows_per_head = c->rows_per_head;
+    p.rows = batch->rows;
+    p.plen = batch->prefix_len;
+    p.pos = batch->pos;
+    p.n_seqs = batch->n;
+    p.n_new = n_new;
+    p.knew = k_new;
+    p.vnew = v_new;
+    ps::RopeFreqs f{};
+    const int d = c->desc.head_dim;
+    for (int e = 0; e < d / 2; ++e) f.inv_freq[e] = pow((double)rope_base, -2.0 * e / (double)d);
+    return hip_status(ps::launch_append_rope(c->desc.dtype, d, p, f, (hipStream_t)stream));
+}
+
 int ps_kv_rerotate(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int64_t delta, float rope_base,
                    void* stream) {
     if (!c || !batch_ok(c, batch)) return PS_ERR_INVALID;

@@ -100,6 +100,12 @@ struct AppendParams {
     const void* vnew;
 };
 hipError_t launch_append(int dtype, int head_dim, const AppendParams& p, hipStream_t stream);
+// Append with the rotary encoding of the new keys fused in (keys arrive unrotated).
+struct RopeFreqs {
+    double inv_freq[64];   // base^(-2e/d), e < d/2, computed on the host
+};
+hipError_t launch_append_rope(int dtype, int head_dim, const AppendParams& p, const RopeFreqs& f,
+                              hipStream_t stream);
 
 // Reset-PE re-rotation of the window keys of a batch by delta positions.
 struct RerotateParams {

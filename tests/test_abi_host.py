@@ -168,3 +168,8 @@ def test_rerotate_rejects_null_cache_before_any_launch():
     b = ps._SeqBatch(1, None, None, None)
     assert ps.lib.ps_kv_rerotate(None, 0, ctypes.byref(b), 1, 1e4, None) == ps.PS_ERR_INVALID
     assert ps.lib.ps_kv_rerotate(None, 0, None, 1, 1e4, None) == ps.PS_ERR_INVALID
+
+
+def test_append_rope_rejects_null_cache_before_any_launch():
+    b = ps._SeqBatch(1, None, None, None)
+    assert ps.lib.ps_kv_append_rope(None, 0, ctypes.byref(b), 1, None, None, 1e4, None) == ps.PS_ERR_INVALID

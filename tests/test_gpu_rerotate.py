@@ -84,3 +84,63 @@ def test_rerotate_argument_checks():
             ps.ps_kv_rerotate(cache.handle, kw["layer"], b, 1, kw["rope_base"])
     ps.ps_kv_rerotate(cache.handle, 0, b, 0, 1e4)  # delta 0: nothing to do
     cache.close()
+
+
+@pytest.mark.parametrize("dtype,d,base", [(DT_BF16, 128, 1e6), (DT_F32, 64, 1e4)])
+def test_append_with_fused_rope(dtype, d, base):
+    """ps_kv_append_rope against ps_kv_append_evict of the same unrotated keys:
+    V rows and the slot map must be identical, and each K row must be the
+    oracle's turn of the unrotated key by its own position."""
+    from gpu_harness import gen, to_dev
+    import synth
+    note(f"append rope dt={dtype} d={d} base={base}")
+    hq, hkv, W, pcap = 4, 2, 48, 12
+    # (row, P, first pos, count); the last one far out, where the angle needs
+    # its double-precision reduction
+    seqs = [(0, 12, 0, 200), (1, 5, 0, 30), (2, 0, 100, 70), (3, 4, 1_000_000_000, 60)]
+    ca = ps.Cache(1, 4, hq, hkv, d, pcap, W, dtype)
+    cb = ps.Cache(1, 4, hq, hkv, d, pcap, W, dtype)
+    for c in (ca, cb):
+        k, v = c.kv(0)
+        k.zero_()
+        v.zero_()
+    for row, P, p0, n in seqs:
+        pos = np.arange(p0, p0 + n)
+        z = to_dev(gen(7, synth.K, 0, row, pos, hkv, d, 0.0, dtype))  # unrotated draws
+        vv = to_dev(gen(7, synth.V, 0, row, pos, hkv, d, 0.0, dtype))
+        bt = seq_batch(ps, [row], [P], [p0])
+        ps.ps_kv_append_rope(ca.handle, 0, bt, n, z, vv, base)
+        ps.ps_kv_append_evict(cb.handle, 0, bt, n, z, vv)
+    torch.cuda.synchronize()
+    ka, va = ca.kv(0)
+    kb, vb = cb.kv(0)
+    assert torch.equal(va, vb)
+    for row, P, p0, n in seqs:
+        last = p0 + n - 1
+        slots, spos = [], []
+        for p_ in range(min(P, last + 1)):
+            if p_ >= p0:
+                slots.append(p_)
+                spos.append(p_)
+        ring = oracle.expected_ring(last, P, W)
+        for r, p_ in enumerate(ring):
+            if p_ >= p0:
+                slots.append(pcap + r)
+                spos.append(int(p_))
+        got = dev_to_f32(ka[row][:, slots])                  # [hkv][n][d]
+        raw = dev_to_f32(kb[row][:, slots])
+        want = oracle.rope_turn(raw, np.array(spos)[None, :], base)
+        h = d // 2
+        pn = np.sqrt(raw[..., :h].astype(np.float64) ** 2 + raw[..., h:].astype(np.float64) ** 2)
+        pn = np.concatenate([pn, pn], axis=-1)
+        if dtype == DT_BF16:
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(np.abs(want), 2.0 ** -126))) - 7)
+            bound = np.maximum(ulp, 2e-6 * pn)
+        else:
+            bound = 2e-6 * (np.abs(want) + pn)
+        assert np.all(np.abs(got - want) <= bound), (row, float(np.max(np.abs(got - want) / bound)))
+        # slots this call never wrote are untouched (still zero)
+        other = sorted(set(range(pcap + W)) - set(slots))
+        assert torch.count_nonzero(ka[row][:, other]) == 0
+    ca.close()
+    cb.close()
