@@ -252,23 +252,6 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
     return u;
 }
 
-// Scheduling recipe for a region with N LDS operand reads each feeding one
-// MFMA: issue 4 reads, then alternate one MFMA with one read, then the
-// remaining MFMAs, so four reads are always in flight ahead of their use.
-template <int N, int RPM>
-__device__ inline void pipeline_reads_and_mfma() {
-    constexpr int kAhead = 4;
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read(s)
-#pragma unroll
-    for (int i = 0; i < N - kAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // DS read(s)
-    }
-#pragma unroll
-    for (int i = 0; i < kAhead; ++i) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-}
-
 // Sum of the 8 bf16 values of a packed P operand, in fp32 (v_dot2 with ones):
 // the row sum then matches the bf16 P the P.V product uses.
 __device__ inline float sum_bf16x8(const Vec16& v) {
