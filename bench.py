@@ -17,10 +17,12 @@ Printed as one JSON line (rank 0, N=1):
                98304..102399) and trainer forward (B=8, T=8192, P=256,
                W=2048): TFLOP/s on exact visible pairs and on unskipped tiles
   baselines    full attention (W >= L) and a vanilla sliding window (P = 0)
-               through the same decode kernel at 8K / 32K / 128K, beside
+               through the same decode kernel from 2K to 128K, beside
                Prefix Sliding (attention-only tok/s)
   batched_decode  64 ragged sequences (P ~ U[64,512], L ~ U[4K,128K]), one
                token each per layer: tok/s and achieved HBM GB/s
+  rollouts_decode 64 rollouts of one prompt (P=1024) with the prompt in one
+               shared prefix block, and with private copies
 """
 from __future__ import annotations
 
@@ -237,9 +239,8 @@ def baselines_bench(torch, ps):
     def rate(pcap, Pn, Wn, L):
         cache = ps.Cache(LAYERS, 1, HQ, HKV, D, pcap, Wn, ps.PS_BF16)
         for layer in range(LAYERS):
-            k, v = cache.kv(layer)
-            k.normal_()
-            v.normal_()
+            for t in cache.blocks(layer):
+                t.normal_()
         plen = torch.full((1,), Pn, dtype=torch.int32, device="cuda")
         pos_t = torch.full((1,), L - 1, dtype=torch.int64, device="cuda")
         batch = ps.SeqBatch(rows, plen, pos_t)
@@ -290,9 +291,8 @@ def batched_bench(torch, ps, np):
         Ls[s] = rng.integers(4096, Ps[s] + W)
     cache = ps.Cache(LAYERS, n, HQ, HKV, D, pcap, W, ps.PS_BF16)
     for layer in range(LAYERS):
-        k, v = cache.kv(layer)
-        k.normal_()
-        v.normal_()
+        for t in cache.blocks(layer):
+            t.normal_()
     rows = torch.arange(n, dtype=torch.int32, device="cuda")
     plen = torch.tensor(Ps, dtype=torch.int32, device="cuda")
     pos_t = torch.tensor(Ls - 1, dtype=torch.int64, device="cuda")
@@ -330,6 +330,62 @@ def batched_bench(torch, ps, np):
     log(f"batched ragged decode: {res}")
     del g
     cache.close()
+    return res
+
+
+def rollouts_bench(torch, ps, np):
+    """64 rollouts of one prompt (P = 1024, W = 4096, L_s ~ U[8K, 128K],
+    seeded), 28 layers, one decode token per sequence per layer (attention
+    only, one captured graph), twice: with the prompt's rows in one prefix
+    block that all rollouts share, and with a private copy per rollout.
+    Unique bytes per step = 28 * 2*Hkv*d*2 * (P_copies * P + sum_s min(W, L_s - P))."""
+    n, P = 64, 1024
+    rng = np.random.default_rng(1001)
+    Ls = rng.integers(8192, TRACE + 1, size=n)
+    res = {"workload": "64 rollouts of one prompt, P=1024, W=4096, L ~ U[8K,128K], 28 layers, attention only"}
+    for shared in (True, False):
+        cache = ps.Cache(LAYERS, n, HQ, HKV, D, P, W, ps.PS_BF16, prefix_blocks=1 if shared else n)
+        for layer in range(LAYERS):
+            for t in cache.blocks(layer):
+                t.normal_()
+        rows = torch.arange(n, dtype=torch.int32, device="cuda")
+        prows = torch.zeros(n, dtype=torch.int32, device="cuda") if shared else rows
+        batch = ps.SeqBatch(rows, torch.full((n,), P, dtype=torch.int32, device="cuda"),
+                            torch.tensor(Ls - 1, dtype=torch.int64, device="cuda"), prows)
+        q = torch.randn(LAYERS, n, HQ, D, device="cuda").to(torch.bfloat16)
+        out = torch.empty_like(q)
+        scale = 1.0 / math.sqrt(D)
+        stream = torch.cuda.current_stream()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gs):
+            for layer in range(LAYERS):
+                ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None, scale, gs)
+            with torch.cuda.graph(g, stream=gs):
+                for layer in range(LAYERS):
+                    ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None, scale, gs)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        row_bytes = 2 * HKV * D * 2
+        uniq = LAYERS * row_bytes * ((1 if shared else n) * P + sum(min(W, int(L) - P) for L in Ls))
+        gbs = uniq / (ms * 1e-3) / 1e9
+        res["shared_prefix" if shared else "private_prefix"] = {
+            "ms_per_step": round(ms, 4), "tok_s": round(n * 1e3 / ms, 1), "unique_bytes_per_step": uniq,
+            "cache_kv_bytes": LAYERS * row_bytes * ((1 if shared else n) * P + n * W),
+            "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        del g
+        cache.close()
+    log(f"rollouts of one prompt: {res}")
     return res
 
 
@@ -536,6 +592,7 @@ def main():
     pre = {} if args.no_prefill else prefill_bench(torch, ps, synth, np)
     base_cmp = {} if args.no_baselines else baselines_bench(torch, ps)
     batched = {} if args.no_baselines else batched_bench(torch, ps, np)
+    rollouts = {} if args.no_baselines else rollouts_bench(torch, ps, np)
     cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
     line = {
         "metric": METRIC,
@@ -566,6 +623,7 @@ def main():
         "prefill": pre,
         "baselines": base_cmp,
         "batched_decode": batched,
+        "rollouts_decode": rollouts,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

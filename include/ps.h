@@ -57,33 +57,45 @@ typedef enum {
 typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
 
 /* Static shape of a cache.  One cache holds every layer of up to max_seqs
- * sequences.  Per (layer, sequence, kv head) it has prefix_cap PREFIX slots
- * and a W-slot RING: the two-region cache of the papers.ananclaw.com explainer,
- * section "核心方法" (PREFIX block kept read-only after prefill, WINDOW block of
- * the last W tokens, middle evicted).  Its size is bounded by P + W tokens no
- * matter how long the trace grows (njhaofan.com, same section as above). */
+ * sequences as two pools of blocks: PREFIX blocks of prefix_cap slots and
+ * WINDOW blocks of W slots (a ring), per (layer, block, kv head) -- the
+ * two-block cache of the papers.ananclaw.com explainer, section "核心方法"
+ * (PREFIX block kept read-only after prefill, WINDOW block of the last W
+ * tokens, middle evicted).  A sequence uses one window block (its row) and
+ * one prefix block, which several sequences may share: rollouts of the same
+ * prompt keep one copy of the pinned prefix (the explainer notes the policy
+ * is orthogonal to paged memory management and can be combined with it).
+ * A sequence's size is bounded by P + W tokens no matter how long the trace
+ * grows (njhaofan.com, same section as above). */
 typedef struct {
-    int32_t n_layers;    /* >= 1 */
-    int32_t max_seqs;    /* >= 1 */
-    int32_t n_q_heads;   /* Hq >= 1, multiple of n_kv_heads */
-    int32_t n_kv_heads;  /* Hkv >= 1 */
-    int32_t head_dim;    /* d: 64 or 128 */
-    int32_t prefix_cap;  /* largest prefix length P any sequence may use, >= 0 */
-    int32_t window;      /* W >= 1 */
-    int32_t dtype;       /* ps_dtype of K, V, queries and outputs */
+    int32_t n_layers;       /* >= 1 */
+    int32_t max_seqs;       /* >= 1: window blocks (sequence rows) */
+    int32_t n_q_heads;      /* Hq >= 1, multiple of n_kv_heads */
+    int32_t n_kv_heads;     /* Hkv >= 1 */
+    int32_t head_dim;       /* d: 64 or 128 */
+    int32_t prefix_cap;     /* largest prefix length P any sequence may use, >= 0 */
+    int32_t window;         /* W >= 1 */
+    int32_t dtype;          /* ps_dtype of K, V, queries and outputs */
+    int32_t prefix_blocks;  /* prefix blocks, >= 0; 0 means max_seqs (one per row) */
 } ps_cache_desc;
 
 typedef struct ps_cache ps_cache; /* opaque host handle */
 
-/* A batch of sequences for append / decode.  All three arrays are DEVICE
- * arrays of length n.  Preconditions (not checked): rows are distinct values
- * in [0, max_seqs); 0 <= prefix_len[b] <= prefix_cap; pos[b] >= 0. */
+/* A batch of sequences for append / decode.  All arrays are DEVICE arrays of
+ * length n.  Preconditions (not checked): rows are distinct values in
+ * [0, max_seqs); prefix_rows values in [0, prefix_blocks); 0 <= prefix_len[b]
+ * <= prefix_cap; pos[b] >= 0.  Sequences that share a prefix block have the
+ * same prefix_len; its rows are appended once (by any one of them) and only
+ * read afterwards. */
 typedef struct {
     int32_t n;                  /* number of sequences in the call, 1..max_seqs */
-    const int32_t* rows;        /* device: cache row of each sequence */
+    const int32_t* rows;        /* device: window block (cache row) of each sequence */
     const int32_t* prefix_len;  /* device: P of each sequence */
     const int64_t* pos;         /* device: position of the first new token /
                                    of the query (see each call) */
+    const int32_t* prefix_rows; /* device: prefix block of each sequence, or NULL:
+                                   prefix block = rows[b] (requires prefix_blocks
+                                   == max_seqs) */
 } ps_seq_batch;
 
 /* Bytes of device memory a cache with this shape needs (K and V for every
@@ -103,14 +115,15 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
 /* Free the host handle.  The device buffer stays the caller's.  NULL is a no-op. */
 int ps_cache_destroy(ps_cache* cache);
 
-/* Device addresses of layer `layer`'s K and V regions.  Layout of each:
- *   [max_seqs][n_kv_heads][prefix_cap + window][head_dim]   (cache dtype)
- * Row s < prefix_cap of a (sequence, kv head) holds prefix position s; row
- * prefix_cap + r holds the token at the position p >= P with
- * (p - P) mod W == r that was appended last.  For inspection and snapshot /
- * restore (a plain device copy of the whole buffer restores a cache).
- * Errors: PS_ERR_INVALID. */
-int ps_cache_kv(const ps_cache* cache, int32_t layer, void** k, void** v);
+/* Device addresses of layer `layer`'s K and V pools.  Layouts (cache dtype):
+ *   prefix pools  [prefix_blocks][n_kv_heads][prefix_cap][head_dim]
+ *   window pools  [max_seqs][n_kv_heads][window][head_dim]
+ * Slot s of a prefix block holds prefix position s; slot r of a window block
+ * holds the token at the position p >= P with (p - P) mod W == r that was
+ * appended last.  For inspection and snapshot / restore (a plain device copy
+ * of the whole buffer restores a cache).  Errors: PS_ERR_INVALID. */
+int ps_cache_blocks(const ps_cache* cache, int32_t layer, void** k_prefix, void** v_prefix,
+                    void** k_window, void** v_window);
 
 /* Split-K granularity of decode: rows (keys) handled per workgroup.  0 picks
  * automatically (default); otherwise one of 16, 32, 64, 128, 256, 512 for
@@ -120,8 +133,9 @@ int ps_cache_kv(const ps_cache* cache, int32_t layer, void** k, void** v);
 int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
 
 /* Append n_new consecutive tokens per sequence to layer `layer`: token t of
- * sequence b has position pos[b] + t.  A position p < P goes to prefix row p;
- * p >= P goes to ring row (p - P) mod W, overwriting the token at p - W, which
+ * sequence b has position pos[b] + t.  A position p < P goes to slot p of the
+ * sequence's prefix block; p >= P goes to slot (p - P) mod W of its window
+ * block, overwriting the token at p - W, which
  * is exactly the token that falls out of the window (positional eviction:
  * njhaofan.com section above; papers.ananclaw.com "被丢弃的中间区").  When more
  * than W ring-bound tokens arrive in one call only the last W are written, so
@@ -223,13 +237,16 @@ typedef struct {
     int64_t start_pos;      /* position of chunk token 0, >= 0 */
     int64_t prefix_len;     /* P >= 0 (<= prefix_cap in cache mode) */
     int64_t window;         /* W >= 1 (must equal the cache's W in cache mode) */
-    const int32_t* rows;    /* device [B] cache rows (cache mode), else NULL */
+    const int32_t* rows;    /* device [B] window blocks (cache mode), else NULL */
     const void* q;          /* device [B][T][n_q_heads][head_dim] */
     const void* k;          /* device [B][T][n_kv_heads][head_dim] */
     const void* v;          /* device [B][T][n_kv_heads][head_dim] */
     void* out;              /* device [B][T][n_q_heads][head_dim] */
     float* lse;             /* device [B][T][n_q_heads] natural log, or NULL */
     float scale;            /* multiplier of q.k, > 0 */
+    const int32_t* prefix_rows; /* device [B] prefix blocks (cache mode), or NULL:
+                                   prefix block = rows[b] (requires prefix_blocks
+                                   == max_seqs) */
 } ps_prefill_args;
 
 /* Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,

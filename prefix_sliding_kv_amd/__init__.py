@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "PS_BF16", "PS_F32", "PSError", "CacheDesc", "Cache", "lib",
-    "ps_cache_bytes", "ps_cache_create", "ps_cache_destroy", "ps_cache_kv",
+    "ps_cache_bytes", "ps_cache_create", "ps_cache_destroy", "ps_cache_blocks",
     "ps_cache_set_decode_split", "ps_kv_append_evict", "ps_decode_attn", "ps_decode_step",
     "ps_prefill_attn", "ps_tile_class", "ps_status_str", "ps_version", "SeqBatch",
 ]
@@ -36,12 +36,13 @@ class CacheDesc(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("prefix_cap", ctypes.c_int32),
-                ("window", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("window", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("prefix_blocks", ctypes.c_int32)]
 
 
 class _SeqBatch(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("rows", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
-                ("pos", ctypes.c_void_p)]
+                ("pos", ctypes.c_void_p), ("prefix_rows", ctypes.c_void_p)]
 
 
 class _PrefillArgs(ctypes.Structure):
@@ -52,7 +53,7 @@ class _PrefillArgs(ctypes.Structure):
                 ("prefix_len", ctypes.c_int64), ("window", ctypes.c_int64),
                 ("rows", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("prefix_rows", ctypes.c_void_p)]
 
 
 class _PrefillBwdArgs(ctypes.Structure):
@@ -71,7 +72,8 @@ _SIGS = {
     "ps_cache_create": (ctypes.c_int, [ctypes.POINTER(CacheDesc), _vp, ctypes.c_size_t, _vp,
                                        ctypes.POINTER(_vp)]),
     "ps_cache_destroy": (ctypes.c_int, [_vp]),
-    "ps_cache_kv": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "ps_cache_blocks": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
     "ps_cache_set_decode_split": (ctypes.c_int, [_vp, _i32]),
     "ps_kv_append_evict": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, _vp]),
     "ps_kv_append_rope": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, ctypes.c_float,
@@ -146,10 +148,12 @@ def ps_cache_destroy(handle: int) -> None:
     _check(lib.ps_cache_destroy(ctypes.c_void_p(handle)), "ps_cache_destroy")
 
 
-def ps_cache_kv(handle: int, layer: int):
-    k, v = ctypes.c_void_p(), ctypes.c_void_p()
-    _check(lib.ps_cache_kv(ctypes.c_void_p(handle), layer, ctypes.byref(k), ctypes.byref(v)), "ps_cache_kv")
-    return k.value, v.value
+def ps_cache_blocks(handle: int, layer: int):
+    """Device addresses (k_prefix, v_prefix, k_window, v_window) of a layer's pools."""
+    ptrs = [ctypes.c_void_p() for _ in range(4)]
+    _check(lib.ps_cache_blocks(ctypes.c_void_p(handle), layer, *[ctypes.byref(p) for p in ptrs]),
+           "ps_cache_blocks")
+    return tuple(p.value for p in ptrs)
 
 
 def ps_cache_set_decode_split(handle: int, rows_per_split: int) -> None:
@@ -158,15 +162,21 @@ def ps_cache_set_decode_split(handle: int, rows_per_split: int) -> None:
 
 
 class SeqBatch:
-    """Device-resident per-sequence metadata: cache rows (int32), prefix
-    lengths (int32) and positions (int64), each a CUDA tensor of length n."""
+    """Device-resident per-sequence metadata: window blocks (cache rows, int32),
+    prefix lengths (int32), positions (int64) and optionally prefix blocks
+    (int32; None = each sequence's own row), each a CUDA tensor of length n."""
 
-    def __init__(self, rows: torch.Tensor, prefix_len: torch.Tensor, pos: torch.Tensor):
+    def __init__(self, rows: torch.Tensor, prefix_len: torch.Tensor, pos: torch.Tensor,
+                 prefix_rows: torch.Tensor | None = None):
         assert rows.dtype == torch.int32 and prefix_len.dtype == torch.int32 and pos.dtype == torch.int64
         assert rows.is_cuda and prefix_len.is_cuda and pos.is_cuda
         assert rows.numel() == prefix_len.numel() == pos.numel()
-        self.rows, self.prefix_len, self.pos = rows, prefix_len, pos
-        self._c = _SeqBatch(rows.numel(), rows.data_ptr(), prefix_len.data_ptr(), pos.data_ptr())
+        if prefix_rows is not None:
+            assert prefix_rows.dtype == torch.int32 and prefix_rows.is_cuda
+            assert prefix_rows.numel() == rows.numel()
+        self.rows, self.prefix_len, self.pos, self.prefix_rows = rows, prefix_len, pos, prefix_rows
+        self._c = _SeqBatch(rows.numel(), rows.data_ptr(), prefix_len.data_ptr(), pos.data_ptr(),
+                            prefix_rows.data_ptr() if prefix_rows is not None else None)
 
     @property
     def n(self) -> int:
@@ -204,7 +214,7 @@ def ps_decode_step(handle: int, layer: int, batch: SeqBatch, q, k_new, v_new, ou
 
 def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: int, scale: float,
                     lse=None, cache: int | None = None, layer: int = 0, rows=None,
-                    dtype: int | None = None, stream=None) -> None:
+                    prefix_rows=None, dtype: int | None = None, stream=None) -> None:
     """q/out [B][T][Hq][d], k/v [B][T][Hkv][d] CUDA tensors; ``cache`` None means
     trainer mode (self-attention over the given tokens only)."""
     B, T, hq, d = q.shape
@@ -213,7 +223,8 @@ def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: in
         dtype = PS_BF16 if q.dtype == torch.bfloat16 else PS_F32
     a = _PrefillArgs(cache or 0, layer, B, T, hq, hkv, d, dtype, start_pos, prefix_len, window,
                      rows.data_ptr() if rows is not None else 0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                     out.data_ptr(), lse.data_ptr() if lse is not None else 0, scale)
+                     out.data_ptr(), lse.data_ptr() if lse is not None else 0, scale,
+                     prefix_rows.data_ptr() if prefix_rows is not None else 0)
     _check(lib.ps_prefill_attn(ctypes.byref(a), _stream(stream)), "ps_prefill_attn")
 
 
@@ -236,8 +247,9 @@ class Cache:
     the library only carves it)."""
 
     def __init__(self, n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window,
-                 dtype=PS_BF16, device="cuda", stream=None):
-        self.desc = CacheDesc(n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window, dtype)
+                 dtype=PS_BF16, device="cuda", stream=None, prefix_blocks: int = 0):
+        self.desc = CacheDesc(n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window, dtype,
+                              prefix_blocks)
         nbytes = ps_cache_bytes(self.desc)
         if nbytes == 0:
             raise PSError(PS_ERR_INVALID, "ps_cache_bytes")
@@ -246,19 +258,37 @@ class Cache:
         self.handle = ps_cache_create(self.desc, self.buffer, stream)
         self.dtype = _TORCH_DTYPE[dtype]
 
-    def kv(self, layer: int):
-        """Views of layer's K and V regions: [max_seqs][Hkv][prefix_cap+W][d]."""
-        kp, vp = ps_cache_kv(self.handle, layer)
+    @property
+    def prefix_blocks(self) -> int:
+        return self.desc.prefix_blocks or self.desc.max_seqs
+
+    def blocks(self, layer: int):
+        """Views of layer's pools: (k_prefix, v_prefix) [prefix_blocks][Hkv][prefix_cap][d]
+        and (k_window, v_window) [max_seqs][Hkv][W][d]."""
         d = self.desc
-        shape = (d.max_seqs, d.n_kv_heads, d.prefix_cap + d.window, d.head_dim)
         esz = 2 if d.dtype == PS_BF16 else 4
         base = self.buffer.data_ptr()
-        n = d.max_seqs * d.n_kv_heads * (d.prefix_cap + d.window) * d.head_dim
+        shapes = [(self.prefix_blocks, d.n_kv_heads, d.prefix_cap, d.head_dim)] * 2 + \
+                 [(d.max_seqs, d.n_kv_heads, d.window, d.head_dim)] * 2
         out = []
-        for p in (kp, vp):
+        for p, shape in zip(ps_cache_blocks(self.handle, layer), shapes):
+            n = shape[0] * shape[1] * shape[2] * shape[3]
             off = p - base
             out.append(self.buffer[off:off + n * esz].view(self.dtype).view(shape))
-        return out[0], out[1]
+        return tuple(out)
+
+    def seq_kv(self, layer: int, row: int, prefix_row: int | None = None):
+        """Copies of one sequence's K and V slots, [Hkv][prefix_cap+W][d]: the
+        prefix block's slots followed by the window block's."""
+        kp, vp, kw, vw = self.blocks(layer)
+        pr = row if prefix_row is None else prefix_row
+        return torch.cat([kp[pr], kw[row]], dim=1), torch.cat([vp[pr], vw[row]], dim=1)
+
+    def fill_(self, value: float) -> None:
+        """Set every K/V slot of every layer (not the workspace) to ``value``."""
+        for layer in range(self.desc.n_layers):
+            for t in self.blocks(layer):
+                t.fill_(value)
 
     def close(self):
         if getattr(self, "handle", None):

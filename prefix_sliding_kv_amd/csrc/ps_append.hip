@@ -24,33 +24,35 @@ struct alignas(16) Vec16 {
 };
 
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_per_row) {
-    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.hkv * pieces_per_row;
+    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.c.hkv * pieces_per_row;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t row_bytes = (int64_t)pieces_per_row * 16;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
         const int piece = (int)(idx % pieces_per_row);
         int64_t rest = idx / pieces_per_row;
-        const int g = (int)(rest % p.hkv);
-        rest /= p.hkv;
+        const int g = (int)(rest % p.c.hkv);
+        rest /= p.c.hkv;
         const int t = (int)(rest % p.n_new);
         const int b = (int)(rest / p.n_new);
 
         const int64_t P = p.plen[b];
         const int64_t pos = p.pos[b] + t;
         const int64_t last = p.pos[b] + p.n_new - 1;
-        int64_t phys;
-        if (pos < P) {
-            phys = pos;
-        } else {
-            if (pos <= last - p.window) continue;  // overwritten later in this same call
-            phys = p.pcap + (pos - P) % p.window;
+        char* kd;
+        char* vd;
+        if (pos < P) {  // slot pos of the prefix block
+            const int64_t row = ((int64_t)p.c.prows[b] * p.c.hkv + g) * p.c.pcap + pos;
+            kd = static_cast<char*>(p.c.kpre) + row * row_bytes;
+            vd = static_cast<char*>(p.c.vpre) + row * row_bytes;
+        } else {        // slot (pos - P) mod W of the window block
+            if (pos <= last - p.c.window) continue;  // overwritten later in this same call
+            const int64_t row = ((int64_t)p.c.rows[b] * p.c.hkv + g) * p.c.window + (pos - P) % p.c.window;
+            kd = static_cast<char*>(p.c.kwin) + row * row_bytes;
+            vd = static_cast<char*>(p.c.vwin) + row * row_bytes;
         }
-        const int64_t src = ((((int64_t)b * p.n_new + t) * p.hkv + g) * row_bytes) + piece * 16;
-        const int64_t dst = ((((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head + phys) * row_bytes) + piece * 16;
-        *reinterpret_cast<Vec16*>(static_cast<char*>(p.kc) + dst) =
-            *reinterpret_cast<const Vec16*>(static_cast<const char*>(p.knew) + src);
-        *reinterpret_cast<Vec16*>(static_cast<char*>(p.vc) + dst) =
-            *reinterpret_cast<const Vec16*>(static_cast<const char*>(p.vnew) + src);
+        const int64_t src = ((((int64_t)b * p.n_new + t) * p.c.hkv + g) * row_bytes) + piece * 16;
+        *reinterpret_cast<Vec16*>(kd + piece * 16) = *reinterpret_cast<const Vec16*>(static_cast<const char*>(p.knew) + src);
+        *reinterpret_cast<Vec16*>(vd + piece * 16) = *reinterpret_cast<const Vec16*>(static_cast<const char*>(p.vnew) + src);
     }
 }
 
@@ -66,32 +68,34 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_
 template <typename T, int D>
 __global__ void __launch_bounds__(256) append_rope_kernel(AppendParams p, RopeFreqs f) {
     constexpr int LPR = D / 16;
-    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.hkv * LPR;
+    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.c.hkv * LPR;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total; idx += stride) {
         const int j = (int)(idx % LPR);
         int64_t rest = idx / LPR;
-        const int g = (int)(rest % p.hkv);
-        rest /= p.hkv;
+        const int g = (int)(rest % p.c.hkv);
+        rest /= p.c.hkv;
         const int t = (int)(rest % p.n_new);
         const int b = (int)(rest / p.n_new);
 
         const int64_t P = p.plen[b];
         const int64_t pos = p.pos[b] + t;
         const int64_t last = p.pos[b] + p.n_new - 1;
-        int64_t phys;
+        T* kd;
+        T* vd;
         if (pos < P) {
-            phys = pos;
+            const int64_t row = ((int64_t)p.c.prows[b] * p.c.hkv + g) * p.c.pcap + pos;
+            kd = static_cast<T*>(p.c.kpre) + row * D;
+            vd = static_cast<T*>(p.c.vpre) + row * D;
         } else {
-            if (pos <= last - p.window) continue;  // overwritten later in this same call
-            phys = p.pcap + (pos - P) % p.window;
+            if (pos <= last - p.c.window) continue;  // overwritten later in this same call
+            const int64_t row = ((int64_t)p.c.rows[b] * p.c.hkv + g) * p.c.window + (pos - P) % p.c.window;
+            kd = static_cast<T*>(p.c.kwin) + row * D;
+            vd = static_cast<T*>(p.c.vwin) + row * D;
         }
-        const int64_t src = (((int64_t)b * p.n_new + t) * p.hkv + g) * D;
-        const int64_t dst = (((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head + phys) * D;
+        const int64_t src = (((int64_t)b * p.n_new + t) * p.c.hkv + g) * D;
         const T* ks = static_cast<const T*>(p.knew) + src;
         const T* vs = static_cast<const T*>(p.vnew) + src;
-        T* kd = static_cast<T*>(p.kc) + dst;
-        T* vd = static_cast<T*>(p.vc) + dst;
         T a[8], c[8];
         __builtin_memcpy(a, ks + 8 * j, sizeof(a));
         __builtin_memcpy(c, ks + 8 * j + D / 2, sizeof(c));
@@ -135,7 +139,7 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
     const int g = blockIdx.y, b = blockIdx.z;
     const int64_t P = p.plen[b];
     const int64_t pos = p.pos[b];
-    const int64_t lo = pos - p.window > P ? pos - p.window : P;
+    const int64_t lo = pos - p.c.window > P ? pos - p.c.window : P;
     const int64_t count = pos - lo;      // window tokens [lo, pos)
     if ((int64_t)blockIdx.x * RPW >= count) return;
     float cs[8], sn[8];
@@ -144,11 +148,11 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
         cs[i] = p.cs[8 * j + i];
         sn[i] = p.sn[8 * j + i];
     }
-    T* head = static_cast<T*>(p.kc) + ((int64_t)p.rows[b] * p.hkv + g) * p.rows_per_head * D;
+    T* head = static_cast<T*>(p.c.kwin) + ((int64_t)p.c.rows[b] * p.c.hkv + g) * p.c.window * D;
     for (int64_t k = (int64_t)blockIdx.x * RPW + rsub; k < count; k += (int64_t)gridDim.x * RPW) {
         const int64_t t = lo + k;
-        const int64_t slot = (t - P) % p.window;
-        T* row = head + (p.pcap + slot) * D;
+        const int64_t slot = (t - P) % p.c.window;
+        T* row = head + slot * D;
         T a[8], c[8];
         __builtin_memcpy(a, row + 8 * j, sizeof(a));
         __builtin_memcpy(c, row + 8 * j + D / 2, sizeof(c));
@@ -173,7 +177,7 @@ __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
 hipError_t launch_append(int dtype, int head_dim, const AppendParams& p, hipStream_t stream) {
     const int elem = dtype == PS_BF16 ? 2 : 4;
     const int pieces = head_dim * elem / 16;
-    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.hkv * pieces;
+    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.c.hkv * pieces;
     if (total == 0) return hipSuccess;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
@@ -193,7 +197,7 @@ hipError_t launch_rerotate(int dtype, int head_dim, const RerotateParams& p, hip
     // one pass of 256 threads covers 256 / (d / 16) rows; the grid covers the
     // whole window of the longest possible sequence
     const int rpw = 256 / (head_dim / 16);
-    const dim3 grid((unsigned)((p.window + rpw - 1) / rpw), (unsigned)p.hkv, (unsigned)p.n_seqs);
+    const dim3 grid((unsigned)((p.c.window + rpw - 1) / rpw), (unsigned)p.c.hkv, (unsigned)p.n_seqs);
     if (dtype == PS_BF16) {
         if (head_dim == 128) hipLaunchKernelGGL((rerotate_kernel<__hip_bfloat16, 128>), grid, dim3(256), 0, stream, p);
         else hipLaunchKernelGGL((rerotate_kernel<__hip_bfloat16, 64>), grid, dim3(256), 0, stream, p);
@@ -206,7 +210,7 @@ hipError_t launch_rerotate(int dtype, int head_dim, const RerotateParams& p, hip
 
 hipError_t launch_append_rope(int dtype, int head_dim, const AppendParams& p, const RopeFreqs& f,
                               hipStream_t stream) {
-    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.hkv * (head_dim / 16);
+    const int64_t total = (int64_t)p.n_seqs * p.n_new * p.c.hkv * (head_dim / 16);
     if (total == 0) return hipSuccess;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;

@@ -18,7 +18,7 @@ bool desc_ok(const ps_cache_desc* d) {
     if (!d) return false;
     if (d->n_layers < 1 || d->max_seqs < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
     if (d->n_q_heads % d->n_kv_heads != 0) return false;
-    if (d->prefix_cap < 0 || d->window < 1) return false;
+    if (d->prefix_cap < 0 || d->window < 1 || d->prefix_blocks < 0) return false;
     return true;
 }
 
@@ -29,30 +29,54 @@ bool desc_supported(const ps_cache_desc* d) {
     return g == 1 || g == 2 || g == 4 || g == 8;
 }
 
+// Buffer layout: K prefix pools of every layer, K window pools, V prefix
+// pools, V window pools, then the decode workspace.
 struct Layout {
-    size_t elem, layer_bytes, kv_bytes, ws_o_bytes, ws_ml_bytes, ticket_bytes, total;
+    size_t elem, pre_layer_bytes, win_layer_bytes, pre_bytes, win_bytes, ws_o_bytes, ws_ml_bytes, ticket_bytes,
+        total;
     int64_t rows_per_head;
-    int32_t s_max;
+    int32_t prefix_blocks, s_max;
 };
 
 Layout layout_of(const ps_cache_desc* d) {
     Layout l{};
     l.elem = d->dtype == PS_BF16 ? 2 : 4;
     l.rows_per_head = (int64_t)d->prefix_cap + d->window;
-    l.layer_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * l.rows_per_head * d->head_dim * l.elem);
-    l.kv_bytes = l.layer_bytes * (size_t)d->n_layers;
+    l.prefix_blocks = d->prefix_blocks > 0 ? d->prefix_blocks : d->max_seqs;
+    l.pre_layer_bytes = align_up((size_t)l.prefix_blocks * d->n_kv_heads * d->prefix_cap * d->head_dim * l.elem);
+    l.win_layer_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * d->window * d->head_dim * l.elem);
+    l.pre_bytes = l.pre_layer_bytes * (size_t)d->n_layers;
+    l.win_bytes = l.win_layer_bytes * (size_t)d->n_layers;
     l.s_max = (int32_t)((l.rows_per_head + ps::kMinSplitRows - 1) / ps::kMinSplitRows);
     l.ws_o_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * d->head_dim * 4);
     l.ws_ml_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * 2 * 4);
     l.ticket_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * ps::kTicketStride * 4);
-    l.total = 2 * l.kv_bytes + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes;
+    l.total = 2 * (l.pre_bytes + l.win_bytes) + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes;
     return l;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? PS_OK : PS_ERR_HIP; }
 
+// Without prefix_rows a sequence's prefix block is its row, which needs one
+// prefix block per row.
 bool batch_ok(const ps_cache* c, const ps_seq_batch* b) {
-    return b && b->n >= 1 && b->n <= c->desc.max_seqs && b->rows && b->prefix_len && b->pos;
+    if (!b || b->n < 1 || b->n > c->desc.max_seqs || !b->rows || !b->prefix_len || !b->pos) return false;
+    return b->prefix_rows || c->prefix_blocks == c->desc.max_seqs;
+}
+
+ps::CacheLayer cache_layer(const ps_cache* c, int32_t layer, const ps_seq_batch* b) {
+    ps::CacheLayer v{};
+    v.kpre = c->k_pre + (size_t)layer * c->pre_layer_bytes;
+    v.vpre = c->v_pre + (size_t)layer * c->pre_layer_bytes;
+    v.kwin = c->k_win + (size_t)layer * c->win_layer_bytes;
+    v.vwin = c->v_win + (size_t)layer * c->win_layer_bytes;
+    v.hkv = c->desc.n_kv_heads;
+    v.pcap = c->desc.prefix_cap;
+    v.window = c->desc.window;
+    v.rows = b->rows;
+    v.prows = b->prefix_rows ? b->prefix_rows : b->rows;
+    v.v_off = c->v_pre - c->k_pre;  // == v_win - k_win (see ps_cache_create)
+    return v;
 }
 
 // Rows per decode split.  A decode launch is short (tens of MB at batch 1),
@@ -83,14 +107,9 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
     if (!isfinite(scale)) return PS_ERR_INVALID;
     ps::DecodeParams p{};
-    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
-    p.vc = c->v_region + (size_t)layer * c->layer_bytes;
+    p.c = cache_layer(c, layer, batch);
     p.hq = c->desc.n_q_heads;
-    p.hkv = c->desc.n_kv_heads;
-    p.pcap = c->desc.prefix_cap;
-    p.window = c->desc.window;
     p.rows_per_head = c->rows_per_head;
-    p.rows = batch->rows;
     p.plen = batch->prefix_len;
     p.pos = batch->pos;
     p.q = q;
@@ -136,12 +155,20 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
     c->bytes = bytes;
     c->elem_bytes = l.elem;
     c->rows_per_head = l.rows_per_head;
-    c->layer_bytes = l.layer_bytes;
-    c->k_region = c->base;
-    c->v_region = c->base + l.kv_bytes;
-    c->ws_o = reinterpret_cast<float*>(c->base + 2 * l.kv_bytes);
-    c->ws_ml = reinterpret_cast<float*>(c->base + 2 * l.kv_bytes + l.ws_o_bytes);
-    c->tickets = reinterpret_cast<uint32_t*>(c->base + 2 * l.kv_bytes + l.ws_o_bytes + l.ws_ml_bytes);
+    c->prefix_blocks = l.prefix_blocks;
+    c->pre_layer_bytes = l.pre_layer_bytes;
+    c->win_layer_bytes = l.win_layer_bytes;
+    // K pools, then V pools in the same order: a V slot lies at one fixed
+    // distance from its K slot in both pools, which lets a kernel address V
+    // from K with one add
+    c->k_pre = c->base;
+    c->k_win = c->k_pre + l.pre_bytes;
+    c->v_pre = c->k_win + l.win_bytes;
+    c->v_win = c->v_pre + l.pre_bytes;
+    char* ws = c->v_win + l.win_bytes;
+    c->ws_o = reinterpret_cast<float*>(ws);
+    c->ws_ml = reinterpret_cast<float*>(ws + l.ws_o_bytes);
+    c->tickets = reinterpret_cast<uint32_t*>(ws + l.ws_o_bytes + l.ws_ml_bytes);
     c->s_max = l.s_max;
     c->decode_rows = 0;
     const hipError_t e = ps::launch_fill_u32(c->tickets, (size_t)desc->max_seqs * desc->n_kv_heads * ps::kTicketStride, 0u,
@@ -159,10 +186,14 @@ int ps_cache_destroy(ps_cache* cache) {
     return PS_OK;
 }
 
-int ps_cache_kv(const ps_cache* c, int32_t layer, void** k, void** v) {
-    if (!c || !k || !v || layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
-    *k = c->k_region + (size_t)layer * c->layer_bytes;
-    *v = c->v_region + (size_t)layer * c->layer_bytes;
+int ps_cache_blocks(const ps_cache* c, int32_t layer, void** k_prefix, void** v_prefix, void** k_window,
+                    void** v_window) {
+    if (!c || !k_prefix || !v_prefix || !k_window || !v_window || layer < 0 || layer >= c->desc.n_layers)
+        return PS_ERR_INVALID;
+    *k_prefix = c->k_pre + (size_t)layer * c->pre_layer_bytes;
+    *v_prefix = c->v_pre + (size_t)layer * c->pre_layer_bytes;
+    *k_window = c->k_win + (size_t)layer * c->win_layer_bytes;
+    *v_window = c->v_win + (size_t)layer * c->win_layer_bytes;
     return PS_OK;
 }
 
@@ -180,13 +211,7 @@ int ps_kv_append_evict(ps_cache* c, int32_t layer, const ps_seq_batch* batch, in
     if (n_new == 0) return PS_OK;
     if (!k_new || !v_new) return PS_ERR_INVALID;
     ps::AppendParams p{};
-    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
-    p.vc = c->v_region + (size_t)layer * c->layer_bytes;
-    p.hkv = c->desc.n_kv_heads;
-    p.pcap = c->desc.prefix_cap;
-    p.window = c->desc.window;
-    p.rows_per_head = c->rows_per_head;
-    p.rows = batch->rows;
+    p.c = cache_layer(c, layer, batch);
     p.plen = batch->prefix_len;
     p.pos = batch->pos;
     p.n_seqs = batch->n;
@@ -204,13 +229,7 @@ int ps_kv_append_rope(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int
     if (n_new == 0) return PS_OK;
     if (!k_new || !v_new) return PS_ERR_INVALID;
     ps::AppendParams p{};
-    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
-    p.vc = c->v_region + (size_t)layer * c->layer_bytes;
-    p.hkv = c->desc.n_kv_heads;
-    p.pcap = c->desc.prefix_cap;
-    p.window = c->desc.window;
-    p.rows_per_head = c->rows_per_head;
-    p.rows = batch->rows;
+    p.c = cache_layer(c, layer, batch);
     p.plen = batch->prefix_len;
     p.pos = batch->pos;
     p.n_seqs = batch->n;
@@ -230,12 +249,7 @@ int ps_kv_rerotate(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int64_
     if (!isfinite(rope_base) || !(rope_base > 1.f)) return PS_ERR_INVALID;
     if (delta == 0) return PS_OK;
     ps::RerotateParams p{};
-    p.kc = c->k_region + (size_t)layer * c->layer_bytes;
-    p.hkv = c->desc.n_kv_heads;
-    p.pcap = c->desc.prefix_cap;
-    p.window = c->desc.window;
-    p.rows_per_head = c->rows_per_head;
-    p.rows = batch->rows;
+    p.c = cache_layer(c, layer, batch);
     p.plen = batch->prefix_len;
     p.pos = batch->pos;
     p.n_seqs = batch->n;
@@ -275,6 +289,7 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
             dtype != c->desc.dtype)
             return PS_ERR_INVALID;
         if (a->window != c->desc.window || a->prefix_len > c->desc.prefix_cap) return PS_ERR_INVALID;
+        if (!a->prefix_rows && c->prefix_blocks != c->desc.max_seqs) return PS_ERR_INVALID;
     }
     if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
     if (dtype != PS_BF16 && dtype != PS_F32) return PS_ERR_UNSUPPORTED;
@@ -288,30 +303,36 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     const int64_t P = a->prefix_len, W = a->window, S = a->start_pos, T = a->seq_len;
     int nr = 0;
     if (c) {
-        const char* kl = c->k_region + (size_t)a->layer * c->layer_bytes;
-        const char* vl = c->v_region + (size_t)a->layer * c->layer_bytes;
-        const int64_t rph = c->rows_per_head;
         const size_t el = c->elem_bytes;
-        auto cache_run = [&](int64_t first_row, int64_t pos0, int64_t n) {
+        const int64_t pcap = c->desc.prefix_cap, Wc = c->desc.window;
+        // run of n cache rows starting at block slot `first_slot` of a prefix
+        // block (block_rows = pcap) or of a window block (block_rows = W)
+        auto cache_run = [&](const char* kpool, const char* vpool, int64_t block_rows, const int32_t* blocks,
+                             int64_t first_slot, int64_t pos0, int64_t n) {
             ps::KeyRun& r = p.runs[nr++];
-            r.k = kl + (size_t)first_row * d * el;
-            r.v = vl + (size_t)first_row * d * el;
-            r.seq_stride = (int64_t)hkv * rph * d;
-            r.head_stride = rph * d;
+            r.k = kpool + (size_t)first_slot * d * el;
+            r.v = vpool + (size_t)first_slot * d * el;
+            r.seq_stride = (int64_t)hkv * block_rows * d;
+            r.head_stride = block_rows * d;
             r.row_stride = d;
             r.pos0 = pos0;
             r.n = n;
-            r.rows = a->rows;
+            r.rows = blocks;
         };
+        const char* kpre = c->k_pre + (size_t)a->layer * c->pre_layer_bytes;
+        const char* vpre = c->v_pre + (size_t)a->layer * c->pre_layer_bytes;
+        const char* kwin = c->k_win + (size_t)a->layer * c->win_layer_bytes;
+        const char* vwin = c->v_win + (size_t)a->layer * c->win_layer_bytes;
+        const int32_t* prows = a->prefix_rows ? a->prefix_rows : a->rows;
         const int64_t n_pre = S < P ? S : P;
-        if (n_pre > 0) cache_run(0, 0, n_pre);
+        if (n_pre > 0) cache_run(kpre, vpre, pcap, prows, 0, 0, n_pre);
         if (S > P) {
             const int64_t first = S - W > P ? S - W : P;  // oldest position the ring still holds
             const int64_t cnt = S - first;
             const int64_t slot = (first - P) % W;
             const int64_t n_a = slot + cnt <= W ? cnt : W - slot;
-            cache_run(c->desc.prefix_cap + slot, first, n_a);
-            if (n_a < cnt) cache_run(c->desc.prefix_cap, first + n_a, cnt - n_a);
+            cache_run(kwin, vwin, Wc, a->rows, slot, first, n_a);
+            if (n_a < cnt) cache_run(kwin, vwin, Wc, a->rows, 0, first + n_a, cnt - n_a);
         }
     }
     {

@@ -197,16 +197,16 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // group share blockIdx % 8 whenever the group count is a multiple of 8, so
     // the hardware's round-robin deal puts them on one XCD (one L2); measured
     // 3% faster at batch 1 than the (split, kv head, sequence) grid.
-    const int n_groups = p.n_seqs * p.hkv;
+    const int n_groups = p.n_seqs * p.c.hkv;
     const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
-    const int g = group % p.hkv, b = group / p.hkv;
+    const int g = group % p.c.hkv, b = group / p.c.hkv;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int sub = lane % LPR, rg = lane / LPR;
 
     // Metadata and queries first: independent loads, issued together.
     const int64_t P = p.plen[b];
     const int64_t i = p.pos[b];
-    const int64_t crow = p.rows[b];
+    const int64_t crow = p.c.rows[b], prow = p.c.prows[b];
     Vec16 qraw[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -214,22 +214,30 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 
     const int64_t n_pre = i + 1 < P ? i + 1 : P;
     int64_t n_ring = i - P + 1;
-    n_ring = n_ring < 0 ? 0 : (n_ring > p.window ? (int64_t)p.window : n_ring);
+    n_ring = n_ring < 0 ? 0 : (n_ring > p.c.window ? (int64_t)p.c.window : n_ring);
     const int64_t n = n_pre + n_ring;
     const int nsplit = (int)((n + R - 1) / R);
     if (split >= nsplit) return;
 
-    const int64_t head_off = (crow * p.hkv + g) * p.rows_per_head;
-    const T* kbase = reinterpret_cast<const T*>(p.kc) + head_off * D;
-    const T* vbase = reinterpret_cast<const T*>(p.vc) + head_off * D;
+    // Key row r of the sequence: r < n_pre is slot r of its prefix block,
+    // else slot r - n_pre of its window block.  The choice is one select of a
+    // base per row: r's byte offset goes on the prefix block's base or on the
+    // window block's base moved back by n_pre rows.  A V row lies v_off bytes
+    // after its K row in both pools.
+    constexpr int64_t kRowBytes = (int64_t)D * sizeof(T);
+    const int64_t pre_off = (prow * p.c.hkv + g) * p.c.pcap;
+    const int64_t win_off = (crow * p.c.hkv + g) * p.c.window;
+    const char* kpre_a = static_cast<const char*>(p.c.kpre) + pre_off * kRowBytes;
+    const char* kwin_a = static_cast<const char*>(p.c.kwin) + (win_off - n_pre) * kRowBytes;
+    const int64_t v_off = p.c.v_off;
     const bool fused = p.knew != nullptr;
-    int64_t new_phys = i;
+    int64_t new_r = i;  // key row of the new token
     if (fused && i >= P) {
         const int64_t off = i - P;
-        new_phys = p.pcap + (off < 0x7FFFFFFF ? (int64_t)((uint32_t)off % (uint32_t)p.window) : off % p.window);
+        new_r = n_pre + (off < 0x7FFFFFFF ? (int64_t)((uint32_t)off % (uint32_t)p.c.window) : off % p.c.window);
     }
-    const T* knew_row = fused ? reinterpret_cast<const T*>(p.knew) + ((int64_t)b * p.hkv + g) * D : nullptr;
-    const T* vnew_row = fused ? reinterpret_cast<const T*>(p.vnew) + ((int64_t)b * p.hkv + g) * D : nullptr;
+    const T* knew_row = fused ? reinterpret_cast<const T*>(p.knew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
+    const T* vnew_row = fused ? reinterpret_cast<const T*>(p.vnew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
 
     // Issue every K/V load of this lane's rows before any math.  Rows past
     // the end are clamped to the last valid row (a harmless in-bounds read,
@@ -242,10 +250,10 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         int64_t r = r0 + (int64_t)(wave * U + u) * RPW + rg;
         valid[u] = r < n;
         r = valid[u] ? r : n - 1;
-        const int64_t phys = r < n_pre ? r : p.pcap + (r - n_pre);
-        const bool is_new = fused && phys == new_phys;
-        const T* kp = is_new ? knew_row : kbase + phys * D;
-        const T* vp = is_new ? vnew_row : vbase + phys * D;
+        const bool is_new = fused && r == new_r;
+        const char* ka = (r < n_pre ? kpre_a : kwin_a) + r * kRowBytes;
+        const T* kp = is_new ? knew_row : reinterpret_cast<const T*>(ka);
+        const T* vp = is_new ? vnew_row : reinterpret_cast<const T*>(ka + v_off);
         kr[u] = load16_stream<NTL>(kp + sub * VEC);
         vr[u] = load16_stream<NTL>(vp + sub * VEC);
     }
@@ -268,8 +276,9 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // The split that owns the new token's slot also commits it to the cache
     // (after the loads above, so no wait on them is forced here).
     if (fused && split == 0 && tid < LPR) {
-        T* kd = const_cast<T*>(kbase) + new_phys * D + tid * VEC;
-        T* vd = const_cast<T*>(vbase) + new_phys * D + tid * VEC;
+        const char* ka = (new_r < n_pre ? kpre_a : kwin_a) + new_r * kRowBytes;
+        T* kd = const_cast<T*>(reinterpret_cast<const T*>(ka)) + tid * VEC;
+        T* vd = const_cast<T*>(reinterpret_cast<const T*>(ka + v_off)) + tid * VEC;
         *reinterpret_cast<Vec16*>(kd) = load16(knew_row + tid * VEC);
         *reinterpret_cast<Vec16*>(vd) = load16(vnew_row + tid * VEC);
     }
@@ -373,7 +382,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
-        uint32_t* t = p.tickets + ((int64_t)b * p.hkv + g) * kTicketStride;
+        uint32_t* t = p.tickets + ((int64_t)b * p.c.hkv + g) * kTicketStride;
         const uint32_t prev = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (prev == (uint32_t)(nsplit - 1));
         if (s_last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -461,7 +470,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 template <typename T, int D, int G, int NW, int U, bool NTL = false>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
     constexpr int R = NW * (64 / (D / Elem<T>::kPerVec)) * U;
-    const int64_t n_wg = ((p.rows_per_head + R - 1) / R) * (int64_t)p.hkv * p.n_seqs;
+    const int64_t n_wg = ((p.rows_per_head + R - 1) / R) * (int64_t)p.c.hkv * p.n_seqs;
     if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
     hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U, NTL>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();

@@ -13,10 +13,14 @@ struct ps_cache {
     char* base = nullptr;        // caller's device buffer
     size_t bytes = 0;
     size_t elem_bytes = 0;       // 2 (bf16) or 4 (f32)
-    int64_t rows_per_head = 0;   // prefix_cap + window
-    size_t layer_bytes = 0;      // bytes of one layer's K (or V) region
-    char* k_region = nullptr;    // [L][max_seqs][Hkv][Pcap+W][d]
-    char* v_region = nullptr;
+    int64_t rows_per_head = 0;   // prefix_cap + window: the most keys one sequence can hold
+    int32_t prefix_blocks = 0;   // prefix pool size (blocks)
+    size_t pre_layer_bytes = 0;  // bytes of one layer's K (or V) prefix pool
+    size_t win_layer_bytes = 0;  // bytes of one layer's K (or V) window pool
+    char* k_pre = nullptr;       // [L][prefix_blocks][Hkv][Pcap][d]
+    char* v_pre = nullptr;
+    char* k_win = nullptr;       // [L][max_seqs][Hkv][W][d]
+    char* v_win = nullptr;
     float* ws_o = nullptr;       // [max_seqs][Hq][s_max][d]  unnormalised partial outputs
     float* ws_ml = nullptr;      // [max_seqs][Hq][s_max][2]  (running max in log2 units, sum)
     uint32_t* tickets = nullptr; // [max_seqs][Hkv] arrival counters, one per 256-byte line (self-resetting)
@@ -28,6 +32,22 @@ namespace ps {
 
 constexpr int kMinSplitRows = 16;  // smallest rows-per-split the workspace is sized for
 constexpr int kTicketStride = 64;  // u32 words between arrival counters: one counter per 256-byte line
+
+// A layer of the cache as the kernels address it: prefix block b, kv head g
+// starts at kpre + (b * hkv + g) * pcap rows; window block r, kv head g at
+// kwin + (r * hkv + g) * window rows.
+struct CacheLayer {
+    void* kpre;
+    void* vpre;
+    void* kwin;
+    void* vwin;
+    int32_t hkv;
+    int32_t pcap, window;
+    const int32_t* rows;   // window block of each sequence of the batch
+    const int32_t* prows;  // prefix block of each sequence of the batch
+    int64_t v_off;         // bytes from a K slot to its V slot: vpre - kpre == vwin - kwin
+};
+
 
 // Visibility of key position j to query position i (prefix + window, causal).
 __host__ __device__ inline bool visible(int64_t i, int64_t j, int64_t P, int64_t W) {
@@ -54,12 +74,9 @@ __host__ __device__ inline int tile_class(int64_t i0, int64_t i1, int64_t j0, in
 
 // ------------------------------------------------------------ decode
 struct DecodeParams {
-    const void* kc;        // layer's K region
-    const void* vc;        // layer's V region
-    int32_t hq, hkv;
-    int32_t pcap, window;
-    int64_t rows_per_head; // pcap + window
-    const int32_t* rows;
+    CacheLayer c;
+    int32_t hq;
+    int64_t rows_per_head; // pcap + window: the most keys a sequence can hold
     const int32_t* plen;
     const int64_t* pos;
     const void* q;
@@ -87,12 +104,7 @@ bool decode_rows_valid(int dtype, int head_dim, int rows);
 
 // ------------------------------------------------------------ append
 struct AppendParams {
-    void* kc;
-    void* vc;
-    int32_t hkv;
-    int32_t pcap, window;
-    int64_t rows_per_head;
-    const int32_t* rows;
+    CacheLayer c;
     const int32_t* plen;
     const int64_t* pos;
     int32_t n_seqs, n_new;
@@ -109,11 +121,7 @@ hipError_t launch_append_rope(int dtype, int head_dim, const AppendParams& p, co
 
 // Reset-PE re-rotation of the window keys of a batch by delta positions.
 struct RerotateParams {
-    void* kc;              // layer's K region
-    int32_t hkv;
-    int32_t pcap, window;
-    int64_t rows_per_head;
-    const int32_t* rows;
+    CacheLayer c;          // only the window pool is touched
     const int32_t* plen;
     const int64_t* pos;    // window = tokens [max(P, pos - W), pos)
     int32_t n_seqs;

@@ -103,7 +103,7 @@ def test_calls_reject_null_handles_and_args():
     assert ps.lib.ps_decode_step(None, 0, ctypes.byref(b), None, None, None, None, None, 1.0, None) == \
         ps.PS_ERR_INVALID
     assert ps.lib.ps_prefill_attn(None, None) == ps.PS_ERR_INVALID
-    assert ps.lib.ps_cache_kv(None, 0, None, None) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_cache_blocks(None, 0, None, None, None, None) == ps.PS_ERR_INVALID
     assert ps.lib.ps_cache_set_decode_split(None, 0) == ps.PS_ERR_INVALID
     assert ps.lib.ps_cache_destroy(None) == ps.PS_OK
 

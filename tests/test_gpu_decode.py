@@ -22,18 +22,15 @@ def new_cache(n_layers, max_seqs, hq, hkv, d, pcap, W, dtype, poison=True):
     c = ps.Cache(n_layers, max_seqs, hq, hkv, d, pcap, W, dtype)
     if poison:
         # unwritten slots hold NaN: reading one would poison the output
-        for l in range(n_layers):
-            k, v = c.kv(l)
-            k.fill_(float("nan"))
-            v.fill_(float("nan"))
+        c.fill_(float("nan"))
     return c
 
 
 def check_cache_map(c, layer, row, P, W, last, seed, seq_id, hkv, d, base, dtype):
     """Bit-exact: every retained position sits in its slot."""
-    k, v = c.kv(layer)
-    kk = k[row].cpu()
-    vv = v[row].cpu()
+    k, v = c.seq_kv(layer, row)
+    kk = k.cpu()
+    vv = v.cpu()
     pos = oracle.retained_positions(last, P, W)
     ref_k = gen(seed, synth.K, layer, seq_id, pos, hkv, d, base, dtype)
     ref_v = gen(seed, synth.V, layer, seq_id, pos, hkv, d, base, dtype)
@@ -234,10 +231,8 @@ def test_chunk_append_equals_single_appends():
         for t in range(n):
             append_positions(ps, b, 0, 1, P, start + t, 1, seed, 0, hkv, d, base, DT_BF16)
         torch.cuda.synchronize()
-        ka, va = a.kv(0)
-        kb, vb = b.kv(0)
-        assert torch.equal(ka.view(torch.int16), kb.view(torch.int16))
-        assert torch.equal(va.view(torch.int16), vb.view(torch.int16))
+        for ta, tb in zip(a.blocks(0), b.blocks(0)):
+            assert torch.equal(ta.view(torch.int16), tb.view(torch.int16))
         check_cache_map(a, 0, 1, P, W, start + n - 1, seed, 0, hkv, d, base, DT_BF16)
 
 

@@ -88,10 +88,7 @@ def test_chunked_prefill_against_cache(dtype, hq, hkv, P, W, start, T, scale):
     seed, d, base = 12, 128, 1e4
     note(f"chunked prefill dt={dtype} P={P} W={W} start={start} T={T}")
     c = ps.Cache(2, 3, hq, hkv, d, max(P, 1), W, dtype)
-    for l in range(2):
-        kk, vv = c.kv(l)
-        kk.fill_(float("nan"))
-        vv.fill_(float("nan"))
+    c.fill_(float("nan"))
     layer, row = 1, 2
     if start > 0:
         fill_retained(ps, c, layer, row, P, W, start - 1, seed, 0, hkv, d, base, dtype, scale)
@@ -115,8 +112,8 @@ def test_chunked_prefill_against_cache(dtype, hq, hkv, P, W, start, T, scale):
                     torch.tensor([start], dtype=torch.int64, device="cuda"))
     ps.ps_kv_append_evict(c.handle, layer, b, T, kd[0], vd[0])
     torch.cuda.synchronize()
-    kc, _ = c.kv(layer)
-    kc = kc[row].cpu()
+    kc, _ = c.seq_kv(layer, row)
+    kc = kc.cpu()
     last = start + T - 1
     for p in oracle.retained_positions(last, P, W)[:: max(1, (P + W) // 97)]:
         kind, s = oracle.slot_of(int(p), P, W)

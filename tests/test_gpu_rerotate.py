@@ -31,28 +31,29 @@ def test_rerotate_window_keys(dtype, d, delta, base):
     # window entirely prefix-free, no window token yet
     seqs = [(0, 10, 300), (2, 16, 40), (3, 0, 130), (1, 5, 4)]
     cache = ps.Cache(1, 4, hq, hkv, d, pcap, W, dtype)
-    k_all, v_all = cache.kv(0)
-    k_all.zero_()
-    v_all.zero_()
+    cache.fill_(0.0)
+    kp, vp, k_all, v_all = cache.blocks(0)  # rotation touches window blocks only
     for i, (row, P, last) in enumerate(seqs):
         fill_retained(ps, cache, 0, row, P, W, last, 5, i, hkv, d, 1e4, dtype)
     torch.cuda.synchronize()
     k0 = k_all.clone()
     v0 = v_all.clone()
+    kp0, vp0 = kp.clone(), vp.clone()
     # rotate three of the four sequences (row 1 is left out of the batch)
     batch = [s for s in seqs if s[0] != 1]
     b = seq_batch(ps, [s[0] for s in batch], [s[1] for s in batch], [s[2] + 1 for s in batch])
     ps.ps_kv_rerotate(cache.handle, 0, b, delta, base)
     torch.cuda.synchronize()
     assert torch.equal(v_all, v0)
+    assert torch.equal(kp, kp0) and torch.equal(vp, vp0)
     k1 = k_all.clone()
     changed = torch.zeros(k_all.shape[:3], dtype=torch.bool, device="cuda")
     for row, P, last in batch:
         pos = last + 1
         lo = max(P, pos - W)
         for t in range(lo, pos):
-            changed[row, :, pcap + (t - P) % W] = True
-        slots = [pcap + (t - P) % W for t in range(lo, pos)]
+            changed[row, :, (t - P) % W] = True
+        slots = [(t - P) % W for t in range(lo, pos)]
         if not slots:
             continue
         before = dev_to_f32(k0[row][:, slots])          # [hkv][n][d]
@@ -101,9 +102,7 @@ def test_append_with_fused_rope(dtype, d, base):
     ca = ps.Cache(1, 4, hq, hkv, d, pcap, W, dtype)
     cb = ps.Cache(1, 4, hq, hkv, d, pcap, W, dtype)
     for c in (ca, cb):
-        k, v = c.kv(0)
-        k.zero_()
-        v.zero_()
+        c.fill_(0.0)
     for row, P, p0, n in seqs:
         pos = np.arange(p0, p0 + n)
         z = to_dev(gen(7, synth.K, 0, row, pos, hkv, d, 0.0, dtype))  # unrotated draws
@@ -112,9 +111,12 @@ def test_append_with_fused_rope(dtype, d, base):
         ps.ps_kv_append_rope(ca.handle, 0, bt, n, z, vv, base)
         ps.ps_kv_append_evict(cb.handle, 0, bt, n, z, vv)
     torch.cuda.synchronize()
-    ka, va = ca.kv(0)
-    kb, vb = cb.kv(0)
-    assert torch.equal(va, vb)
+    ka_p, va_p, ka_w, va_w = ca.blocks(0)
+    kb_p, vb_p, kb_w, vb_w = cb.blocks(0)
+    assert torch.equal(va_p, vb_p) and torch.equal(va_w, vb_w)
+    # one sequence's slots as [Hkv][prefix_cap + W][d], prefix block first
+    ka = torch.cat([ka_p, ka_w], dim=2)
+    kb = torch.cat([kb_p, kb_w], dim=2)
     for row, P, p0, n in seqs:
         last = p0 + n - 1
         slots, spos = [], []
