@@ -439,7 +439,10 @@ def prefill_bench(torch, ps, synth, np):
             ps.ps_prefill_attn(q, k, v, out, start_pos=start, prefix_len=Pc, window=Wc, scale=scale,
                                cache=cache.handle, layer=layer, rows=rows, stream=stream)
 
-    run()
+    # untimed warm-up: the MFMA-heavy kernels run slower for the first few
+    # milliseconds after the GPU was idle
+    for _ in range(3):
+        run()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     reps = 5
@@ -468,7 +471,8 @@ def prefill_bench(torch, ps, synth, np):
     v = torch.stack([bf16_dev(torch, synth.rows(0, synth.V, 0, b, pos, HKV, D)) for b in range(B)])
     out = torch.empty_like(q)
     run2 = lambda: ps.ps_prefill_attn(q, k, v, out, start_pos=0, prefix_len=Pt, window=Wt, scale=scale, stream=stream)
-    run2()
+    for _ in range(20):
+        run2()
     torch.cuda.synchronize()
     reps = 10
     e0.record(stream)
@@ -493,7 +497,8 @@ def prefill_bench(torch, ps, synth, np):
     delta = torch.empty(B, T, HQ, device="cuda")
     run3 = lambda: ps.ps_prefill_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, start_pos=0, prefix_len=Pt,
                                           window=Wt, scale=scale, stream=stream)
-    run3()
+    for _ in range(5):
+        run3()
     torch.cuda.synchronize()
     reps = 5
     e0.record(stream)

@@ -206,8 +206,13 @@ int ps_kv_rerotate(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, in
 /* Chunked prefill (cache != NULL) or trainer-side forward (cache == NULL).
  *
  * Every sequence of the batch has the same prefix length P and its chunk
- * occupies positions start_pos .. start_pos + seq_len - 1.  Query i of the
- * chunk attends to the visible keys among
+ * occupies positions start_pos .. start_pos + seq_len - 1, unless `starts` is
+ * given (ragged chunks of a continuous batch): then sequence b's chunk starts
+ * at starts[b] and its prefix length is prefix_lens[b] (or P when
+ * prefix_lens is NULL).  Device-side preconditions of ragged chunks (not
+ * checked): 0 <= starts[b], starts[b] + seq_len < 2^31, 0 <= prefix_lens[b]
+ * (<= prefix_cap in cache mode).  Query i of the chunk attends to the visible
+ * keys among
  *   - the cached prefix rows [0, min(P, start_pos))          (cache mode)
  *   - the cached ring rows holding positions
  *     [max(P, start_pos - W), start_pos)                      (cache mode)
@@ -247,6 +252,10 @@ typedef struct {
     const int32_t* prefix_rows; /* device [B] prefix blocks (cache mode), or NULL:
                                    prefix block = rows[b] (requires prefix_blocks
                                    == max_seqs) */
+    const int64_t* starts;      /* device [B] chunk start of each sequence (ragged
+                                   chunks), or NULL: start_pos for every sequence */
+    const int32_t* prefix_lens; /* device [B] prefix length of each sequence, or
+                                   NULL: prefix_len; only together with starts */
 } ps_prefill_args;
 
 /* Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,

@@ -53,7 +53,8 @@ class _PrefillArgs(ctypes.Structure):
                 ("prefix_len", ctypes.c_int64), ("window", ctypes.c_int64),
                 ("rows", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
-                ("scale", ctypes.c_float), ("prefix_rows", ctypes.c_void_p)]
+                ("scale", ctypes.c_float), ("prefix_rows", ctypes.c_void_p), ("starts", ctypes.c_void_p),
+                ("prefix_lens", ctypes.c_void_p)]
 
 
 class _PrefillBwdArgs(ctypes.Structure):
@@ -214,9 +215,13 @@ def ps_decode_step(handle: int, layer: int, batch: SeqBatch, q, k_new, v_new, ou
 
 def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: int, scale: float,
                     lse=None, cache: int | None = None, layer: int = 0, rows=None,
-                    prefix_rows=None, dtype: int | None = None, stream=None) -> None:
+                    prefix_rows=None, starts=None, prefix_lens=None, dtype: int | None = None,
+                    stream=None) -> None:
     """q/out [B][T][Hq][d], k/v [B][T][Hkv][d] CUDA tensors; ``cache`` None means
-    trainer mode (self-attention over the given tokens only)."""
+    trainer mode (self-attention over the given tokens only).  ``starts``
+    (int64 [B]) and ``prefix_lens`` (int32 [B]) give ragged chunks: per-sequence
+    start positions and prefix lengths (then ``start_pos``/``prefix_len`` are
+    not used for the sequences)."""
     B, T, hq, d = q.shape
     hkv = k.shape[2]
     if dtype is None:
@@ -224,7 +229,13 @@ def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: in
     a = _PrefillArgs(cache or 0, layer, B, T, hq, hkv, d, dtype, start_pos, prefix_len, window,
                      rows.data_ptr() if rows is not None else 0, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                      out.data_ptr(), lse.data_ptr() if lse is not None else 0, scale,
-                     prefix_rows.data_ptr() if prefix_rows is not None else 0)
+                     prefix_rows.data_ptr() if prefix_rows is not None else 0,
+                     starts.data_ptr() if starts is not None else 0,
+                     prefix_lens.data_ptr() if prefix_lens is not None else 0)
+    if starts is not None:
+        assert starts.dtype == torch.int64 and starts.numel() == B
+    if prefix_lens is not None:
+        assert prefix_lens.dtype == torch.int32 and prefix_lens.numel() == B
     _check(lib.ps_prefill_attn(ctypes.byref(a), _stream(stream)), "ps_prefill_attn")
 
 

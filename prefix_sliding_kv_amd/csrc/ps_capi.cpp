@@ -278,6 +278,7 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1)
         return PS_ERR_INVALID;
     if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
+    if (a->prefix_lens && !a->starts) return PS_ERR_INVALID;
     // positions are handled as 32-bit tile-relative offsets inside the kernel
     if (a->start_pos + (int64_t)a->seq_len >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
     int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim, dtype = a->dtype;
@@ -301,39 +302,24 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
 
     ps::PrefillParams p{};
     const int64_t P = a->prefix_len, W = a->window, S = a->start_pos, T = a->seq_len;
+    const bool ragged = a->starts != nullptr;
     int nr = 0;
     if (c) {
-        const size_t el = c->elem_bytes;
-        const int64_t pcap = c->desc.prefix_cap, Wc = c->desc.window;
-        // run of n cache rows starting at block slot `first_slot` of a prefix
-        // block (block_rows = pcap) or of a window block (block_rows = W)
-        auto cache_run = [&](const char* kpool, const char* vpool, int64_t block_rows, const int32_t* blocks,
-                             int64_t first_slot, int64_t pos0, int64_t n) {
-            ps::KeyRun& r = p.runs[nr++];
-            r.k = kpool + (size_t)first_slot * d * el;
-            r.v = vpool + (size_t)first_slot * d * el;
-            r.seq_stride = (int64_t)hkv * block_rows * d;
-            r.head_stride = block_rows * d;
-            r.row_stride = d;
-            r.pos0 = pos0;
-            r.n = n;
-            r.rows = blocks;
-        };
-        const char* kpre = c->k_pre + (size_t)a->layer * c->pre_layer_bytes;
-        const char* vpre = c->v_pre + (size_t)a->layer * c->pre_layer_bytes;
-        const char* kwin = c->k_win + (size_t)a->layer * c->win_layer_bytes;
-        const char* vwin = c->v_win + (size_t)a->layer * c->win_layer_bytes;
-        const int32_t* prows = a->prefix_rows ? a->prefix_rows : a->rows;
-        const int64_t n_pre = S < P ? S : P;
-        if (n_pre > 0) cache_run(kpre, vpre, pcap, prows, 0, 0, n_pre);
-        if (S > P) {
-            const int64_t first = S - W > P ? S - W : P;  // oldest position the ring still holds
-            const int64_t cnt = S - first;
-            const int64_t slot = (first - P) % W;
-            const int64_t n_a = slot + cnt <= W ? cnt : W - slot;
-            cache_run(kwin, vwin, Wc, a->rows, slot, first, n_a);
-            if (n_a < cnt) cache_run(kwin, vwin, Wc, a->rows, 0, first + n_a, cnt - n_a);
-        }
+        ps::PrefillCache& pc = p.cache;
+        pc.kpre = c->k_pre + (size_t)a->layer * c->pre_layer_bytes;
+        pc.vpre = c->v_pre + (size_t)a->layer * c->pre_layer_bytes;
+        pc.kwin = c->k_win + (size_t)a->layer * c->win_layer_bytes;
+        pc.vwin = c->v_win + (size_t)a->layer * c->win_layer_bytes;
+        pc.pcap = c->desc.prefix_cap;
+        pc.window = c->desc.window;
+        pc.hkv = hkv;
+        pc.head_dim = d;
+        pc.elem_bytes = (int32_t)c->elem_bytes;
+        pc.rows = a->rows;
+        pc.prows = a->prefix_rows ? a->prefix_rows : a->rows;
+        p.cache_mode = 1;
+        // uniform chunks: the cached runs are the same for every sequence
+        if (!ragged) nr = ps::cache_key_runs(pc, S, P, p.runs);
     }
     {
         ps::KeyRun& r = p.runs[nr++];
@@ -358,6 +344,8 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     p.out = a->out;
     p.lse = a->lse;
     p.scale_log2 = a->scale * kLog2e;
+    p.starts = a->starts;
+    p.plens = ragged ? a->prefix_lens : nullptr;
     return hip_status(ps::launch_prefill(dtype, d, group, p, (hipStream_t)stream));
 }
 

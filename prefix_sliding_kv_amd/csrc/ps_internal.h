@@ -147,6 +147,52 @@ struct KeyRun {
 
 constexpr int kMaxRuns = 4;
 
+// One layer's cache pools as a chunk reads them.
+struct PrefillCache {
+    const char* kpre;      // prefix pool: [prefix_blocks][hkv][pcap][d]
+    const char* vpre;
+    const char* kwin;      // window pool: [max_seqs][hkv][window][d]
+    const char* vwin;
+    int64_t pcap, window;
+    int32_t hkv, head_dim, elem_bytes;
+    const int32_t* rows;   // window block of each sequence
+    const int32_t* prows;  // prefix block of each sequence
+};
+
+__host__ __device__ inline void set_cache_run(KeyRun& r, const char* kpool, const char* vpool, int64_t block_rows,
+                                              const int32_t* blocks, const PrefillCache& c, int64_t first_slot,
+                                              int64_t pos0, int64_t n) {
+    const int64_t d = c.head_dim;
+    r.k = kpool + first_slot * d * c.elem_bytes;
+    r.v = vpool + first_slot * d * c.elem_bytes;
+    r.seq_stride = (int64_t)c.hkv * block_rows * d;
+    r.head_stride = block_rows * d;
+    r.row_stride = d;
+    r.pos0 = pos0;
+    r.n = n;
+    r.rows = blocks;
+}
+
+// Runs of the cached keys a chunk starting at position S (prefix length P)
+// reads: the prefix slots [0, min(S, P)), then the ring slots of positions
+// [max(P, S - W), S) as one or two runs (split where the ring wraps).
+// Returns the number of runs written (0 to 3).
+__host__ __device__ inline int cache_key_runs(const PrefillCache& c, int64_t S, int64_t P, KeyRun* runs) {
+    int nr = 0;
+    const int64_t W = c.window;
+    const int64_t n_pre = S < P ? S : P;
+    if (n_pre > 0) set_cache_run(runs[nr++], c.kpre, c.vpre, c.pcap, c.prows, c, 0, 0, n_pre);
+    if (S > P) {
+        const int64_t first = S - W > P ? S - W : P;  // oldest position the ring still holds
+        const int64_t cnt = S - first;
+        const int64_t slot = (first - P) % W;
+        const int64_t n_a = slot + cnt <= W ? cnt : W - slot;
+        set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, slot, first, n_a);
+        if (n_a < cnt) set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, 0, first + n_a, cnt - n_a);
+    }
+    return nr;
+}
+
 struct PrefillParams {
     KeyRun runs[kMaxRuns];
     int32_t n_runs;
@@ -156,7 +202,27 @@ struct PrefillParams {
     void* out;
     float* lse;
     float scale_log2;
+    // Ragged chunks: when `starts` is set, sequence b's chunk starts at
+    // starts[b] (its prefix length is plens[b], or P when plens is null);
+    // runs[0] is then the chunk run alone (its pos0 is replaced by starts[b])
+    // and, in cache mode, the cached runs come from cache_key_runs(cache).
+    const int64_t* starts;
+    const int32_t* plens;
+    int32_t cache_mode;
+    PrefillCache cache;
 };
+
+// Key runs of sequence b and its chunk start / prefix length.
+__device__ inline int seq_key_runs(const PrefillParams& p, int b, int64_t S, int64_t P, KeyRun* out) {
+    if (!p.starts) {
+        for (int r = 0; r < p.n_runs; ++r) out[r] = p.runs[r];
+        return p.n_runs;
+    }
+    const int nr = p.cache_mode ? cache_key_runs(p.cache, S, P, out) : 0;
+    out[nr] = p.runs[0];
+    out[nr].pos0 = S;
+    return nr + 1;
+}
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p,
                           hipStream_t stream);
 

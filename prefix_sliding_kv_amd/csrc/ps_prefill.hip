@@ -74,16 +74,17 @@ __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <int TILE>
-__device__ inline void plan_walk(const PrefillParams& p, int64_t i0, int64_t i1, TileWalk& w) {
+__device__ inline void plan_walk(const KeyRun* runs, int n_runs, int64_t P, int64_t W, int64_t i0, int64_t i1,
+                                 TileWalk& w) {
     w.n_ranges = 0;
-    for (int r = 0; r < p.n_runs; ++r) {
-        const KeyRun& run = p.runs[r];
+    for (int r = 0; r < n_runs; ++r) {
+        const KeyRun& run = runs[r];
         const int64_t n = run.n;
         if (n <= 0) continue;
         // prefix part: positions < min(P, i1 + 1)
-        const int64_t hiA = clamp64((p.P < i1 + 1 ? p.P : i1 + 1) - run.pos0, 0, n);
+        const int64_t hiA = clamp64((P < i1 + 1 ? P : i1 + 1) - run.pos0, 0, n);
         // window part: positions in [i0 - W + 1, i1]
-        const int64_t loB = clamp64(i0 - p.W + 1 - run.pos0, 0, n);
+        const int64_t loB = clamp64(i0 - W + 1 - run.pos0, 0, n);
         const int64_t hiB = clamp64(i1 + 1 - run.pos0, 0, n);
         const int endA = (int)((hiA + TILE - 1) / TILE);
         int begB = (int)(loB / TILE);
@@ -327,11 +328,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     // Positions are below 2^31 (the host rejects larger ones), so they are
     // handled in 32 bits; P and W are clamped to 2^31 - 1, which changes no
     // visibility decision for such positions.
+    // chunk start and prefix length of this sequence
+    const int64_t S = p.starts ? p.starts[b] : p.start_pos;
+    const int64_t Pb = p.plens ? (int64_t)p.plens[b] : p.P;
     const int t0 = qt * QP;                    // first chunk row of the tile
     const int t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
-    const int i0 = (int)p.start_pos + t0;
-    const int i1 = (int)p.start_pos + t_last;
-    const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
+    const int i0 = (int)S + t0;
+    const int i1 = (int)S + t_last;
+    const int P32 = Pb > 0x7FFFFFFF ? 0x7FFFFFFF : (int)Pb;
     const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
     const float c = p.scale_log2;                              // > 0 (checked on the host)
 
@@ -340,7 +344,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     const int head = g * G + qrow / QP;
     const int my_t = t0 + qrow % QP;
     const bool q_ok = my_t < p.seq_len;
-    const int my_i = (int)p.start_pos + my_t;
+    const int my_i = (int)S + my_t;
     Vec16 qreg[8];
     {
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
@@ -352,10 +356,12 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
 
     __shared__ TileWalk walk;
     __shared__ RunView views[kMaxRuns];
+    __shared__ KeyRun s_runs[kMaxRuns];
     if (tid == 0) {
-        plan_walk<kBNB>(p, (int64_t)i0, (int64_t)i1, walk);
-        for (int r = 0; r < p.n_runs; ++r) {
-            const KeyRun& run = p.runs[r];
+        const int n_runs = seq_key_runs(p, b, S, Pb, s_runs);
+        plan_walk<kBNB>(s_runs, n_runs, Pb, p.W, (int64_t)i0, (int64_t)i1, walk);
+        for (int r = 0; r < n_runs; ++r) {
+            const KeyRun& run = s_runs[r];
             const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
             const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride;
             views[r].k = static_cast<const char*>(run.k) + base_el * 2;
@@ -559,12 +565,14 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
     const int group = p.hq / p.hkv;
     const int g = head / group;
+    const int64_t S = p.starts ? p.starts[b] : p.start_pos;
+    const int64_t Pb = p.plens ? (int64_t)p.plens[b] : p.P;
     const int64_t t0 = (int64_t)qt * 64;
     const int64_t t_last = (t0 + 64 < p.seq_len ? t0 + 64 : p.seq_len) - 1;
-    const int64_t i0 = p.start_pos + t0, i1 = p.start_pos + t_last;
+    const int64_t i0 = S + t0, i1 = S + t_last;
     const int64_t my_t = t0 + tid;
     const bool q_ok = my_t < p.seq_len;
-    const int64_t my_i = p.start_pos + my_t;
+    const int64_t my_i = S + my_t;
 
     float q[D], o[D];
     const float* qp = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
@@ -574,10 +582,11 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     }
     float m_run = -INFINITY, l_run = 0.f;
 
-    if (tid == 0) plan_walk<kBN>(p, i0, i1, walk);
+    __shared__ KeyRun s_runs[kMaxRuns];
+    if (tid == 0) plan_walk<kBN>(s_runs, seq_key_runs(p, b, S, Pb, s_runs), Pb, p.W, i0, i1, walk);
     __syncthreads();
     for (int rr = 0; rr < walk.n_ranges; ++rr) {
-        const KeyRun& run = p.runs[walk.run[rr]];
+        const KeyRun& run = s_runs[walk.run[rr]];
         const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
         const float* kb = reinterpret_cast<const float*>(run.k) + seq * run.seq_stride + (int64_t)g * run.head_stride;
         const float* vb = reinterpret_cast<const float*>(run.v) + seq * run.seq_stride + (int64_t)g * run.head_stride;
@@ -585,7 +594,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
             const int64_t row0 = (int64_t)tile * kBN;
             const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
             const int64_t j0 = run.pos0 + row0;
-            const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j0 + nrows - 1, p.P, p.W);
+            const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j0 + nrows - 1, Pb, p.W);
             if (cls == kSkip) continue;
             for (int pass = 0; pass < 2; ++pass) {
                 float tmax = -INFINITY;
@@ -603,7 +612,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
                         const int64_t row = half * BR + r;
                         float acc = 0.f;
                         for (int e = 0; e < D; ++e) acc = fmaf(q[e], ks[r][e], acc);
-                        if (cls == kMasked && (row >= nrows || !visible(my_i, j0 + row, p.P, p.W))) acc = -INFINITY;
+                        if (cls == kMasked && (row >= nrows || !visible(my_i, j0 + row, Pb, p.W))) acc = -INFINITY;
                         if (pass == 0) {
                             tmax = fmaxf(tmax, acc);
                         } else {
@@ -810,7 +819,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
     __shared__ TileWalk walk;
     __shared__ RunView views[kMaxRuns];
     if (tid == 0) {
-        plan_walk<kBNB>(p, (int64_t)i0, (int64_t)i1, walk);
+        plan_walk<kBNB>(p.runs, p.n_runs, p.P, p.W, (int64_t)i0, (int64_t)i1, walk);
         for (int r = 0; r < p.n_runs; ++r) {
             const KeyRun& run = p.runs[r];
             const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;

@@ -88,3 +88,47 @@ def tol(dtype):
 
 def lse_tol(dtype):
     return 2e-3 if dtype == DT_BF16 else 1e-5
+
+
+# Sequences sharing a prefix block (rollouts of one prompt): positions < P
+# are drawn for the prompt (seq id PROMPT_BASE + prefix block), positions >= P
+# for the sequence itself (seq id = its row).
+PROMPT_BASE = 1000
+
+
+def shared_batch(ps, rows, prows, plen, pos):
+    dev = "cuda"
+    return ps.SeqBatch(torch.tensor(rows, dtype=torch.int32, device=dev),
+                       torch.tensor(plen, dtype=torch.int32, device=dev),
+                       torch.tensor(pos, dtype=torch.int64, device=dev),
+                       torch.tensor(prows, dtype=torch.int32, device=dev))
+
+
+def seq_rows(seed, tensor, layer, row, prow, positions, P, heads, d, base, dtype):
+    """Rows of a sequence: the prompt's draw below P, the sequence's own above."""
+    positions = np.asarray(positions, dtype=np.int64)
+    out = gen(seed, tensor, layer, row, positions, heads, d, base, dtype)
+    pre = positions < P
+    if pre.any():
+        out[pre] = gen(seed, tensor, layer, PROMPT_BASE + prow, positions[pre], heads, d, base, dtype)
+    return out
+
+
+def fill_shared(ps, c, layer, seqs, W, seed, hkv, d, base, dtype):
+    """seqs: (row, prefix block, P, last).  Prompt rows are appended once per
+    prefix block (through its first sequence), window rows per sequence."""
+    done = set()
+    for row, prow, P, last in seqs:
+        if prow not in done and P > 0:
+            pos = np.arange(0, P)
+            k = gen(seed, synth.K, layer, PROMPT_BASE + prow, pos, hkv, d, base, dtype)
+            v = gen(seed, synth.V, layer, PROMPT_BASE + prow, pos, hkv, d, base, dtype)
+            ps.ps_kv_append_evict(c.handle, layer, shared_batch(ps, [row], [prow], [P], [0]), P, to_dev(k), to_dev(v))
+            done.add(prow)
+        first = max(P, last - W + 1)
+        if last >= first:
+            pos = np.arange(first, last + 1)
+            k = gen(seed, synth.K, layer, row, pos, hkv, d, base, dtype)
+            v = gen(seed, synth.V, layer, row, pos, hkv, d, base, dtype)
+            ps.ps_kv_append_evict(c.handle, layer, shared_batch(ps, [row], [prow], [P], [first]), len(pos), to_dev(k),
+                                  to_dev(v))

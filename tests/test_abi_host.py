@@ -133,6 +133,7 @@ def test_prefill_validation():
     assert call(scale=0.0) == ps.PS_ERR_INVALID
     assert call(scale=-0.1) == ps.PS_ERR_INVALID
     assert call(start_pos=2**31 - 2, seq_len=4) == ps.PS_ERR_UNSUPPORTED  # positions are 32-bit in the kernel
+    assert call(prefix_lens=8) == ps.PS_ERR_INVALID            # per-sequence P only with per-sequence starts
 
 
 def _bwd_args(**kw):

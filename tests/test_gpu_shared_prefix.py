@@ -15,50 +15,11 @@ import torch
 
 import oracle
 import synth
-from gpu_harness import DT_BF16, DT_F32, as_f32, dev_to_f32, gen, lse_tol, note, to_dev, tol
+from gpu_harness import (DT_BF16, DT_F32, PROMPT_BASE, as_f32, dev_to_f32, gen, lse_tol, note, shared_batch,
+                         fill_shared, seq_rows, to_dev, tol)
 
 pytestmark = pytest.mark.gpu
 ps = pytest.importorskip("prefix_sliding_kv_amd")
-
-PROMPT_BASE = 1000  # seq ids of the prompts' draws; sequences use their row
-
-
-def batch(rows, prows, plen, pos):
-    dev = "cuda"
-    return ps.SeqBatch(torch.tensor(rows, dtype=torch.int32, device=dev),
-                       torch.tensor(plen, dtype=torch.int32, device=dev),
-                       torch.tensor(pos, dtype=torch.int64, device=dev),
-                       torch.tensor(prows, dtype=torch.int32, device=dev))
-
-
-def seq_rows(seed, tensor, layer, row, prow, positions, P, heads, d, base, dtype):
-    """Rows of a sequence: the prompt's draw below P, the sequence's own above."""
-    positions = np.asarray(positions, dtype=np.int64)
-    out = gen(seed, tensor, layer, row, positions, heads, d, base, dtype)
-    pre = positions < P
-    if pre.any():
-        out[pre] = gen(seed, tensor, layer, PROMPT_BASE + prow, positions[pre], heads, d, base, dtype)
-    return out
-
-
-def fill_shared(c, layer, seqs, W, seed, hkv, d, base, dtype):
-    """seqs: (row, prefix block, P, last).  Prompt rows are appended once per
-    prefix block (through its first sequence), window rows per sequence."""
-    done = set()
-    for row, prow, P, last in seqs:
-        if prow not in done and P > 0:
-            pos = np.arange(0, P)
-            k = gen(seed, synth.K, layer, PROMPT_BASE + prow, pos, hkv, d, base, dtype)
-            v = gen(seed, synth.V, layer, PROMPT_BASE + prow, pos, hkv, d, base, dtype)
-            ps.ps_kv_append_evict(c.handle, layer, batch([row], [prow], [P], [0]), P, to_dev(k), to_dev(v))
-            done.add(prow)
-        first = max(P, last - W + 1)
-        if last >= first:
-            pos = np.arange(first, last + 1)
-            k = gen(seed, synth.K, layer, row, pos, hkv, d, base, dtype)
-            v = gen(seed, synth.V, layer, row, pos, hkv, d, base, dtype)
-            ps.ps_kv_append_evict(c.handle, layer, batch([row], [prow], [P], [first]), len(pos), to_dev(k),
-                                  to_dev(v))
 
 
 def reference(seed, layer, row, prow, i, P, W, hq, hkv, d, base, dtype):
@@ -85,7 +46,7 @@ def test_decode_shared_prefix(dtype, d, fused):
     c.fill_(float("nan"))
     layer = 1
     # the cache as after positions 0..i-1 of each sequence
-    fill_shared(c, layer, [(r, pr, P, i - 1) for r, pr, P, i in seqs], W, seed, hkv, d, base, dtype)
+    fill_shared(ps, c, layer, [(r, pr, P, i - 1) for r, pr, P, i in seqs], W, seed, hkv, d, base, dtype)
     torch.cuda.synchronize()
     kp0, vp0 = [t.clone() for t in c.blocks(layer)[:2]]
     rows = [s[0] for s in seqs]
@@ -96,7 +57,7 @@ def test_decode_shared_prefix(dtype, d, fused):
     qd = to_dev(q)
     out = torch.empty(len(seqs), hq, d, device="cuda", dtype=qd.dtype)
     lse = torch.empty(len(seqs), hq, device="cuda")
-    b = batch(rows, prows, plen, pos)
+    b = shared_batch(ps, rows, prows, plen, pos)
     scale = 1.0 / math.sqrt(d)
     prefix_query = [s for s in seqs if s[3] < s[2]]
     assert not prefix_query  # a query inside the prefix would write the shared block
@@ -105,7 +66,7 @@ def test_decode_shared_prefix(dtype, d, fused):
         vn = to_dev(np.stack([gen(seed, synth.V, layer, r, [i], hkv, d, base, dtype)[0] for r, _, _, i in seqs]))
         ps.ps_decode_step(c.handle, layer, b, qd, kn, vn, out, lse, scale)
     else:
-        fill_shared(c, layer, [(r, pr, P, i) for r, pr, P, i in seqs], W, seed, hkv, d, base, dtype)
+        fill_shared(ps, c, layer, [(r, pr, P, i) for r, pr, P, i in seqs], W, seed, hkv, d, base, dtype)
         ps.ps_decode_attn(c.handle, layer, b, qd, out, lse, scale)
     torch.cuda.synchronize()
     got, got_lse = dev_to_f32(out), dev_to_f32(lse)
@@ -127,7 +88,7 @@ def test_append_slot_map_shared_prefix():
     seqs = [(0, 1, 24, 100), (1, 1, 24, 40), (2, 0, 11, 77), (3, 0, 11, 11)]
     c = ps.Cache(1, 5, hq, hkv, d, pcap, W, DT_BF16, prefix_blocks=2)
     c.fill_(0.0)
-    fill_shared(c, 0, seqs, W, seed, hkv, d, base, DT_BF16)
+    fill_shared(ps, c, 0, seqs, W, seed, hkv, d, base, DT_BF16)
     torch.cuda.synchronize()
     kp, vp, kw, vw = [t.cpu().view(torch.int16).numpy() for t in c.blocks(0)]
     for row, prow, P, last in seqs:
@@ -157,7 +118,7 @@ def test_chunked_prefill_shared_prefix(start, T):
     c = ps.Cache(1, 3, hq, hkv, d, 64, W, DT_BF16, prefix_blocks=1)
     c.fill_(float("nan"))
     seqs = [(2, 0, P, start - 1), (0, 0, P, start - 1)]
-    fill_shared(c, 0, seqs, W, seed, hkv, d, base, DT_BF16)
+    fill_shared(ps, c, 0, seqs, W, seed, hkv, d, base, DT_BF16)
     pos = np.arange(start, start + T)
     q = np.stack([gen(seed, synth.Q, 0, r, pos, hq, d, base, DT_BF16) for r, *_ in seqs])
     k = np.stack([seq_rows(seed, synth.K, 0, r, 0, pos, P, hkv, d, base, DT_BF16) for r, *_ in seqs])
@@ -195,14 +156,14 @@ def test_rollouts_of_one_prompt_qwen_shape():
     c = ps.Cache(1, n, hq, hkv, d, P, W, DT_BF16, prefix_blocks=1)
     c.fill_(float("nan"))
     seqs = [(r, 0, P, int(last[r]) - 1) for r in range(n)]
-    fill_shared(c, 0, seqs, W, seed, hkv, d, base, DT_BF16)
+    fill_shared(ps, c, 0, seqs, W, seed, hkv, d, base, DT_BF16)
     pos = [int(x) for x in last]
     q = to_dev(np.stack([gen(seed, synth.Q, 0, r, [pos[r]], hq, d, base, DT_BF16)[0] for r in range(n)]))
     kn = to_dev(np.stack([gen(seed, synth.K, 0, r, [pos[r]], hkv, d, base, DT_BF16)[0] for r in range(n)]))
     vn = to_dev(np.stack([gen(seed, synth.V, 0, r, [pos[r]], hkv, d, base, DT_BF16)[0] for r in range(n)]))
     out = torch.empty(n, hq, d, device="cuda", dtype=torch.bfloat16)
     lse = torch.empty(n, hq, device="cuda")
-    ps.ps_decode_step(c.handle, 0, batch(list(range(n)), [0] * n, [P] * n, pos), q, kn, vn, out, lse,
+    ps.ps_decode_step(c.handle, 0, shared_batch(ps, list(range(n)), [0] * n, [P] * n, pos), q, kn, vn, out, lse,
                       1.0 / math.sqrt(d))
     torch.cuda.synchronize()
     got, got_lse = dev_to_f32(out), dev_to_f32(lse)
