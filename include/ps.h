@@ -125,6 +125,35 @@ int ps_cache_destroy(ps_cache* cache);
 int ps_cache_blocks(const ps_cache* cache, int32_t layer, void** k_prefix, void** v_prefix,
                     void** k_window, void** v_window);
 
+/* Debug checks of the device-resident arguments (off by default).  While
+ * they are on, every call on the cache (append, decode, rerotate, cache-mode
+ * prefill) first runs a one-workgroup check kernel on the same stream, which
+ * ORs a bit per violated precondition into a flag word kept in the cache
+ * buffer; every kernel of the call, and of any later call, does nothing while
+ * the word is set, so a bad batch never touches the cache.  The word stays set
+ * until ps_cache_check_flags clears it.  Positions are followed per (layer,
+ * row): an append must start where the row's last append ended (or at 0,
+ * which starts a new sequence in the row), a decode query must sit at the
+ * last appended position (ps_decode_attn) or at the next one
+ * (ps_decode_step), and a cache-mode chunk must start at the next one. */
+enum ps_check_flag {
+    PS_CHECK_ROW = 1u << 0,            /* a window block (row) outside [0, max_seqs) */
+    PS_CHECK_DUPLICATE_ROW = 1u << 1,  /* two sequences of one call on the same row */
+    PS_CHECK_PREFIX_BLOCK = 1u << 2,   /* a prefix block outside [0, prefix_blocks) */
+    PS_CHECK_PREFIX_LEN = 1u << 3,     /* a prefix length outside [0, prefix_cap] */
+    PS_CHECK_POSITION = 1u << 4,       /* a negative position */
+    PS_CHECK_SEQUENCE = 1u << 5,       /* a position that does not continue its row */
+    PS_CHECK_SHARED_PREFIX = 1u << 6   /* one prefix block with two prefix lengths */
+};
+
+/* Turn the checks on (on != 0) or off.  Errors: PS_ERR_INVALID (NULL). */
+int ps_cache_set_checks(ps_cache* cache, int32_t on);
+
+/* Wait for `stream`, then return the flag word in *flags (host) and, if clear
+ * != 0, reset it to 0 (with a kernel on `stream`, waited for).  Errors:
+ * PS_ERR_INVALID (NULL), PS_ERR_HIP. */
+int ps_cache_check_flags(ps_cache* cache, uint32_t* flags, int32_t clear, void* stream);
+
 /* Split-K granularity of decode: rows (keys) handled per workgroup.  0 picks
  * automatically (default); otherwise one of 16, 32, 64, 128, 256, 512 for
  * bf16 head_dim 128 and fp32 head_dim 64 (32..1024 for bf16 head_dim 64,

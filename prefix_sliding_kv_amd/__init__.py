@@ -17,12 +17,15 @@ import torch
 __all__ = [
     "PS_BF16", "PS_F32", "PSError", "CacheDesc", "Cache", "lib",
     "ps_cache_bytes", "ps_cache_create", "ps_cache_destroy", "ps_cache_blocks",
-    "ps_cache_set_decode_split", "ps_kv_append_evict", "ps_decode_attn", "ps_decode_step",
+    "ps_cache_set_decode_split", "ps_cache_set_checks", "ps_cache_check_flags", "ps_kv_append_evict", "ps_decode_attn", "ps_decode_step",
     "ps_prefill_attn", "ps_tile_class", "ps_status_str", "ps_version", "SeqBatch",
 ]
 
 PS_OK, PS_ERR_INVALID, PS_ERR_UNSUPPORTED, PS_ERR_CAPACITY, PS_ERR_HIP = range(5)
 PS_BF16, PS_F32 = 0, 1
+# bits of the debug-check flag word (ps_check_flag)
+(PS_CHECK_ROW, PS_CHECK_DUPLICATE_ROW, PS_CHECK_PREFIX_BLOCK, PS_CHECK_PREFIX_LEN, PS_CHECK_POSITION,
+ PS_CHECK_SEQUENCE, PS_CHECK_SHARED_PREFIX) = (1 << i for i in range(7))
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprefix_sliding.so")
@@ -76,6 +79,8 @@ _SIGS = {
     "ps_cache_blocks": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                        ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
     "ps_cache_set_decode_split": (ctypes.c_int, [_vp, _i32]),
+    "ps_cache_set_checks": (ctypes.c_int, [_vp, _i32]),
+    "ps_cache_check_flags": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_uint32), _i32, _vp]),
     "ps_kv_append_evict": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, _vp]),
     "ps_kv_append_rope": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, ctypes.c_float,
                                          _vp]),
@@ -160,6 +165,18 @@ def ps_cache_blocks(handle: int, layer: int):
 def ps_cache_set_decode_split(handle: int, rows_per_split: int) -> None:
     _check(lib.ps_cache_set_decode_split(ctypes.c_void_p(handle), rows_per_split),
            "ps_cache_set_decode_split")
+
+
+def ps_cache_set_checks(handle: int, on: bool) -> None:
+    _check(lib.ps_cache_set_checks(ctypes.c_void_p(handle), int(bool(on))), "ps_cache_set_checks")
+
+
+def ps_cache_check_flags(handle: int, clear: bool = False, stream=None) -> int:
+    """Waits for the stream; returns the debug-check flag word (PS_CHECK_* bits)."""
+    f = ctypes.c_uint32()
+    _check(lib.ps_cache_check_flags(ctypes.c_void_p(handle), ctypes.byref(f), int(bool(clear)), _stream(stream)),
+           "ps_cache_check_flags")
+    return f.value
 
 
 class SeqBatch:

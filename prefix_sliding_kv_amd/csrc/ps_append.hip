@@ -24,6 +24,7 @@ struct alignas(16) Vec16 {
 };
 
 __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_per_row) {
+    if (p.c.guard && *p.c.guard) return;
     const int64_t total = (int64_t)p.n_seqs * p.n_new * p.c.hkv * pieces_per_row;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     const int64_t row_bytes = (int64_t)pieces_per_row * 16;
@@ -67,6 +68,7 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_
 // and the same bytes of V); slots as in append_kernel.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) append_rope_kernel(AppendParams p, RopeFreqs f) {
+    if (p.c.guard && *p.c.guard) return;
     constexpr int LPR = D / 16;
     const int64_t total = (int64_t)p.n_seqs * p.n_new * p.c.hkv * LPR;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -132,6 +134,7 @@ __global__ void __launch_bounds__(256) append_rope_kernel(AppendParams p, RopeFr
 // row is read and written once; V rows and prefix rows are not touched.
 template <typename T, int D>
 __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
+    if (p.c.guard && *p.c.guard) return;
     constexpr int LPR = D / 16;          // lanes per row (each: 8 pairs)
     constexpr int RPW = 256 / LPR;       // rows per workgroup pass
     const int j = threadIdx.x % LPR;
@@ -167,6 +170,45 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
     }
 }
 
+// One workgroup checks every sequence of a call (pairs of sequences for the
+// duplicate-row and shared-prefix rules), then, if no check anywhere has
+// failed, moves the rows' next positions past an append.
+__global__ void __launch_bounds__(256) check_kernel(CheckParams p) {
+    for (int b = threadIdx.x; b < p.n; b += blockDim.x) {
+        const int32_t row = p.rows[b];
+        const int32_t pr = p.prows ? p.prows[b] : row;
+        const int64_t P = p.plen ? (int64_t)p.plen[b] : p.plen_scalar;
+        const int64_t pos = p.pos ? p.pos[b] : p.pos_scalar;
+        uint32_t f = 0;
+        const bool row_ok = row >= 0 && row < p.max_seqs;
+        if (!row_ok) f |= PS_CHECK_ROW;
+        if (pr < 0 || pr >= p.prefix_blocks) f |= PS_CHECK_PREFIX_BLOCK;
+        if (P < 0 || P > p.pcap) f |= PS_CHECK_PREFIX_LEN;
+        if (pos < 0) f |= PS_CHECK_POSITION;
+        for (int o = 0; o < b; ++o) {
+            const int32_t orow = p.rows[o];
+            if (orow == row) f |= PS_CHECK_DUPLICATE_ROW;
+            const int32_t opr = p.prows ? p.prows[o] : orow;
+            const int64_t oP = p.plen ? (int64_t)p.plen[o] : p.plen_scalar;
+            if (opr == pr && oP != P) f |= PS_CHECK_SHARED_PREFIX;
+        }
+        if (row_ok && p.mode != kCheckNone) {
+            const int64_t nx = p.next_pos[row];
+            const int64_t want = p.mode == kCheckQuery ? nx - 1 : nx;
+            // position 0 starts a new sequence in the row
+            if (nx >= 0 && pos != 0 && pos != want) f |= PS_CHECK_SEQUENCE;
+        }
+        if (f) atomicOr(p.flags, f);
+    }
+    __syncthreads();
+    if (p.mode != kCheckAppend) return;
+    if (__hip_atomic_load(p.flags, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return;
+    for (int b = threadIdx.x; b < p.n; b += blockDim.x) {
+        const int64_t pos = p.pos ? p.pos[b] : p.pos_scalar;
+        p.next_pos[p.rows[b]] = pos + p.n_new;
+    }
+}
+
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t value) {
     for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
         p[i] = value;
@@ -182,6 +224,11 @@ hipError_t launch_append(int dtype, int head_dim, const AppendParams& p, hipStre
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p, pieces);
+    return hipGetLastError();
+}
+
+hipError_t launch_check(const CheckParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(check_kernel, dim3(1), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

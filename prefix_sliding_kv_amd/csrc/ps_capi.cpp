@@ -33,7 +33,7 @@ bool desc_supported(const ps_cache_desc* d) {
 // pools, V window pools, then the decode workspace.
 struct Layout {
     size_t elem, pre_layer_bytes, win_layer_bytes, pre_bytes, win_bytes, ws_o_bytes, ws_ml_bytes, ticket_bytes,
-        total;
+        flag_bytes, next_pos_bytes, total;
     int64_t rows_per_head;
     int32_t prefix_blocks, s_max;
 };
@@ -51,7 +51,10 @@ Layout layout_of(const ps_cache_desc* d) {
     l.ws_o_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * d->head_dim * 4);
     l.ws_ml_bytes = align_up((size_t)d->max_seqs * d->n_q_heads * l.s_max * 2 * 4);
     l.ticket_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * ps::kTicketStride * 4);
-    l.total = 2 * (l.pre_bytes + l.win_bytes) + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes;
+    l.flag_bytes = kAlign;
+    l.next_pos_bytes = align_up((size_t)d->n_layers * d->max_seqs * 8);
+    l.total = 2 * (l.pre_bytes + l.win_bytes) + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes + l.flag_bytes +
+              l.next_pos_bytes;
     return l;
 }
 
@@ -76,7 +79,35 @@ ps::CacheLayer cache_layer(const ps_cache* c, int32_t layer, const ps_seq_batch*
     v.rows = b->rows;
     v.prows = b->prefix_rows ? b->prefix_rows : b->rows;
     v.v_off = c->v_pre - c->k_pre;  // == v_win - k_win (see ps_cache_create)
+    v.guard = c->checks ? c->check_flags : nullptr;
     return v;
+}
+
+// Debug checks of a call's per-sequence arguments, enqueued before its kernels.
+int run_checks(const ps_cache* c, int32_t layer, const int32_t* rows, const int32_t* prows, const int32_t* plen,
+               const int64_t* pos, int64_t plen_scalar, int64_t pos_scalar, int32_t n, int32_t n_new, int32_t mode,
+               void* stream) {
+    ps::CheckParams p{};
+    p.rows = rows;
+    p.prows = prows;
+    p.plen = plen;
+    p.pos = pos;
+    p.plen_scalar = plen_scalar;
+    p.pos_scalar = pos_scalar;
+    p.n = n;
+    p.n_new = n_new;
+    p.mode = mode;
+    p.max_seqs = c->desc.max_seqs;
+    p.prefix_blocks = c->prefix_blocks;
+    p.pcap = c->desc.prefix_cap;
+    p.next_pos = c->next_pos + (size_t)layer * c->desc.max_seqs;
+    p.flags = c->check_flags;
+    return hip_status(ps::launch_check(p, (hipStream_t)stream));
+}
+
+int batch_checks(const ps_cache* c, int32_t layer, const ps_seq_batch* b, int32_t n_new, int32_t mode, void* stream) {
+    if (!c->checks) return PS_OK;
+    return run_checks(c, layer, b->rows, b->prefix_rows, b->prefix_len, b->pos, 0, 0, b->n, n_new, mode, stream);
 }
 
 // Rows per decode split.  A decode launch is short (tens of MB at batch 1),
@@ -123,6 +154,8 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     p.tickets = c->tickets;
     p.s_max = c->s_max;
     p.n_seqs = batch->n;
+    const int st = batch_checks(c, layer, batch, knew ? 1 : 0, knew ? ps::kCheckAppend : ps::kCheckQuery, stream);
+    if (st != PS_OK) return st;
     const int rows = c->decode_rows > 0 ? c->decode_rows : auto_decode_rows(c, batch->n);
     const int group = c->desc.n_q_heads / c->desc.n_kv_heads;
     // several workgroups per CU: the kernel marks its K/V loads non-temporal
@@ -169,10 +202,17 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
     c->ws_o = reinterpret_cast<float*>(ws);
     c->ws_ml = reinterpret_cast<float*>(ws + l.ws_o_bytes);
     c->tickets = reinterpret_cast<uint32_t*>(ws + l.ws_o_bytes + l.ws_ml_bytes);
+    c->check_flags = reinterpret_cast<uint32_t*>(ws + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes);
+    c->next_pos = reinterpret_cast<int64_t*>(ws + l.ws_o_bytes + l.ws_ml_bytes + l.ticket_bytes + l.flag_bytes);
     c->s_max = l.s_max;
     c->decode_rows = 0;
-    const hipError_t e = ps::launch_fill_u32(c->tickets, (size_t)desc->max_seqs * desc->n_kv_heads * ps::kTicketStride, 0u,
-                                             (hipStream_t)stream);
+    c->checks = 0;
+    hipError_t e = ps::launch_fill_u32(c->tickets, (size_t)desc->max_seqs * desc->n_kv_heads * ps::kTicketStride, 0u,
+                                       (hipStream_t)stream);
+    if (e == hipSuccess) e = ps::launch_fill_u32(c->check_flags, kAlign / 4, 0u, (hipStream_t)stream);
+    if (e == hipSuccess)  // -1 in every next position: nothing appended yet
+        e = ps::launch_fill_u32(reinterpret_cast<uint32_t*>(c->next_pos), (size_t)desc->n_layers * desc->max_seqs * 2,
+                                0xFFFFFFFFu, (hipStream_t)stream);
     if (e != hipSuccess) {
         delete c;
         return PS_ERR_HIP;
@@ -197,6 +237,21 @@ int ps_cache_blocks(const ps_cache* c, int32_t layer, void** k_prefix, void** v_
     return PS_OK;
 }
 
+int ps_cache_set_checks(ps_cache* c, int32_t on) {
+    if (!c) return PS_ERR_INVALID;
+    c->checks = on != 0;
+    return PS_OK;
+}
+
+int ps_cache_check_flags(ps_cache* c, uint32_t* flags, int32_t clear, void* stream) {
+    if (!c || !flags) return PS_ERR_INVALID;
+    hipStream_t s = (hipStream_t)stream;
+    if (hipMemcpyAsync(flags, c->check_flags, sizeof(uint32_t), hipMemcpyDeviceToHost, s) != hipSuccess)
+        return PS_ERR_HIP;
+    if (clear && ps::launch_fill_u32(c->check_flags, 1, 0u, s) != hipSuccess) return PS_ERR_HIP;
+    return hip_status(hipStreamSynchronize(s));
+}
+
 int ps_cache_set_decode_split(ps_cache* c, int32_t rows_per_split) {
     if (!c || rows_per_split < 0) return PS_ERR_INVALID;
     if (rows_per_split != 0 && !decode_rows_ok(c, rows_per_split)) return PS_ERR_UNSUPPORTED;
@@ -210,6 +265,8 @@ int ps_kv_append_evict(ps_cache* c, int32_t layer, const ps_seq_batch* batch, in
     if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
     if (n_new == 0) return PS_OK;
     if (!k_new || !v_new) return PS_ERR_INVALID;
+    const int st = batch_checks(c, layer, batch, n_new, ps::kCheckAppend, stream);
+    if (st != PS_OK) return st;
     ps::AppendParams p{};
     p.c = cache_layer(c, layer, batch);
     p.plen = batch->prefix_len;
@@ -228,6 +285,8 @@ int ps_kv_append_rope(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int
     if (!isfinite(rope_base) || !(rope_base > 1.f)) return PS_ERR_INVALID;
     if (n_new == 0) return PS_OK;
     if (!k_new || !v_new) return PS_ERR_INVALID;
+    const int st = batch_checks(c, layer, batch, n_new, ps::kCheckAppend, stream);
+    if (st != PS_OK) return st;
     ps::AppendParams p{};
     p.c = cache_layer(c, layer, batch);
     p.plen = batch->prefix_len;
@@ -248,6 +307,8 @@ int ps_kv_rerotate(ps_cache* c, int32_t layer, const ps_seq_batch* batch, int64_
     if (layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
     if (!isfinite(rope_base) || !(rope_base > 1.f)) return PS_ERR_INVALID;
     if (delta == 0) return PS_OK;
+    const int st = batch_checks(c, layer, batch, 0, ps::kCheckNext, stream);
+    if (st != PS_OK) return st;
     ps::RerotateParams p{};
     p.c = cache_layer(c, layer, batch);
     p.plen = batch->prefix_len;
@@ -320,6 +381,12 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
         p.cache_mode = 1;
         // uniform chunks: the cached runs are the same for every sequence
         if (!ragged) nr = ps::cache_key_runs(pc, S, P, p.runs);
+        if (c->checks) {
+            const int st = run_checks(c, a->layer, a->rows, a->prefix_rows, ragged ? a->prefix_lens : nullptr,
+                                      a->starts, P, S, a->batch, 0, ps::kCheckNext, stream);
+            if (st != PS_OK) return st;
+            p.guard = c->check_flags;
+        }
     }
     {
         ps::KeyRun& r = p.runs[nr++];

@@ -197,6 +197,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // group share blockIdx % 8 whenever the group count is a multiple of 8, so
     // the hardware's round-robin deal puts them on one XCD (one L2); measured
     // 3% faster at batch 1 than the (split, kv head, sequence) grid.
+    if (p.c.guard && *p.c.guard) return;  // checks on and a check failed
     const int n_groups = p.n_seqs * p.c.hkv;
     const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
     const int g = group % p.c.hkv, b = group / p.c.hkv;

@@ -26,6 +26,9 @@ struct ps_cache {
     uint32_t* tickets = nullptr; // [max_seqs][Hkv] arrival counters, one per 256-byte line (self-resetting)
     int32_t s_max = 0;           // split slots per (seq, q head) in the workspace
     int32_t decode_rows = 0;     // requested rows per split, 0 = automatic
+    uint32_t* check_flags = nullptr;  // debug checks: sticky violation bits (own 256-byte line)
+    int64_t* next_pos = nullptr;      // debug checks: [L][max_seqs] next position of each row, -1 unknown
+    int32_t checks = 0;               // debug checks on
 };
 
 namespace ps {
@@ -46,7 +49,31 @@ struct CacheLayer {
     const int32_t* rows;   // window block of each sequence of the batch
     const int32_t* prows;  // prefix block of each sequence of the batch
     int64_t v_off;         // bytes from a K slot to its V slot: vpre - kpre == vwin - kwin
+    const uint32_t* guard; // checks on: the cache's flag word; a kernel does nothing while it is set
 };
+
+// Device-side checks of a call's per-sequence arguments (debug mode of a
+// cache).  One workgroup: every violation is OR-ed into *flags (bits of
+// ps_check_flag); when the word is still clear afterwards, an appending call
+// advances next_pos[row] to the position after its last token.
+enum CheckMode : int32_t {
+    kCheckNone = 0,     // ranges only
+    kCheckAppend = 1,   // pos = the row's next position; the call appends n_new tokens
+    kCheckNext = 2,     // pos = the row's next position; nothing appended
+    kCheckQuery = 3     // pos = the row's last appended position
+};
+struct CheckParams {
+    const int32_t* rows;
+    const int32_t* prows;  // or null: rows
+    const int32_t* plen;   // or null: plen_scalar
+    const int64_t* pos;    // or null: pos_scalar
+    int64_t plen_scalar, pos_scalar;
+    int32_t n, n_new, mode;
+    int32_t max_seqs, prefix_blocks, pcap;
+    int64_t* next_pos;     // [max_seqs] of the layer; -1 = nothing appended yet
+    uint32_t* flags;
+};
+hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 
 
 // Visibility of key position j to query position i (prefix + window, causal).
@@ -210,6 +237,7 @@ struct PrefillParams {
     const int32_t* plens;
     int32_t cache_mode;
     PrefillCache cache;
+    const uint32_t* guard;  // checks on: the cache's flag word; the kernel does nothing while it is set
 };
 
 // Key runs of sequence b and its chunk start / prefix length.

@@ -313,6 +313,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     constexpr int D = 128;
     constexpr int QP = 32 * kWaves / G;  // positions per query tile
     extern __shared__ __attribute__((aligned(16))) char smem[];
+    if (p.guard && *p.guard) return;  // checks on and a check failed
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -561,6 +562,7 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     __shared__ float ks[BR][D];
     __shared__ float vs[BR][D];
     __shared__ TileWalk walk;
+    if (p.guard && *p.guard) return;  // checks on and a check failed
     const int tid = threadIdx.x;
     const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
     const int group = p.hq / p.hkv;

@@ -105,6 +105,8 @@ def test_calls_reject_null_handles_and_args():
     assert ps.lib.ps_prefill_attn(None, None) == ps.PS_ERR_INVALID
     assert ps.lib.ps_cache_blocks(None, 0, None, None, None, None) == ps.PS_ERR_INVALID
     assert ps.lib.ps_cache_set_decode_split(None, 0) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_cache_set_checks(None, 1) == ps.PS_ERR_INVALID
+    assert ps.lib.ps_cache_check_flags(None, None, 0, None) == ps.PS_ERR_INVALID
     assert ps.lib.ps_cache_destroy(None) == ps.PS_OK
 
 
