@@ -219,6 +219,37 @@ def test_decode_edge_cases(P, W, L, hq, hkv, d, dtype, split):
     c.close()
 
 
+@pytest.mark.parametrize("fused", [False, True])
+def test_decode_at_positions_beyond_2_31(fused):
+    """Traces past 2^31 tokens: the slot of position p is (p - P) mod W in
+    64-bit arithmetic.  Queries at 2^31 + 5 (ring slot arithmetic just past
+    the 32-bit range), 2^33 + 77 and 2^40 + 3, each over a cache holding the
+    prefix and the last W - 1 tokens."""
+    seed, P, W, hq, hkv, d, base = 6, 20, 64, 4, 2, 128, 1e4
+    scale = 1.0 / math.sqrt(d)
+    for i in (2**31 + 5, 2**33 + 77, 2**40 + 3):
+        note(f"decode beyond 2^31 i={i} fused={fused}")
+        c = new_cache(1, 2, hq, hkv, d, P, W, DT_BF16)
+        fill_retained(ps, c, 0, 1, P, W, i - 1, seed, 3, hkv, d, base, DT_BF16)
+        q = to_dev(gen(seed, synth.Q, 0, 3, [i], hq, d, base, DT_BF16))
+        k = to_dev(gen(seed, synth.K, 0, 3, [i], hkv, d, base, DT_BF16))
+        v = to_dev(gen(seed, synth.V, 0, 3, [i], hkv, d, base, DT_BF16))
+        out = torch.empty(1, hq, d, device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty(1, hq, device="cuda")
+        b = seq_batch(ps, [1], [P], [i])
+        if fused:
+            ps.ps_decode_step(c.handle, 0, b, q, k, v, out, lse, scale)
+        else:
+            ps.ps_kv_append_evict(c.handle, 0, b, 1, k, v)
+            ps.ps_decode_attn(c.handle, 0, b, q, out, lse, scale)
+        torch.cuda.synchronize()
+        ref, ref_lse = decode_reference(seed, 0, 3, i, P, W, hq, hkv, d, base, DT_BF16)
+        assert np.max(np.abs(dev_to_f32(out)[0] - ref)) <= tol(DT_BF16), i
+        np.testing.assert_allclose(dev_to_f32(lse)[0], ref_lse, rtol=0, atol=lse_tol(DT_BF16))
+        check_cache_map(c, 0, 1, P, W, i, seed, 3, hkv, d, base, DT_BF16)
+        c.close()
+
+
 def test_chunk_append_equals_single_appends():
     """A chunk longer than W (plus prefix tokens) in one call leaves the same
     bytes as appending its tokens one by one."""
