@@ -23,6 +23,11 @@ Printed as one JSON line (rank 0, N=1):
                token each per layer: tok/s and achieved HBM GB/s
   rollouts_decode 64 rollouts of one prompt (P=1024) with the prompt in one
                shared prefix block, and with private copies
+  hbm_copy     measured device-to-device copy bandwidth (read + write) and the
+               decode rates as fractions of it (the decode only reads, so it
+               can exceed a copy)
+  cpu_baseline also one thread on the decode sample, the host CPU, and the
+               oracle's TFLOP/s on sampled rows of the two prefill workloads
 """
 from __future__ import annotations
 
@@ -536,10 +541,71 @@ def decode_traffic():
     return int(round(fetch + write))
 
 
+def copy_bandwidth(torch, src, dst):
+    """Measured HBM bandwidth: a device-to-device copy, read + write bytes per second."""
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * src.numel() / (e0.elapsed_time(e1) / reps * 1e-3) / 1e9
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def timed(fn, seconds):
+    """Runs fn until `seconds` elapse (at least once); returns (calls, elapsed)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            return n, time.perf_counter() - t0
+
+
+def cpu_prefill_sample(np, oracle, synth, threads, seconds):
+    """The oracle on sampled query rows of the two prefill workloads: a
+    chunked-prefill layer (P=1024, W=8192, queries in 98304..102399) and the
+    trainer forward (P=256, W=2048, T=8192); exact visible-pair flops of the
+    sampled rows per second."""
+    res = {}
+    for name, Pp, Wp, lo, hi, kpos in (
+            ("chunked", 1024, 8192, 98304, 102400,
+             np.concatenate([np.arange(0, 1024), np.arange(98304 - 8192, 102400)])),
+            ("trainer", 256, 2048, 0, 8192, np.arange(0, 8192))):
+        qpos = np.linspace(lo, hi - 1, 16).astype(np.int64)
+        q = synth.bf16_bits_to_f32(synth.rows(0, synth.Q, 0, 0, qpos, HQ, D, 1e6))
+        k = synth.bf16_bits_to_f32(synth.rows(0, synth.K, 0, 0, kpos, HKV, D, 1e6))
+        v = synth.bf16_bits_to_f32(synth.rows(0, synth.V, 0, 0, kpos, HKV, D))
+        flops = sum(4 * D * HQ * int(oracle.visible_count(int(i), Pp, Wp)) for i in qpos)
+        n, dt = timed(lambda: oracle.attention(q, qpos, k, v, kpos, Pp, Wp, 1.0 / math.sqrt(D), threads=threads),
+                      seconds)
+        res[name] = {"tflops": round(flops * n / dt / 1e12, 5),
+                     "sample": f"16 query positions spread over {lo}..{hi - 1}, all {HQ} heads, "
+                               f"{len(kpos)} candidate keys; run {n} times ({dt:.1f} s)"}
+    return res
+
+
 def cpu_baseline(np, seconds):
     """The CPU oracle on a bounded sample: one decode token of the same
     workload on `n_layers` layers, repeated until `seconds` elapse; scaled to
-    tok/s for all 28 layers."""
+    tok/s for all 28 layers.  Also one thread on the same sample, and the
+    oracle's rate on sampled rows of the two prefill workloads."""
     import oracle
     import synth
     threads = max(1, min(16, os.cpu_count() or 1))
@@ -562,9 +628,15 @@ def cpu_baseline(np, seconds):
             break
     dt = time.perf_counter() - t0
     per_layer = dt / (reps * n_layers)
+    q, k, v = data[0]
+    n1, dt1 = timed(lambda: oracle.attention(q, [i], k, v, kpos, P, W, 1.0 / math.sqrt(D), threads=1),
+                    max(1.0, seconds / 5))
     return {"value": round(1.0 / (per_layer * LAYERS), 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
             "sample": f"one decode token at position {i} (P=100, W=4096, Hq=16, Hkv=8, d=128) on {n_layers} "
-                      f"layers, oracle run {reps} times ({dt:.1f} s); tok/s scaled to 28 layers"}
+                      f"layers, oracle run {reps} times ({dt:.1f} s); tok/s scaled to 28 layers",
+            "single_thread_tok_s": round(1.0 / (dt1 / n1 * LAYERS), 3),
+            "host": {"cpu_model": cpu_model(), "nproc": os.cpu_count()},
+            "prefill": cpu_prefill_sample(np, oracle, synth, threads, max(1.0, seconds / 3))}
 
 
 def main():
@@ -587,6 +659,7 @@ def main():
     calib_dst = torch.empty_like(calib_src)
     calib_dst.copy_(calib_src)
     torch.cuda.synchronize()
+    copy_gbs = copy_bandwidth(torch, calib_src, calib_dst)
     del calib_src, calib_dst
     dec = decode_bench(args, torch, ps, synth, np)
     bytes_per_launch = 2 * HKV * D * (P + W) * 2
@@ -629,6 +702,11 @@ def main():
         "baselines": base_cmp,
         "batched_decode": batched,
         "rollouts_decode": rollouts,
+        "hbm_copy": {"gbs": round(copy_gbs, 1),
+                     "note": "device-to-device copy of 256 MiB, read + write bytes / time",
+                     "decode_frac_of_copy": round(achieved / copy_gbs, 4),
+                     "batched_decode_frac_of_copy": (round(batched["achieved_gbs"] / copy_gbs, 4)
+                                                     if batched else None)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
