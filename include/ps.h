@@ -172,15 +172,17 @@ int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
  *   k_new, v_new: device [n][n_new][n_kv_heads][head_dim], pre-rotated keys.
  * Preconditions: positions of a sequence are appended in increasing order and
  * a decode/prefill query at position i sees the cache as left by appending
- * every position < i (Continue PE: nothing is ever re-encoded).
+ * every position < i (Continue PE: nothing is ever re-encoded); the debug
+ * checks (ps_cache_set_checks) verify them on the device.
  * Errors: PS_ERR_INVALID, PS_ERR_HIP. */
 int ps_kv_append_evict(ps_cache* cache, int32_t layer, const ps_seq_batch* batch,
                        int32_t n_new, const void* k_new, const void* v_new, void* stream);
 
 /* One decode query per sequence at position i = pos[b], which must already be
  * appended: GQA attention over the visible keys of i, which are exactly the
- * retained cache rows (prefix rows [0, min(P, i+1)) and ring rows of positions
- * (i - W, i]).  Query head h reads kv head floor(h * Hkv / Hq).
+ * retained slots (prefix-block slots [0, min(P, i+1)) and the window-block
+ * slots of positions (i - W, i]).  Query head h reads kv head
+ * floor(h * Hkv / Hq).
  *   q:   device [n][n_q_heads][head_dim]
  *   out: device [n][n_q_heads][head_dim]  (cache dtype; normalised output)
  *   lse: device [n][n_q_heads] float, natural-log log-sum-exp of the scaled
