@@ -254,7 +254,7 @@ __device__ inline int seq_key_runs(const PrefillParams& p, int b, int64_t S, int
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p,
                           hipStream_t stream);
 
-// Trainer-side backward (bf16, head_dim 128): Delta, dQ, then dK/dV on one stream.
+// Trainer-side backward (bf16, head_dim 128): Delta, dK/dV, then dQ on one stream.
 struct BwdParams {
     PrefillParams f;       // trainer-mode walk: one key run (the chunk); f.q = Q, f.out = forward O
     const void* dout;      // [B][T][Hq][d]

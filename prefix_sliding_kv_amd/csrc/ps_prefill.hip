@@ -1275,15 +1275,18 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
         if (e != hipSuccess) return e;
         lds_set[gi] = true;
     }
+    // dK/dV first: its prefix blocks are the longest workgroups of the two
+    // launches (measured 1.3% faster than dQ first; running the two on two
+    // streams gained nothing)
     switch (group) {
-        case 1: hipLaunchKernelGGL(bwd_dq_kernel<1>, grid_q, dim3(kThreads), lds_q, stream, p);
-                hipLaunchKernelGGL(bwd_dkdv_kernel<1>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
-        case 2: hipLaunchKernelGGL(bwd_dq_kernel<2>, grid_q, dim3(kThreads), lds_q, stream, p);
-                hipLaunchKernelGGL(bwd_dkdv_kernel<2>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
-        case 4: hipLaunchKernelGGL(bwd_dq_kernel<4>, grid_q, dim3(kThreads), lds_q, stream, p);
-                hipLaunchKernelGGL(bwd_dkdv_kernel<4>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
-        case 8: hipLaunchKernelGGL(bwd_dq_kernel<8>, grid_q, dim3(kThreads), lds_q, stream, p);
-                hipLaunchKernelGGL(bwd_dkdv_kernel<8>, grid_k, dim3(kThreads), kDkdvLds, stream, p); break;
+        case 1: hipLaunchKernelGGL(bwd_dkdv_kernel<1>, grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                hipLaunchKernelGGL(bwd_dq_kernel<1>, grid_q, dim3(kThreads), lds_q, stream, p); break;
+        case 2: hipLaunchKernelGGL(bwd_dkdv_kernel<2>, grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                hipLaunchKernelGGL(bwd_dq_kernel<2>, grid_q, dim3(kThreads), lds_q, stream, p); break;
+        case 4: hipLaunchKernelGGL(bwd_dkdv_kernel<4>, grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                hipLaunchKernelGGL(bwd_dq_kernel<4>, grid_q, dim3(kThreads), lds_q, stream, p); break;
+        case 8: hipLaunchKernelGGL(bwd_dkdv_kernel<8>, grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                hipLaunchKernelGGL(bwd_dq_kernel<8>, grid_q, dim3(kThreads), lds_q, stream, p); break;
     }
     return hipGetLastError();
 }
