@@ -176,3 +176,48 @@ def test_rerotate_rejects_null_cache_before_any_launch():
 def test_append_rope_rejects_null_cache_before_any_launch():
     b = ps._SeqBatch(1, None, None, None)
     assert ps.lib.ps_kv_append_rope(None, 0, ctypes.byref(b), 1, None, None, 1e4, None) == ps.PS_ERR_INVALID
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "ps.h"
+
+int main(void) {
+    ps_cache_desc d;
+    memset(&d, 0, sizeof d);
+    d.n_layers = 28; d.max_seqs = 1; d.n_q_heads = 16; d.n_kv_heads = 8; d.head_dim = 128;
+    d.prefix_cap = 100; d.window = 4096; d.dtype = PS_BF16; d.prefix_blocks = 0;
+    size_t bytes = ps_cache_bytes(&d);
+    ps_cache* c = NULL;
+    int st = ps_cache_create(&d, NULL, bytes, NULL, &c);
+    printf("%s|%zu|%d|%s|%d\n", ps_version(), bytes, st, ps_status_str(st),
+           ps_tile_class(100, 227, 0, 63, 100, 4096));
+    return st == PS_ERR_INVALID && c == NULL ? 0 : 1;
+}
+"""
+
+
+@pytest.mark.parametrize("compiler,std", [("gcc", "-std=c99"), ("g++", "-std=c++17")])
+def test_header_is_plain_c_and_links(tmp_path, compiler, std):
+    """ps.h compiles as strict C99 (and as C++) with no warnings, and a
+    program linked against the library runs its host-only calls."""
+    import shutil
+    import subprocess
+    if shutil.which(compiler) is None:
+        pytest.skip(f"{compiler} not available")
+    src = tmp_path / ("prog.c" if compiler == "gcc" else "prog.cpp")
+    src.write_text(C_PROGRAM)
+    exe = tmp_path / "prog"
+    pkg = os.path.dirname(ps.LIB_PATH)
+    cmd = [compiler, std, "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+           str(src), "-o", str(exe), "-L", pkg, "-lprefix_sliding", f"-Wl,-rpath,{pkg}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stdout + r.stderr
+    version, nbytes, status, text, cls = r.stdout.strip().split("|")
+    assert version == ps.ps_version()
+    assert int(nbytes) == ps.ps_cache_bytes(ps.CacheDesc(28, 1, 16, 8, 128, 100, 4096, ps.PS_BF16, 0))
+    assert int(status) == ps.PS_ERR_INVALID and text == ps.ps_status_str(ps.PS_ERR_INVALID)
+    assert int(cls) == ps.ps_tile_class(100, 227, 0, 63, 100, 4096)
