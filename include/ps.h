@@ -289,10 +289,14 @@ typedef struct {
                                    NULL: prefix_len; only together with starts */
 } ps_prefill_args;
 
-/* Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,
- * scale <= 0 or not finite), PS_ERR_UNSUPPORTED (head_dim other than 128 for
- * bf16, GQA group other than 1, 2, 4 or 8 for bf16, a chunk reaching position
- * 2^31), PS_ERR_HIP. */
+/* bf16 with head_dim 128 and GQA group 1, 2, 4 or 8 runs on the MFMA kernel;
+ * every other supported shape (bf16 head_dim 64, other GQA groups, fp32) runs
+ * on a plain kernel with fp32 arithmetic: same results within the dtype's
+ * tolerance, far slower.
+ * Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,
+ * scale <= 0 or not finite), PS_ERR_UNSUPPORTED (head_dim other than 64 or
+ * 128, a dtype other than bf16 / fp32, a chunk reaching position 2^31),
+ * PS_ERR_HIP. */
 
 int ps_prefill_attn(const ps_prefill_args* args, void* stream);
 

@@ -357,7 +357,6 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     if (dtype != PS_BF16 && dtype != PS_F32) return PS_ERR_UNSUPPORTED;
     if (d != 64 && d != 128) return PS_ERR_UNSUPPORTED;
     const int group = hq / hkv;
-    if (dtype == PS_BF16 && (d != 128 || (group != 1 && group != 2 && group != 4 && group != 8))) return PS_ERR_UNSUPPORTED;
     if (a->seq_len == 0) return PS_OK;
     if (!a->q || !a->k || !a->v || !a->out) return PS_ERR_INVALID;
 

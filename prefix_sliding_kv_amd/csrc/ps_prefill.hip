@@ -24,8 +24,10 @@
 // before its MFMAs.  K and V tiles go from global memory straight into two
 // LDS stages (buffer_load ... lds), the next tile loading while the current
 // one is computed, one barrier per tile.  The tile walk is kept in scalar
-// registers and touches LDS only at range boundaries.  fp32 path: a plain
-// debug kernel with 64-key tiles, the same walk and classification.
+// registers and touches LDS only at range boundaries.  Plain path: one
+// thread per query row with 64-key tiles, the same walk and classification,
+// fp32 arithmetic; it serves fp32 inputs and the bf16 shapes the MFMA kernel
+// is not built for (head_dim 64, GQA groups other than 1, 2, 4, 8).
 #include "ps_internal.h"
 
 namespace ps {
@@ -33,7 +35,7 @@ namespace {
 
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2eF = 1.4426950408889634f;
-constexpr int kBN = 64;  // keys per tile of the fp32 debug kernel
+constexpr int kBN = 64;  // keys per tile of the plain kernel
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -553,11 +555,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run * c + log2f(l_tot)) * kLn2;
 }
 
-// ----------------------------------------------------------------- fp32 debug
+// ----------------------------------------------------------------- plain path
 // One thread per query row of a 64-position tile of one q head; K/V tiles in
-// LDS; two passes per tile (scores for the tile maximum, then the weighted sum).
-template <int D>
-__global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
+// LDS as fp32; two passes per tile (scores for the tile maximum, then the
+// weighted sum).  T is the storage type: float, or uint16_t holding bf16 bits
+// (widened exactly; the output rounded to nearest even).
+__device__ inline float to_f32(float x) { return x; }
+__device__ inline float to_f32(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+__device__ inline void store_as(float* p, float v) { *p = v; }
+__device__ inline void store_as(uint16_t* p, float v) {
+    const __bf16 b = (__bf16)v;
+    __builtin_memcpy(p, &b, 2);
+}
+
+template <typename T, int D>
+__global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
     constexpr int BR = 32;  // rows staged per LDS fill (two fills per 64-key tile)
     __shared__ float ks[BR][D];
     __shared__ float vs[BR][D];
@@ -577,9 +589,9 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     const int64_t my_i = S + my_t;
 
     float q[D], o[D];
-    const float* qp = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
+    const T* qp = reinterpret_cast<const T*>(p.q) + (((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head) * D;
     for (int e = 0; e < D; ++e) {
-        q[e] = q_ok ? qp[e] * p.scale_log2 : 0.f;
+        q[e] = q_ok ? to_f32(qp[e]) * p.scale_log2 : 0.f;
         o[e] = 0.f;
     }
     float m_run = -INFINITY, l_run = 0.f;
@@ -590,8 +602,8 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
     for (int rr = 0; rr < walk.n_ranges; ++rr) {
         const KeyRun& run = s_runs[walk.run[rr]];
         const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
-        const float* kb = reinterpret_cast<const float*>(run.k) + seq * run.seq_stride + (int64_t)g * run.head_stride;
-        const float* vb = reinterpret_cast<const float*>(run.v) + seq * run.seq_stride + (int64_t)g * run.head_stride;
+        const T* kb = reinterpret_cast<const T*>(run.k) + seq * run.seq_stride + (int64_t)g * run.head_stride;
+        const T* vb = reinterpret_cast<const T*>(run.v) + seq * run.seq_stride + (int64_t)g * run.head_stride;
         for (int tile = walk.begin[rr]; tile < walk.end[rr]; ++tile) {
             const int64_t row0 = (int64_t)tile * kBN;
             const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
@@ -606,8 +618,8 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
                         const int r = idx / D, e = idx % D;
                         const int64_t row = half * BR + r;
                         const bool ok = row < nrows;
-                        ks[r][e] = ok ? kb[(row0 + row) * run.row_stride + e] : 0.f;
-                        vs[r][e] = ok ? vb[(row0 + row) * run.row_stride + e] : 0.f;
+                        ks[r][e] = ok ? to_f32(kb[(row0 + row) * run.row_stride + e]) : 0.f;
+                        vs[r][e] = ok ? to_f32(vb[(row0 + row) * run.row_stride + e]) : 0.f;
                     }
                     __syncthreads();
                     for (int r = 0; r < BR; ++r) {
@@ -635,8 +647,8 @@ __global__ void __launch_bounds__(64) prefill_f32_kernel(PrefillParams p) {
         }
     }
     if (!q_ok) return;
-    float* op = reinterpret_cast<float*>(p.out) + (((int64_t)b * p.seq_len + my_t) * p.hq + head) * D;
-    for (int e = 0; e < D; ++e) op[e] = o[e] / l_run;
+    T* op = reinterpret_cast<T*>(p.out) + (((int64_t)b * p.seq_len + my_t) * p.hq + head) * D;
+    for (int e = 0; e < D; ++e) store_as(op + e, o[e] / l_run);
     if (p.lse) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run + log2f(l_run)) * kLn2;
 }
 
@@ -1203,8 +1215,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p, hipStream_t stream) {
     if (p.seq_len == 0) return hipSuccess;
-    if (dtype == PS_BF16) {
-        if (head_dim != 128) return hipErrorInvalidValue;
+    if (dtype == PS_BF16 && head_dim == 128 && (group == 1 || group == 2 || group == 4 || group == 8)) {
         const int qp = 32 * kWaves / group;
         dim3 grid((unsigned)(((p.seq_len + qp - 1) / qp) * p.hkv * p.batch));
         const size_t lds = (size_t)kStages * kStageBytes;
@@ -1233,10 +1244,14 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
         return hipGetLastError();
     }
     dim3 grid((unsigned)((p.seq_len + 63) / 64), (unsigned)p.hq, (unsigned)p.batch);
-    if (head_dim == 64)
-        hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, stream, p);
+    if (dtype == PS_BF16 && head_dim == 64)
+        hipLaunchKernelGGL((prefill_plain_kernel<uint16_t, 64>), grid, dim3(64), 0, stream, p);
+    else if (dtype == PS_BF16 && head_dim == 128)
+        hipLaunchKernelGGL((prefill_plain_kernel<uint16_t, 128>), grid, dim3(64), 0, stream, p);
+    else if (head_dim == 64)
+        hipLaunchKernelGGL((prefill_plain_kernel<float, 64>), grid, dim3(64), 0, stream, p);
     else if (head_dim == 128)
-        hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, stream, p);
+        hipLaunchKernelGGL((prefill_plain_kernel<float, 128>), grid, dim3(64), 0, stream, p);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

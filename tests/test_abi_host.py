@@ -127,9 +127,9 @@ def test_prefill_validation():
     assert call(batch=0) == ps.PS_ERR_INVALID
     assert call(n_kv_heads=3) == ps.PS_ERR_INVALID
     assert call(head_dim=96) == ps.PS_ERR_UNSUPPORTED
-    assert call(head_dim=64) == ps.PS_ERR_UNSUPPORTED          # bf16 MFMA path is d=128 only
+    assert call(head_dim=64) == ps.PS_OK                       # bf16 d=64: the plain kernel (empty chunk)
     assert call(dtype=5) == ps.PS_ERR_UNSUPPORTED
-    assert call(n_q_heads=128, n_kv_heads=8) == ps.PS_ERR_UNSUPPORTED  # GQA group 16 on the MFMA path
+    assert call(n_q_heads=128, n_kv_heads=8) == ps.PS_OK       # GQA group 16: the plain kernel
     assert call(seq_len=4) == ps.PS_ERR_INVALID                # null tensors
     assert call(scale=float("nan")) == ps.PS_ERR_INVALID
     assert call(scale=0.0) == ps.PS_ERR_INVALID

@@ -60,6 +60,9 @@ def run_trainer(q, k, v, P, W, start, dtype, with_lse=True):
     (DT_BF16, 128, 2, 1, 1, 190, 3, 1, 3.0),    # W=1: prefix + self
     (DT_BF16, 128, 2, 1, 1, 64, 100, 8, 1.0),   # exactly one tile, all prefix
     (DT_BF16, 128, 2, 1, 1, 1, 0, 5, 1.0),      # single token
+    (DT_BF16, 64, 4, 2, 2, 300, 20, 70, 3.0),   # bf16 d=64: plain kernel
+    (DT_BF16, 128, 6, 2, 1, 200, 9, 50, 3.0),   # GQA 3: plain kernel
+    (DT_BF16, 64, 16, 1, 1, 130, 5, 40, 1.0),   # GQA 16, d=64: plain kernel
 ])
 def test_trainer_forward_small(dtype, d, hq, hkv, B, T, P, W, scale):
     seed, base = 11, 1e4
@@ -73,20 +76,21 @@ def test_trainer_forward_small(dtype, d, hq, hkv, B, T, P, W, scale):
         np.testing.assert_allclose(got_lse[b], ref_lse, rtol=0, atol=lse_tol(dtype) * (1 + scale * scale))
 
 
-@pytest.mark.parametrize("dtype,hq,hkv,P,W,start,T,scale", [
-    (DT_BF16, 4, 2, 30, 200, 1000, 300, 3.0),   # ring wrapped, window reaches into the ring
-    (DT_BF16, 4, 2, 30, 200, 130, 100, 3.0),    # ring not full yet
-    (DT_BF16, 4, 2, 300, 64, 100, 400, 3.0),    # chunk straddles the prefix end
-    (DT_BF16, 16, 8, 64, 512, 5000, 700, 1.0),  # Qwen head shape
-    (DT_F32, 4, 2, 30, 200, 1000, 300, 1.0),
-    (DT_F32, 4, 2, 300, 64, 100, 400, 1.0),
+@pytest.mark.parametrize("dtype,d,hq,hkv,P,W,start,T,scale", [
+    (DT_BF16, 128, 4, 2, 30, 200, 1000, 300, 3.0),   # ring wrapped, window reaches into the ring
+    (DT_BF16, 128, 4, 2, 30, 200, 130, 100, 3.0),    # ring not full yet
+    (DT_BF16, 128, 4, 2, 300, 64, 100, 400, 3.0),    # chunk straddles the prefix end
+    (DT_BF16, 128, 16, 8, 64, 512, 5000, 700, 1.0),  # Qwen head shape
+    (DT_BF16, 64, 4, 2, 30, 200, 1000, 300, 3.0),    # bf16 d=64 cache: plain kernel
+    (DT_F32, 128, 4, 2, 30, 200, 1000, 300, 1.0),
+    (DT_F32, 128, 4, 2, 300, 64, 100, 400, 1.0),
 ])
-def test_chunked_prefill_against_cache(dtype, hq, hkv, P, W, start, T, scale):
+def test_chunked_prefill_against_cache(dtype, d, hq, hkv, P, W, start, T, scale):
     """Chunk queries at positions start..start+T-1 attend to the cached prefix
     and ring (left by positions < start) and to the chunk itself; afterwards
     the chunk is committed and the cache map checked."""
-    seed, d, base = 12, 128, 1e4
-    note(f"chunked prefill dt={dtype} P={P} W={W} start={start} T={T}")
+    seed, base = 12, 1e4
+    note(f"chunked prefill dt={dtype} d={d} P={P} W={W} start={start} T={T}")
     c = ps.Cache(2, 3, hq, hkv, d, max(P, 1), W, dtype)
     c.fill_(float("nan"))
     layer, row = 1, 2
