@@ -555,6 +555,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run * c + log2f(l_tot)) * kLn2;
 }
 
+// Whether the dynamic-LDS limit of kernel slot `slot` was raised on the
+// current device (a host call made once per kernel and device).
+constexpr int kMaxDevices = 64;
+inline bool* lds_flag(int slot) {
+    static bool flags[kMaxDevices][8] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    return &flags[dev][slot];
+}
+
 // ----------------------------------------------------------------- plain path
 // One thread per query row of a 64-position tile of one q head; K/V tiles in
 // LDS as fp32; two passes per tile (scores for the tile maximum, then the
@@ -1227,13 +1237,13 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
             case 8: fn = (const void*)prefill_bf16_kernel<8>; break;
             default: return hipErrorInvalidValue;
         }
-        // raise the dynamic LDS limit once per kernel (a host call, not per launch)
-        static bool lds_set[4] = {false, false, false, false};
+        // raise the dynamic LDS limit once per kernel and device (a host call, not per launch)
         const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
-        if (!lds_set[gi]) {
+        bool* set = lds_flag(gi);
+        if (!set || !*set) {
             const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
-            lds_set[gi] = true;
+            if (set) *set = true;
         }
         switch (group) {
             case 1: hipLaunchKernelGGL(prefill_bf16_kernel<1>, grid, dim3(kThreads), lds, stream, p); break;
@@ -1272,7 +1282,6 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
     const int64_t n_pre_pad = (kb_pre * n_bg + kXcds - 1) / kXcds * kXcds;
     const dim3 grid_k((unsigned)(n_pre_pad + (n_kb - kb_pre) * n_bg));
     const size_t lds_q = (size_t)kStages * kStageBytes;
-    static bool lds_set[8] = {false, false, false, false, false, false, false, false};
     const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
     const void* fq = nullptr;
     const void* fk = nullptr;
@@ -1283,12 +1292,13 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
         case 8: fq = (const void*)bwd_dq_kernel<8>; fk = (const void*)bwd_dkdv_kernel<8>; break;
         default: return hipErrorInvalidValue;
     }
-    if (!lds_set[gi]) {
+    bool* set = lds_flag(4 + gi);
+    if (!set || !*set) {
         hipError_t e = hipFuncSetAttribute(fq, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_q);
         if (e != hipSuccess) return e;
         e = hipFuncSetAttribute(fk, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkdvLds);
         if (e != hipSuccess) return e;
-        lds_set[gi] = true;
+        if (set) *set = true;
     }
     // dK/dV first: its prefix blocks are the longest workgroups of the two
     // launches (measured 1.3% faster than dQ first; running the two on two
