@@ -349,6 +349,28 @@ typedef struct {
 
 int ps_prefill_attn_bwd(const ps_prefill_bwd_args* args, void* stream);
 
+/* Host-side pool of block indices with reference counts: the bookkeeping of
+ * the block table.  A serving loop keeps one pool for window blocks (cache
+ * rows, size max_seqs) and one for prefix blocks (size prefix_blocks); a
+ * sequence takes a window block of its own and a prefix block that rollouts
+ * of the same prompt share, each holding one reference (the PREFIX block is
+ * read-only once prefilled, papers.ananclaw.com explainer, section
+ * "核心方法"; the policy combines with paged memory management, same page,
+ * section "工程启发").  A block returns to the free list when its last
+ * reference is released; the cache bytes are not touched.  Blocks are handed
+ * out lowest index first.  A pool is plain host memory, not thread-safe:
+ * callers that share one across threads serialise the calls.  Errors:
+ * PS_ERR_INVALID (NULL, index out of range, releasing or retaining a free
+ * block), PS_ERR_CAPACITY (no free block). */
+typedef struct ps_block_pool ps_block_pool;
+int ps_block_pool_create(int32_t n_blocks, ps_block_pool** out);   /* n_blocks >= 1 */
+int ps_block_pool_destroy(ps_block_pool* pool);                     /* NULL is a no-op */
+int ps_block_alloc(ps_block_pool* pool, int32_t* block);            /* one reference */
+int ps_block_retain(ps_block_pool* pool, int32_t block);            /* one more reference */
+int ps_block_release(ps_block_pool* pool, int32_t block);           /* one less; freed at zero */
+int ps_block_refcount(const ps_block_pool* pool, int32_t block, int32_t* count);
+int ps_block_free_count(const ps_block_pool* pool, int32_t* count);
+
 /* Class of a (query tile, key tile) pair, query positions [i0, i1] and key
  * positions [j0, j1] (both non-empty, contiguous): 0 SKIP (no visible pair),
  * 1 FULL (every pair visible), 2 MASKED.  The same closed form the prefill

@@ -18,7 +18,7 @@ __all__ = [
     "PS_BF16", "PS_F32", "PSError", "CacheDesc", "Cache", "lib",
     "ps_cache_bytes", "ps_cache_create", "ps_cache_destroy", "ps_cache_blocks",
     "ps_cache_set_decode_split", "ps_cache_set_checks", "ps_cache_check_flags", "ps_kv_append_evict", "ps_decode_attn", "ps_decode_step",
-    "ps_prefill_attn", "ps_tile_class", "ps_status_str", "ps_version", "SeqBatch",
+    "ps_prefill_attn", "ps_tile_class", "ps_status_str", "ps_version", "SeqBatch", "BlockPool",
 ]
 
 PS_OK, PS_ERR_INVALID, PS_ERR_UNSUPPORTED, PS_ERR_CAPACITY, PS_ERR_HIP = range(5)
@@ -91,6 +91,13 @@ _SIGS = {
                                       ctypes.c_float, _vp]),
     "ps_prefill_attn": (ctypes.c_int, [ctypes.POINTER(_PrefillArgs), _vp]),
     "ps_prefill_attn_bwd": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), _vp]),
+    "ps_block_pool_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
+    "ps_block_pool_destroy": (ctypes.c_int, [_vp]),
+    "ps_block_alloc": (ctypes.c_int, [_vp, ctypes.POINTER(_i32)]),
+    "ps_block_retain": (ctypes.c_int, [_vp, _i32]),
+    "ps_block_release": (ctypes.c_int, [_vp, _i32]),
+    "ps_block_refcount": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i32)]),
+    "ps_block_free_count": (ctypes.c_int, [_vp, ctypes.POINTER(_i32)]),
     "ps_tile_class": (ctypes.c_int, [_i64, _i64, _i64, _i64, _i64, _i64]),
     "ps_status_str": (ctypes.c_char_p, [ctypes.c_int]),
     "ps_version": (ctypes.c_char_p, []),
@@ -177,6 +184,49 @@ def ps_cache_check_flags(handle: int, clear: bool = False, stream=None) -> int:
     _check(lib.ps_cache_check_flags(ctypes.c_void_p(handle), ctypes.byref(f), int(bool(clear)), _stream(stream)),
            "ps_cache_check_flags")
     return f.value
+
+
+class BlockPool:
+    """Host pool of block indices with reference counts (ps_block_pool_*):
+    one for window blocks (cache rows), one for prefix blocks."""
+
+    def __init__(self, n_blocks: int):
+        h = ctypes.c_void_p()
+        _check(lib.ps_block_pool_create(n_blocks, ctypes.byref(h)), "ps_block_pool_create")
+        self.handle = h.value
+
+    def alloc(self) -> int:
+        b = ctypes.c_int32()
+        _check(lib.ps_block_alloc(ctypes.c_void_p(self.handle), ctypes.byref(b)), "ps_block_alloc")
+        return b.value
+
+    def retain(self, block: int) -> None:
+        _check(lib.ps_block_retain(ctypes.c_void_p(self.handle), block), "ps_block_retain")
+
+    def release(self, block: int) -> None:
+        _check(lib.ps_block_release(ctypes.c_void_p(self.handle), block), "ps_block_release")
+
+    def refcount(self, block: int) -> int:
+        n = ctypes.c_int32()
+        _check(lib.ps_block_refcount(ctypes.c_void_p(self.handle), block, ctypes.byref(n)), "ps_block_refcount")
+        return n.value
+
+    @property
+    def free_count(self) -> int:
+        n = ctypes.c_int32()
+        _check(lib.ps_block_free_count(ctypes.c_void_p(self.handle), ctypes.byref(n)), "ps_block_free_count")
+        return n.value
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            lib.ps_block_pool_destroy(ctypes.c_void_p(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 class SeqBatch:

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libprefix_sliding.so")
-SOURCES = ["ps_capi.cpp", "ps_append.hip", "ps_decode.hip", "ps_prefill.hip"]
+SOURCES = ["ps_capi.cpp", "ps_blocks.cpp", "ps_append.hip", "ps_decode.hip", "ps_prefill.hip"]
 ARCH = os.environ.get("PS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
