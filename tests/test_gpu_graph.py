@@ -78,8 +78,12 @@ def test_graph_replays_match_eager_calls(checks):
         ref, ref_lse = decode_reference(seed, layer, 5, first + 5, P, W, hq, hkv, d, base, DT_BF16)
         assert np.max(np.abs(dev_to_f32(out_g[layer])[0] - ref)) <= tol(DT_BF16), layer
         np.testing.assert_allclose(dev_to_f32(lse_g[layer])[0], ref_lse, rtol=0, atol=lse_tol(DT_BF16))
-    for a, b in zip(*(c.blocks(layer) for c in (cg, ce) for layer in [layers - 1])):
-        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # the sequence's written slots: prefix slots [0, P) and the full window block
+    for layer in range(layers):
+        (kpg, vpg, kwg, vwg), (kpe, vpe, kwe, vwe) = cg.blocks(layer), ce.blocks(layer)
+        for a, b in ((kpg[row][:, :P], kpe[row][:, :P]), (vpg[row][:, :P], vpe[row][:, :P]),
+                     (kwg[row], kwe[row]), (vwg[row], vwe[row])):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), layer
     if checks:
         assert ps.ps_cache_check_flags(cg.handle) == 0 and ps.ps_cache_check_flags(ce.handle) == 0
     del g
