@@ -26,7 +26,7 @@ bool desc_supported(const ps_cache_desc* d) {
     if (d->head_dim != 64 && d->head_dim != 128) return false;
     if (d->dtype != PS_BF16 && d->dtype != PS_F32) return false;
     const int g = d->n_q_heads / d->n_kv_heads;
-    return g == 1 || g == 2 || g == 4 || g == 8;
+    return g >= 1 && g <= 8;  // GQA groups of the Qwen2.5 / Qwen3 / Llama families
 }
 
 // Buffer layout: K prefix pools of every layer, K window pools, V prefix

@@ -398,8 +398,11 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     constexpr int PARTS = NT >= PAIRS ? NT / PAIRS : 1;
     constexpr int kBatch = 16;
     __shared__ float red[PARTS > 1 ? PARTS * 3 * PAIRS : 1];  // [PARTS][3][PAIRS]
+    // (threads past PARTS * PAIRS, when PAIRS does not divide the workgroup,
+    // take no part)
     const int part = NT >= PAIRS ? tid / PAIRS : 0;
-    for (int pair = (NT >= PAIRS ? tid % PAIRS : tid); pair < PAIRS; pair += (NT >= PAIRS ? PAIRS : NT)) {
+    for (int pair = (NT >= PAIRS ? tid % PAIRS : tid); part < PARTS && pair < PAIRS;
+         pair += (NT >= PAIRS ? PAIRS : NT)) {
         const int hh = pair / D, dim = pair % D;
         const float* oh = p.ws_o + ((ws_head0 + hh) * p.s_max) * D + dim;
         const float* mlh = p.ws_ml + ((ws_head0 + hh) * p.s_max) * 2;
@@ -504,7 +507,11 @@ hipError_t dispatch_g(int group, int rows, const DecodeParams& p, hipStream_t st
     switch (group) {
         case 1: return dispatch_rows<T, D, 1>(rows, p, stream);
         case 2: return dispatch_rows<T, D, 2>(rows, p, stream);
+        case 3: return dispatch_rows<T, D, 3>(rows, p, stream);
         case 4: return dispatch_rows<T, D, 4>(rows, p, stream);
+        case 5: return dispatch_rows<T, D, 5>(rows, p, stream);
+        case 6: return dispatch_rows<T, D, 6>(rows, p, stream);
+        case 7: return dispatch_rows<T, D, 7>(rows, p, stream);
         case 8: return dispatch_rows<T, D, 8>(rows, p, stream);
         default: return hipErrorInvalidValue;
     }

@@ -75,7 +75,7 @@ def test_cache_bytes_formula():
     assert ps.ps_cache_bytes(d) >= 2 * kv
     assert ps.ps_cache_bytes(d) < 2 * kv + 8 * 1024 * 1024
     for bad in [dict(window=0), dict(n_kv_heads=3), dict(prefix_cap=-1), dict(head_dim=96),
-                dict(dtype=7), dict(n_q_heads=24, n_kv_heads=8)]:
+                dict(dtype=7), dict(n_q_heads=128, n_kv_heads=8)]:  # GQA 16: no decode kernel
         assert ps.ps_cache_bytes(_desc(**bad)) == 0, bad
 
 

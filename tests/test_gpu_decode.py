@@ -195,6 +195,10 @@ def test_ragged_batched_decode(fused):
     (500, 64, 300, 8, 1, 128, DT_F32, 16),   # all prefix (P > L), GQA 8, fp32 d=128
     (10, 1000, 600, 2, 2, 64, DT_BF16, 64),  # no eviction yet (W > L), MHA, bf16 d=64
     (7, 33, 777, 16, 8, 128, DT_BF16, 256),  # large split, ragged tail
+    (12, 90, 500, 28, 4, 128, DT_BF16, 0),   # GQA 7 (28 q heads over 4 kv heads), automatic split
+    (5, 40, 300, 15, 3, 128, DT_BF16, 32),   # GQA 5
+    (9, 64, 350, 12, 2, 64, DT_BF16, 32),    # GQA 6, bf16 d=64
+    (3, 30, 200, 6, 2, 64, DT_F32, 16),      # GQA 3, fp32
 ])
 def test_decode_edge_cases(P, W, L, hq, hkv, d, dtype, split):
     seed, base = 5, 1e4
