@@ -70,7 +70,7 @@ typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
 typedef struct {
     int32_t n_layers;       /* >= 1 */
     int32_t max_seqs;       /* >= 1: window blocks (sequence rows) */
-    int32_t n_q_heads;      /* Hq >= 1, multiple of n_kv_heads */
+    int32_t n_q_heads;      /* Hq >= 1, n_kv_heads times 1 to 8 (the GQA group) */
     int32_t n_kv_heads;     /* Hkv >= 1 */
     int32_t head_dim;       /* d: 64 or 128 */
     int32_t prefix_cap;     /* largest prefix length P any sequence may use, >= 0 */
@@ -289,10 +289,11 @@ typedef struct {
                                    NULL: prefix_len; only together with starts */
 } ps_prefill_args;
 
-/* bf16 with head_dim 128 and GQA group 1, 2, 4 or 8 runs on the MFMA kernel;
- * every other supported shape (bf16 head_dim 64, other GQA groups, fp32) runs
- * on a plain kernel with fp32 arithmetic: same results within the dtype's
- * tolerance, far slower.
+/* bf16 with head_dim 128 and a GQA group of 1 to 8 runs on the MFMA kernel
+ * (groups 3 and 5-7 on the layout of the next power of two, the missing
+ * heads' rows idle); every other supported shape (bf16 head_dim 64, groups
+ * above 8, fp32) runs on a plain kernel with fp32 arithmetic: same results
+ * within the dtype's tolerance, far slower.
  * Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,
  * scale <= 0 or not finite), PS_ERR_UNSUPPORTED (head_dim other than 64 or
  * 128, a dtype other than bf16 / fp32, a chunk reaching position 2^31),
@@ -317,8 +318,8 @@ int ps_prefill_attn(const ps_prefill_args* args, void* stream);
  * q, k, v (P is rebuilt from it); delta [B][T][n_q_heads] fp32 is a
  * caller-owned workspace the call overwrites.  Every pointer is device memory
  * the caller owns; dq, dk and dv are overwritten (no accumulation into them).
- * bf16 only, head_dim 128, GQA group 1, 2, 4 or 8.  Stream-ordered: Delta,
- * then dq, then dk/dv, on the given stream.
+ * bf16 only, head_dim 128, GQA group 1 to 8.  Stream-ordered: Delta, then
+ * dk/dv, then dq, on the given stream.
  *
  * Errors: PS_ERR_INVALID (NULL pointer, batch < 1, seq_len < 0, start_pos < 0,
  * prefix_len < 0, window < 1, n_q_heads not a multiple of n_kv_heads, scale

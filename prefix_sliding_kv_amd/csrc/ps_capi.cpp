@@ -424,7 +424,7 @@ int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) {
     if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
     if (a->dtype != PS_BF16 || d != 128) return PS_ERR_UNSUPPORTED;
     const int group = hq / hkv;
-    if (group != 1 && group != 2 && group != 4 && group != 8) return PS_ERR_UNSUPPORTED;
+    if (group < 1 || group > 8) return PS_ERR_UNSUPPORTED;
     if (a->start_pos + (int64_t)a->seq_len >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
     // byte offsets of rows inside one sequence (plus one 64-row sub-tile past
     // its end) are 32-bit in the kernels

@@ -342,11 +342,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
     const float c = p.scale_log2;                              // > 0 (checked on the host)
 
-    // this lane's query: stacked row 32*wave + col
+    // this lane's query: stacked row 32*wave + col.  G is the layout's head
+    // count; a group of fewer heads (3 on the 4-head layout, 5 to 7 on the
+    // 8-head one) leaves the rows of the missing heads idle.
     const int qrow = 32 * wave + col;
-    const int head = g * G + qrow / QP;
+    const int greal = p.hq / p.hkv;
+    const int hh = qrow / QP;
+    const int head = g * greal + (hh < greal ? hh : 0);
     const int my_t = t0 + qrow % QP;
-    const bool q_ok = my_t < p.seq_len;
+    const bool q_ok = my_t < p.seq_len && hh < greal;
     const int my_i = (int)S + my_t;
     Vec16 qreg[8];
     {
@@ -554,6 +558,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         }
     if (p.lse && h == 0) p.lse[((int64_t)b * p.seq_len + my_t) * p.hq + head] = (m_run * c + log2f(l_tot)) * kLn2;
 }
+
+// Stacked-row layout of a GQA group: the kernels are built for 1, 2, 4 and
+// 8 heads per kv head; 3 runs on the 4-head layout and 5 to 7 on the 8-head
+// one, the missing heads' rows idle.
+inline int layout_group(int group) { return group <= 2 ? group : (group <= 4 ? 4 : 8); }
 
 // Whether the dynamic-LDS limit of kernel slot `slot` was raised on the
 // current device (a host call made once per kernel and device).
@@ -816,9 +825,11 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
     const float c = p.scale_log2;
 
     const int qrow = 32 * wave + col;
-    const int head = g * G + qrow / QP;
+    const int greal = p.hq / p.hkv;  // heads of the group (<= G; missing heads' rows idle)
+    const int hh = qrow / QP;
+    const int head = g * greal + (hh < greal ? hh : 0);
     const int my_t = t0 + qrow % QP;
-    const bool q_ok = my_t < p.seq_len;
+    const bool q_ok = my_t < p.seq_len && hh < greal;
     const int my_i = (int)p.start_pos + my_t;
     const int64_t row_el = ((int64_t)b * p.seq_len + (q_ok ? my_t : 0)) * p.hq + head;
     Vec16 qreg[8], dreg[8];
@@ -1000,6 +1011,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane >> 5, col = lane & 31;
     const int T = p.seq_len, hq = p.hq, hkv = p.hkv;
+    // heads of the group; with fewer than G the rows of the missing heads
+    // load a real head's data and are masked out of P
+    const int greal = hq / hkv;
+    const bool padded = greal < G;
     const int n_kb = (T + kKB - 1) / kKB;
     const int S0 = (int)p.start_pos;
     const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
@@ -1083,13 +1098,13 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int row = 8 * wave + 4 * i + (lane >> 4);
-            const int t = ts + row % QS, head = g * G + row / QS;
+            const int t = ts + row % QS, head = g * greal + (row / QS < greal ? row / QS : 0);
             const int off = (t * hq + head) * D * 2 + (((lane & 15) ^ b_chunk_swz(row)) << 4);
             dma16_asm(qr, off, sb + (8 * wave + 4 * i) * kRowBytes);
             dma16_asm(dr, off, sb + kSubRowBytes + (8 * wave + 4 * i) * kRowBytes);
         }
         if (wave < 2) {
-            const int t = ts + lane % QS, head = g * G + lane / QS;
+            const int t = ts + lane % QS, head = g * greal + (lane / QS < greal ? lane / QS : 0);
             dma4_asm(xr, (t * hq + head) * 4, sb + 2 * kSubRowBytes + wave * kSubRows * 4);
         }
     };
@@ -1147,9 +1162,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                 for (int r = 0; r < 16; ++r) {
                     const int qr_ = 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
                     float sv = s[r];
-                    if (cls == kMasked) {
+                    if (cls == kMasked || padded) {
                         const int i = S0 + ts + qr_ % QS;
-                        const bool vis = my_j <= i && (my_j < P32 || my_j > i - w32) && col < wk_n;
+                        const bool vis = my_j <= i && (my_j < P32 || my_j > i - w32) && col < wk_n &&
+                                         qr_ / QS < greal;
                         sv = vis ? sv : -INFINITY;
                     }
                     pf[r] = fast_exp2(fmaf(sv, c, -lse_s[qr_] * kLog2eF));
@@ -1225,7 +1241,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p, hipStream_t stream) {
     if (p.seq_len == 0) return hipSuccess;
-    if (dtype == PS_BF16 && head_dim == 128 && (group == 1 || group == 2 || group == 4 || group == 8)) {
+    if (dtype == PS_BF16 && head_dim == 128 && group >= 1 && group <= 8) {
+        group = layout_group(group);
         const int qp = 32 * kWaves / group;
         dim3 grid((unsigned)(((p.seq_len + qp - 1) / qp) * p.hkv * p.batch));
         const size_t lds = (size_t)kStages * kStageBytes;
@@ -1270,6 +1287,8 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
 hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream) {
     const int64_t rows = (int64_t)p.f.batch * p.f.seq_len * p.f.hq;
     if (rows == 0) return hipSuccess;
+    if (group < 1 || group > 8) return hipErrorInvalidValue;
+    group = layout_group(group);
     hipLaunchKernelGGL(bwd_delta_kernel, dim3((unsigned)((rows * 16 + 255) / 256)), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(p.f.out), static_cast<const uint16_t*>(p.dout), p.delta_out, rows);
     const int qp = 32 * kWaves / group;

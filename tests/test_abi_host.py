@@ -159,7 +159,7 @@ def test_prefill_bwd_rejects_bad_arguments_before_any_launch():
     assert call(scale=float("nan")) == ps.PS_ERR_INVALID
     assert call(dtype=ps.PS_F32) == ps.PS_ERR_UNSUPPORTED
     assert call(head_dim=64) == ps.PS_ERR_UNSUPPORTED
-    assert call(n_q_heads=6, n_kv_heads=2) == ps.PS_ERR_UNSUPPORTED
+    assert call(n_q_heads=32, n_kv_heads=2) == ps.PS_ERR_UNSUPPORTED  # GQA 16
     assert call(start_pos=(1 << 31) - 8) == ps.PS_ERR_UNSUPPORTED
     assert call(dv=0) == ps.PS_ERR_INVALID
     assert call(delta=0) == ps.PS_ERR_INVALID

@@ -65,6 +65,9 @@ def check(name, got, ref):
     (2, 1, 1, 300, 400, 8, 0, 1.0),      # P > T: plain causal
     (4, 2, 1, 290, 30, 50, 1000, 3.0),   # chunk not starting at 0
     (2, 1, 1, 1, 0, 5, 0, 1.0),          # single token
+    (6, 2, 1, 250, 12, 60, 0, 3.0),      # G=3 on the 4-head layout
+    (10, 2, 1, 200, 7, 50, 0, 3.0),      # G=5 on the 8-head layout
+    (28, 4, 1, 180, 20, 64, 0, 1.0),     # G=7: 28 q heads over 4 kv heads
 ])
 def test_trainer_backward_small(hq, hkv, B, T, P, W, start, scale):
     note(f"backward hq={hq} hkv={hkv} B={B} T={T} P={P} W={W} start={start} s={scale}")

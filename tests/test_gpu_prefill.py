@@ -61,7 +61,9 @@ def run_trainer(q, k, v, P, W, start, dtype, with_lse=True):
     (DT_BF16, 128, 2, 1, 1, 64, 100, 8, 1.0),   # exactly one tile, all prefix
     (DT_BF16, 128, 2, 1, 1, 1, 0, 5, 1.0),      # single token
     (DT_BF16, 64, 4, 2, 2, 300, 20, 70, 3.0),   # bf16 d=64: plain kernel
-    (DT_BF16, 128, 6, 2, 1, 200, 9, 50, 3.0),   # GQA 3: plain kernel
+    (DT_BF16, 128, 6, 2, 1, 200, 9, 50, 3.0),   # GQA 3 on the 4-head layout
+    (DT_BF16, 128, 10, 2, 1, 230, 9, 50, 3.0),  # GQA 5 on the 8-head layout
+    (DT_BF16, 128, 28, 4, 2, 200, 20, 70, 1.0), # GQA 7: 28 q heads over 4 kv heads
     (DT_BF16, 64, 16, 1, 1, 130, 5, 40, 1.0),   # GQA 16, d=64: plain kernel
 ])
 def test_trainer_forward_small(dtype, d, hq, hkv, B, T, P, W, scale):
@@ -82,6 +84,7 @@ def test_trainer_forward_small(dtype, d, hq, hkv, B, T, P, W, scale):
     (DT_BF16, 128, 4, 2, 300, 64, 100, 400, 3.0),    # chunk straddles the prefix end
     (DT_BF16, 128, 16, 8, 64, 512, 5000, 700, 1.0),  # Qwen head shape
     (DT_BF16, 64, 4, 2, 30, 200, 1000, 300, 3.0),    # bf16 d=64 cache: plain kernel
+    (DT_BF16, 128, 28, 4, 30, 200, 1000, 300, 1.0),  # GQA 7 on the 8-head layout
     (DT_F32, 128, 4, 2, 30, 200, 1000, 300, 1.0),
     (DT_F32, 128, 4, 2, 300, 64, 100, 400, 1.0),
 ])
