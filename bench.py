@@ -23,6 +23,8 @@ Printed as one JSON line (rank 0, N=1):
                token each per layer: tok/s and achieved HBM GB/s
   rollouts_decode 64 rollouts of one prompt (P=1024) with the prompt in one
                shared prefix block, and with private copies
+  r1_distill_qwen7b_shape  the same decode and trainer legs at the attention
+               shape of the pages' second model (Hq=28, Hkv=4: GQA 7)
   hbm_copy     measured device-to-device copy bandwidth (read + write) and the
                decode rates as fractions of it (the decode only reads, so it
                can exceed a copy)
@@ -414,6 +416,85 @@ def exact_flops(q_lo, q_hi, P, Wn, hq, d):
     return 4.0 * d * hq * tot
 
 
+def r1_distill_bench(torch, ps, np):
+    """The attention of DeepSeek-R1-Distill-Qwen-7B's shape (28 layers, Hq=28,
+    Hkv=4, d=128: GQA 7, run on the 8-head layout): batch-1 decode at a 128K
+    trace (P=100, W=4096, one captured 28-launch step) and the trainer forward
+    and backward at B=8, T=8192, P=256, W=2048.  Random inputs (the times do
+    not depend on them)."""
+    L_, hq, hkv = 28, 28, 4
+    scale = 1.0 / math.sqrt(D)
+    cache = ps.Cache(L_, 1, hq, hkv, D, P, W, ps.PS_BF16)
+    for layer in range(L_):
+        for t in cache.blocks(layer):
+            t.normal_()
+    batch = ps.SeqBatch(torch.zeros(1, dtype=torch.int32, device="cuda"),
+                        torch.full((1,), P, dtype=torch.int32, device="cuda"),
+                        torch.full((1,), TRACE - 1, dtype=torch.int64, device="cuda"))
+    q = torch.randn(L_, 1, hq, D, device="cuda").to(torch.bfloat16)
+    kn = torch.randn(L_, 1, hkv, D, device="cuda").to(torch.bfloat16)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        for layer in range(L_):
+            ps.ps_decode_step(cache.handle, layer, batch, q[layer], kn[layer], kn[layer], out[layer], None, scale, gs)
+        with torch.cuda.graph(g, stream=gs):
+            for layer in range(L_):
+                ps.ps_decode_step(cache.handle, layer, batch, q[layer], kn[layer], kn[layer], out[layer], None,
+                                  scale, gs)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 200
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    per_launch = 2 * hkv * D * (P + W) * 2
+    res = {"workload": "DeepSeek-R1-Distill-Qwen-7B attention shape: 28 layers, Hq=28, Hkv=4, d=128 (GQA 7)",
+           "decode": {"config": "batch 1, P=100, W=4096, trace 128K, fused append + decode per layer, hipGraph",
+                      "tok_s": round(1e3 / ms, 1), "ms_per_step": round(ms, 4), "bytes_per_launch": per_launch,
+                      "hbm_frac": round(per_launch * L_ / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
+    del g
+    cache.close()
+    B, T, Pt, Wt = 8, 8192, 256, 2048
+    q = torch.randn(B, T, hq, D, device="cuda").to(torch.bfloat16)
+    k = torch.randn(B, T, hkv, D, device="cuda").to(torch.bfloat16)
+    v = torch.randn(B, T, hkv, D, device="cuda").to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, T, hq, device="cuda")
+    fwd = lambda: ps.ps_prefill_attn(q, k, v, o, start_pos=0, prefix_len=Pt, window=Wt, scale=scale, lse=lse,
+                                     stream=stream)
+    do = torch.randn_like(q)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(B, T, hq, device="cuda")
+    bwd = lambda: ps.ps_prefill_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, start_pos=0, prefix_len=Pt,
+                                         window=Wt, scale=scale, stream=stream)
+    fx = exact_flops(0, T, Pt, Wt, hq, D) * B
+    for name, fn, flops in (("trainer_forward", fwd, fx), ("trainer_backward", bwd, 2.5 * fx)):
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 5
+        res[name] = {"config": "B=8, T=8192, P=256, W=2048", "ms": round(t, 3),
+                     "tflops_exact": round(flops / t / 1e9, 1),
+                     "frac_mfma_exact": round(flops / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    log(f"R1-Distill-Qwen-7B shape: {res}")
+    return res
+
+
 def prefill_bench(torch, ps, synth, np):
     res = {}
     scale = 1.0 / math.sqrt(D)
@@ -671,6 +752,7 @@ def main():
     base_cmp = {} if args.no_baselines else baselines_bench(torch, ps)
     batched = {} if args.no_baselines else batched_bench(torch, ps, np)
     rollouts = {} if args.no_baselines else rollouts_bench(torch, ps, np)
+    r1 = {} if args.no_prefill else r1_distill_bench(torch, ps, np)
     cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
     line = {
         "metric": METRIC,
@@ -702,6 +784,7 @@ def main():
         "baselines": base_cmp,
         "batched_decode": batched,
         "rollouts_decode": rollouts,
+        "r1_distill_qwen7b_shape": r1,
         "hbm_copy": {"gbs": round(copy_gbs, 1),
                      "note": "device-to-device copy of 256 MiB, read + write bytes / time",
                      "decode_frac_of_copy": round(achieved / copy_gbs, 4),
