@@ -156,8 +156,16 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     p.n_seqs = batch->n;
     const int st = batch_checks(c, layer, batch, knew ? 1 : 0, knew ? ps::kCheckAppend : ps::kCheckQuery, stream);
     if (st != PS_OK) return st;
-    const int rows = c->decode_rows > 0 ? c->decode_rows : auto_decode_rows(c, batch->n);
     const int group = c->desc.n_q_heads / c->desc.n_kv_heads;
+    if (c->decode_rows == 0 && c->desc.dtype == PS_BF16 && c->desc.head_dim == 128 && group >= 5) {
+        // five or more heads per kv head: the matrix-core kernel (its own
+        // split size; measured faster from G = 5 on, 2% slower at G = 4)
+        const int64_t n_wg = (int64_t)batch->n * c->desc.n_kv_heads *
+                             ((c->rows_per_head + ps::kDecodeMfmaRows - 1) / ps::kDecodeMfmaRows);
+        p.stream_nt = n_wg >= 1024;
+        return hip_status(ps::launch_decode_mfma(p, (hipStream_t)stream));
+    }
+    const int rows = c->decode_rows > 0 ? c->decode_rows : auto_decode_rows(c, batch->n);
     // several workgroups per CU: the kernel marks its K/V loads non-temporal
     const int64_t n_wg = (int64_t)batch->n * c->desc.n_kv_heads * ((c->rows_per_head + rows - 1) / rows);
     p.stream_nt = n_wg >= 1024;

@@ -471,6 +471,342 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     }
 }
 
+// ------------------------------------------------------------ MFMA decode
+// bf16, head_dim 128, GQA groups of 5 to 8 heads (4 also works; the host
+// sends 4 to the vector kernel, which is 2% faster there).  With many heads per kv
+// head the vector work per key row (one dot product and eight multiply-adds
+// of the V sum per head) outgrows the streaming, so the products run on the
+// matrix cores: per 16-key block S^T = K Q^T with v_mfma_f32_16x16x32_bf16
+// (the key rows are the A operand, loaded straight from global memory; the
+// group's heads are the 16 columns, missing heads zero), then
+// O^T += V^T P^T with v_mfma_f32_16x16x16_bf16, V^T coming from transposing
+// LDS reads (ds_read_b64_tr_b16) of the wave's own V rows.  The lane layout
+// of S^T (lane: key 4 (lane / 16) + r, head lane % 16) is exactly the P^T
+// operand of the second product.  Splits of 256 key rows, 4 waves of 64
+// rows; the split combine and the last-arriver merge follow decode_kernel.
+constexpr int kMfWaves = 4;
+constexpr int kMfKeysPerWave = 64;
+constexpr int kMfRows = kMfWaves * kMfKeysPerWave;  // rows per split
+static_assert(kMfRows == kDecodeMfmaRows, "split size shared with the host");
+
+typedef __bf16 mf_bf16x8 __attribute__((ext_vector_type(8)));
+typedef short mf_s16x4 __attribute__((ext_vector_type(4)));
+typedef float mf_f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline mf_bf16x8 mf_as_bf16x8(const Vec16& v) {
+    mf_bf16x8 r;
+    __builtin_memcpy(&r, &v, 16);
+    return r;
+}
+__device__ inline uint32_t mf_pack_bf16x2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 r = {(__bf16)a, (__bf16)b};
+    uint32_t u;
+    __builtin_memcpy(&u, &r, 4);
+    return u;
+}
+// chunk c (16 bytes) of V row r sits at chunk c ^ 2 (r & 3): the four rows a
+// 16-lane transposing read touches then hit different banks
+__device__ inline int mf_v_swz(int row) { return 2 * (row & 3); }
+
+template <bool NTL>
+__global__ void __launch_bounds__(kMfWaves * 64) decode_mfma_kernel(DecodeParams p) {
+    constexpr int D = 128;
+    constexpr int NT = kMfWaves * 64;
+    constexpr int RB = D * 2;  // bytes per row
+    __shared__ __attribute__((aligned(16))) char s_v[kMfWaves][kMfKeysPerWave * RB];
+    __shared__ __attribute__((aligned(16))) float s_o[kMfWaves][16 * D];
+    __shared__ float s_m[kMfWaves][16], s_l[kMfWaves][16], s_w[kMfWaves][16];
+    __shared__ float s_ref[16];
+    __shared__ int s_last;
+    if (p.c.guard && *p.c.guard) return;  // checks on and a check failed
+
+    const int n_groups = p.n_seqs * p.c.hkv;
+    const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
+    const int g = group % p.c.hkv, b = group / p.c.hkv;
+    const int G = p.hq / p.c.hkv;  // heads of the group, 4..8 (host-checked)
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int kl = lane & 15, kq = lane >> 4;
+
+    const int64_t P = p.plen[b];
+    const int64_t i = p.pos[b];
+    const int64_t crow = p.c.rows[b], prow = p.c.prows[b];
+    const int64_t n_pre = i + 1 < P ? i + 1 : P;
+    int64_t n_ring = i - P + 1;
+    n_ring = n_ring < 0 ? 0 : (n_ring > p.c.window ? (int64_t)p.c.window : n_ring);
+    const int64_t n = n_pre + n_ring;
+    const int nsplit = (int)((n + kMfRows - 1) / kMfRows);
+    if (split >= nsplit) return;
+
+    // key row r: slot r of the prefix block below n_pre, else slot r - n_pre
+    // of the window block; V lies v_off bytes after K (as in decode_kernel)
+    constexpr int64_t kRowBytes = RB;
+    const int64_t pre_off = (prow * p.c.hkv + g) * p.c.pcap;
+    const int64_t win_off = (crow * p.c.hkv + g) * p.c.window;
+    const char* kpre_a = static_cast<const char*>(p.c.kpre) + pre_off * kRowBytes;
+    const char* kwin_a = static_cast<const char*>(p.c.kwin) + (win_off - n_pre) * kRowBytes;
+    const int64_t v_off = p.c.v_off;
+    const bool fused = p.knew != nullptr;
+    int64_t new_r = i;
+    if (fused && i >= P) {
+        const int64_t off = i - P;
+        new_r = n_pre + (off < 0x7FFFFFFF ? (int64_t)((uint32_t)off % (uint32_t)p.c.window) : off % p.c.window);
+    }
+    const char* knew_row = fused ? static_cast<const char*>(p.knew) + ((int64_t)b * p.c.hkv + g) * kRowBytes : nullptr;
+    const char* vnew_row = fused ? static_cast<const char*>(p.vnew) + ((int64_t)b * p.c.hkv + g) * kRowBytes : nullptr;
+    auto k_row = [&](int64_t r) -> const char* {
+        if (fused && r == new_r) return knew_row;
+        return (r < n_pre ? kpre_a : kwin_a) + r * kRowBytes;
+    };
+    auto v_row = [&](int64_t r) -> const char* {
+        if (fused && r == new_r) return vnew_row;
+        return (r < n_pre ? kpre_a : kwin_a) + r * kRowBytes + v_off;
+    };
+
+    // Q^T operand: head kl, dims 32 ks + 8 kq .. + 7 (zero for missing heads)
+    Vec16 qb[4];
+    {
+        const bool hok = kl < G;
+        const char* qp = static_cast<const char*>(p.q) + (((int64_t)b * p.hq + g * G + (hok ? kl : 0)) * D) * 2;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qb[ks] = hok ? load16(qp + (32 * ks + 8 * kq) * 2) : Vec16{{0, 0, 0, 0}};
+    }
+    // K operand rows of this wave (key 16 kb + kl, dims 32 ks + 8 kq ..) and
+    // its V rows (row 4 j + kq, 16-byte chunk kl), every load issued first;
+    // rows past the end are clamped to the last valid row and masked below
+    const int64_t r0w = (int64_t)split * kMfRows + (int64_t)wave * kMfKeysPerWave;
+    Vec16 ka[4][4], vv[16];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        int64_t r = r0w + 16 * kb + kl;
+        r = r < n ? r : n - 1;
+        const char* kp = k_row(r);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) ka[kb][ks] = load16_stream<NTL>(kp + (32 * ks + 8 * kq) * 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        int64_t r = r0w + 4 * j + kq;
+        r = r < n ? r : n - 1;
+        vv[j] = load16_stream<NTL>(v_row(r) + kl * 16);
+    }
+
+    mf_f32x4 s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mf_as_bf16x8(ka[kb][ks]), mf_as_bf16x8(qb[ks]), s[kb], 0, 0, 0);
+    }
+
+    // the commit of the new token by split 0 (after the loads above)
+    if (fused && split == 0 && tid < 16) {
+        char* kd = const_cast<char*>((new_r < n_pre ? kpre_a : kwin_a) + new_r * kRowBytes) + tid * 16;
+        *reinterpret_cast<Vec16*>(kd) = load16(knew_row + tid * 16);
+        *reinterpret_cast<Vec16*>(kd + v_off) = load16(vnew_row + tid * 16);
+    }
+
+    // V rows into this wave's LDS region (read back only by this wave)
+    char* vl = s_v[wave];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int row = 4 * j + kq;
+        *reinterpret_cast<Vec16*>(vl + row * RB + ((kl ^ mf_v_swz(row)) << 4)) = vv[j];
+    }
+
+    // scores (log2 units) of keys 16 kb + 4 kq + r for head kl; the wave's
+    // maximum per head over the four lanes that hold that head
+    float sc[4][4];
+    float mw = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool valid = r0w + 16 * kb + 4 * kq + r < n;
+            sc[kb][r] = valid ? s[kb][r] * p.scale_log2 : -INFINITY;
+            mw = fmaxf(mw, sc[kb][r]);
+        }
+    mw = fmaxf(mw, __shfl_xor(mw, 16, 64));
+    mw = fmaxf(mw, __shfl_xor(mw, 32, 64));
+    float lw = 0.f;
+    mf_s16x4 pb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            pr[r] = mw == -INFINITY ? 0.f : fast_exp2(sc[kb][r] - mw);
+            lw += pr[r];
+        }
+        const uint32_t lo = mf_pack_bf16x2(pr[0], pr[1]), hi = mf_pack_bf16x2(pr[2], pr[3]);
+        __builtin_memcpy(&pb[kb], &lo, 4);
+        __builtin_memcpy(reinterpret_cast<char*>(&pb[kb]) + 4, &hi, 4);
+    }
+    lw += __shfl_xor(lw, 16, 64);
+    lw += __shfl_xor(lw, 32, 64);
+
+    // O^T += V^T P^T: lane i of 16-lane group kq gets dims 16 mb + i of keys
+    // 16 kb + 4 kq + j (j = 0..3): group lane L reads 4 dims of key
+    // 16 kb + 4 kq + L / 4 at dims 16 mb + 4 (L % 4)
+    mf_f32x4 o[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) o[mb] = mf_f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint32_t vbase = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)vl;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const int row = 16 * kb + 4 * kq + (kl >> 2);
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) {
+            const int byte = 32 * mb + 8 * (kl & 3);  // within the row, before the swizzle
+            const uint32_t addr = vbase + row * RB + ((((byte >> 4) ^ mf_v_swz(row)) << 4) | (byte & 15));
+            const mf_s16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) mf_s16x4*)(uintptr_t)addr);
+            o[mb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb[kb], o[mb], 0, 0, 0);
+        }
+    }
+
+    // combine the waves: lane holds O^T[dim 16 mb + 4 kq + r][head kl]
+    if (kl < G) {
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s_o[wave][kl * D + 16 * mb + 4 * kq + r] = o[mb][r];
+        if (kq == 0) {
+            s_m[wave][kl] = mw;
+            s_l[wave][kl] = lw;
+        }
+    }
+    __syncthreads();
+    if (tid < 16 && tid < G) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kMfWaves; ++w) M = fmaxf(M, s_m[w][tid]);
+#pragma unroll
+        for (int w = 0; w < kMfWaves; ++w) s_w[w][tid] = s_m[w][tid] == -INFINITY ? 0.f : fast_exp2(s_m[w][tid] - M);
+        s_ref[tid] = M;  // finite: every split holds at least one valid row
+    }
+    __syncthreads();
+
+    const int64_t ws_head0 = (int64_t)b * p.hq + g * G;
+    const int pairs = G * D;
+    for (int idx = tid; idx < pairs; idx += NT) {
+        const int hh = idx / D, dim = idx % D;
+        float O = 0.f, L = 0.f;
+#pragma unroll
+        for (int w = 0; w < kMfWaves; ++w) {
+            O = fmaf(s_w[w][hh], s_o[w][hh * D + dim], O);
+            L = fmaf(s_w[w][hh], s_l[w][hh], L);
+        }
+        const float M = s_ref[hh];
+        if (nsplit == 1) {
+            uint16_t* op = static_cast<uint16_t*>(p.out) + (ws_head0 + hh) * D + dim;
+            *op = Elem<uint16_t>::from_float(O / L);
+            if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (M + log2f(L)) * kLn2;
+        } else {
+            const int64_t slot = (ws_head0 + hh) * p.s_max + split;
+            store_coherent(p.ws_o + slot * D + dim, O);
+            if (dim == 0) {
+                store_coherent(p.ws_ml + slot * 2, M);
+                store_coherent(p.ws_ml + slot * 2 + 1, L);
+            }
+        }
+    }
+    if (nsplit == 1) return;
+
+    // arrival counter and merge by the last split (as in decode_kernel)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t* t = p.tickets + ((int64_t)b * p.c.hkv + g) * kTicketStride;
+        const uint32_t prev = __hip_atomic_fetch_add(t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (prev == (uint32_t)(nsplit - 1));
+        if (s_last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+
+    // Merge: every load is issued before any is used, so the merge costs one
+    // round trip per batch of kMergeBatch splits.  (m, l) of each (head,
+    // split) are read once, by one thread each, and turned into weights in
+    // LDS (reusing s_o); thread t combines outputs t, t + NT, ... (at most
+    // kMfPairsPerThread of them) from its own o loads.
+    constexpr int kMergeBatch = 32;
+    constexpr int kMfPairsPerThread = 8 * D / NT;  // groups of up to 8 heads (the cache's limit)
+    float* s_ml = &s_o[0][0];                    // [G][kMergeBatch] (m, then weight), [G][kMergeBatch] l
+    float* s_wt = s_ml;
+    float* s_ll = s_ml + 16 * kMergeBatch;
+    __shared__ float s_M[16], s_L[16];
+    if (tid < G) {
+        s_M[tid] = -INFINITY;
+        s_L[tid] = 0.f;
+    }
+    float accO[kMfPairsPerThread];
+#pragma unroll
+    for (int k = 0; k < kMfPairsPerThread; ++k) accO[k] = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
+        const int nb = nsplit - s0 < kMergeBatch ? nsplit - s0 : kMergeBatch;
+        float bo[kMfPairsPerThread][kMergeBatch];
+#pragma unroll
+        for (int k = 0; k < kMfPairsPerThread; ++k) {
+            const int pair = tid + k * NT;
+            if (pair < pairs) {
+                const int hh = pair / D, dim = pair % D;
+                const float* oh = p.ws_o + ((ws_head0 + hh) * p.s_max + s0) * D + dim;
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) bo[k][j] = j < nb ? load_coherent(oh + (int64_t)j * D) : 0.f;
+            }
+        }
+        for (int e = tid; e < G * kMergeBatch; e += NT) {
+            const int hh = e / kMergeBatch, j = e % kMergeBatch;
+            const float* mlh = p.ws_ml + ((ws_head0 + hh) * p.s_max + s0 + j) * 2;
+            s_ml[e] = j < nb ? load_coherent(mlh) : -INFINITY;
+            s_ll[e] = j < nb ? load_coherent(mlh + 1) : 0.f;
+        }
+        __syncthreads();
+        if (tid < G) {
+            // new running maximum of the head, rescale of what came before,
+            // and the weights of this batch relative to it
+            float bM = s_M[tid];
+            for (int j = 0; j < nb; ++j) bM = fmaxf(bM, s_ml[tid * kMergeBatch + j]);
+            const float a = s_M[tid] == -INFINITY ? 0.f : fast_exp2(s_M[tid] - bM);
+            float L = s_L[tid] * a;
+            for (int j = 0; j < kMergeBatch; ++j) {
+                const float m = s_ml[tid * kMergeBatch + j];
+                const float w = m == -INFINITY ? 0.f : fast_exp2(m - bM);
+                s_wt[tid * kMergeBatch + j] = w;
+                L = fmaf(w, s_ll[tid * kMergeBatch + j], L);
+            }
+            s_ll[tid * kMergeBatch] = a;  // the rescale factor of earlier batches, read below
+            s_M[tid] = bM;
+            s_L[tid] = L;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kMfPairsPerThread; ++k) {
+            const int pair = tid + k * NT;
+            if (pair < pairs) {
+                const int hh = pair / D;
+                float O = accO[k] * s_ll[hh * kMergeBatch];
+#pragma unroll
+                for (int j = 0; j < kMergeBatch; ++j) O = fmaf(s_wt[hh * kMergeBatch + j], bo[k][j], O);
+                accO[k] = O;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int k = 0; k < kMfPairsPerThread; ++k) {
+        const int pair = tid + k * NT;
+        if (pair < pairs) {
+            const int hh = pair / D, dim = pair % D;
+            uint16_t* op = static_cast<uint16_t*>(p.out) + (ws_head0 + hh) * D + dim;
+            *op = Elem<uint16_t>::from_float(accO[k] / s_L[hh]);
+            if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (s_M[hh] + log2f(s_L[hh])) * kLn2;
+        }
+    }
+}
+
 template <typename T, int D, int G, int NW, int U, bool NTL = false>
 hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
     constexpr int R = NW * (64 / (D / Elem<T>::kPerVec)) * U;
@@ -529,6 +865,16 @@ bool decode_rows_valid(int dtype, int head_dim, int rows) {
     const int r4 = 4 * rpw, r16 = 16 * rpw;
     if (rows < kMinSplitRows) return false;
     return rows == r4 || rows == 2 * r4 || rows == r16 || rows == 2 * r16 || rows == 4 * r16 || rows == 8 * r16;
+}
+
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
+    const int64_t n_wg = ((p.rows_per_head + kMfRows - 1) / kMfRows) * (int64_t)p.c.hkv * p.n_seqs;
+    if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (p.stream_nt)
+        hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3((unsigned)n_wg), dim3(kMfWaves * 64), 0, stream, p);
+    else
+        hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3((unsigned)n_wg), dim3(kMfWaves * 64), 0, stream, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split, const DecodeParams& p,

@@ -123,6 +123,10 @@ struct DecodeParams {
 // Launch decode attention; rows_per_split chosen by the caller (host).
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split,
                          const DecodeParams& p, hipStream_t stream);
+// Decode on the matrix cores: bf16, head_dim 128, GQA groups 4..8, splits of
+// kDecodeMfmaRows key rows.
+constexpr int kDecodeMfmaRows = 256;
+hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream);
 // Rows one wave covers per 16-byte load instruction for (dtype, head_dim).
 int decode_rows_per_load(int dtype, int head_dim);
 // Split sizes the decode kernel is built for: with r = decode_rows_per_load,

@@ -254,6 +254,48 @@ def test_decode_at_positions_beyond_2_31(fused):
         c.close()
 
 
+@pytest.mark.parametrize("hq,hkv,P,W,L,fused", [
+    (10, 2, 100, 4096, 8192, True),      # G=5, 17 splits
+    (10, 2, 7, 300, 1000, False),        # G=5
+    (28, 4, 100, 4096, 131072, True),    # G=7, 28 q heads over 4 kv heads, 128K trace
+    (16, 2, 0, 33, 200, False),          # G=8, no prefix
+    (12, 2, 30, 1, 31, True),            # G=6, W=1: one split, partly filled waves
+    (8, 1, 5, 16, 6, False),             # G=8, six keys
+    (32, 4, 20, 600, 3000, False),       # G=8, ragged last split
+])
+def test_decode_matrix_core_groups(hq, hkv, P, W, L, fused):
+    """bf16 d=128 with five or more q heads per kv head and the automatic
+    split runs on the matrix-core decode kernel; three sequences at different
+    positions in one call."""
+    seed, d, base = 9, 128, 1e6
+    note(f"mfma decode hq={hq} hkv={hkv} P={P} W={W} L={L} fused={fused}")
+    c = new_cache(1, 4, hq, hkv, d, max(P, 1), W, DT_BF16)
+    scale = 1.0 / math.sqrt(d)
+    seqs = [(0, L - 1), (2, max(L // 2, 1) - 1), (3, max(L // 5, 1) - 1)]  # (row, query position)
+    for row, i in seqs:
+        if i > 0:
+            fill_retained(ps, c, 0, row, P, W, i - 1, seed, row, hkv, d, base, DT_BF16)
+    q = to_dev(np.stack([gen(seed, synth.Q, 0, r, [i], hq, d, base, DT_BF16)[0] for r, i in seqs]))
+    k = to_dev(np.stack([gen(seed, synth.K, 0, r, [i], hkv, d, base, DT_BF16)[0] for r, i in seqs]))
+    v = to_dev(np.stack([gen(seed, synth.V, 0, r, [i], hkv, d, base, DT_BF16)[0] for r, i in seqs]))
+    out = torch.empty(len(seqs), hq, d, device="cuda", dtype=torch.bfloat16)
+    lse = torch.empty(len(seqs), hq, device="cuda")
+    b = seq_batch(ps, [r for r, _ in seqs], [P] * len(seqs), [i for _, i in seqs])
+    if fused:
+        ps.ps_decode_step(c.handle, 0, b, q, k, v, out, lse, scale)
+    else:
+        ps.ps_kv_append_evict(c.handle, 0, b, 1, k[:, None], v[:, None])
+        ps.ps_decode_attn(c.handle, 0, b, q, out, lse, scale)
+    torch.cuda.synchronize()
+    got, got_lse = dev_to_f32(out), dev_to_f32(lse)
+    for s_, (row, i) in enumerate(seqs):
+        ref, ref_lse = decode_reference(seed, 0, row, i, P, W, hq, hkv, d, base, DT_BF16)
+        assert np.max(np.abs(got[s_] - ref)) <= tol(DT_BF16), (row, i)
+        np.testing.assert_allclose(got_lse[s_], ref_lse, rtol=0, atol=lse_tol(DT_BF16), err_msg=str((row, i)))
+        check_cache_map(c, 0, row, P, W, i, seed, row, hkv, d, base, DT_BF16)
+    c.close()
+
+
 def test_chunk_append_equals_single_appends():
     """A chunk longer than W (plus prefix tokens) in one call leaves the same
     bytes as appending its tokens one by one."""
