@@ -747,21 +747,23 @@ __global__ void __launch_bounds__(kMfWaves * 64) decode_mfma_kernel(DecodeParams
     for (int s0 = 0; s0 < nsplit; s0 += kMergeBatch) {
         const int nb = nsplit - s0 < kMergeBatch ? nsplit - s0 : kMergeBatch;
         float bo[kMfPairsPerThread][kMergeBatch];
+        // Unconditional loads (split and pair indices clamped into range; the
+        // extra ones get weight 0 or are not written), so the compiler emits
+        // them back to back instead of one branch and one wait each.
 #pragma unroll
         for (int k = 0; k < kMfPairsPerThread; ++k) {
-            const int pair = tid + k * NT;
-            if (pair < pairs) {
-                const int hh = pair / D, dim = pair % D;
-                const float* oh = p.ws_o + ((ws_head0 + hh) * p.s_max + s0) * D + dim;
+            const int pair = tid + k * NT < pairs ? tid + k * NT : pairs - 1;
+            const int hh = pair / D, dim = pair % D;
+            const float* oh = p.ws_o + ((ws_head0 + hh) * p.s_max + s0) * D + dim;
 #pragma unroll
-                for (int j = 0; j < kMergeBatch; ++j) bo[k][j] = j < nb ? load_coherent(oh + (int64_t)j * D) : 0.f;
-            }
+            for (int j = 0; j < kMergeBatch; ++j) bo[k][j] = load_coherent(oh + (int64_t)(j < nb ? j : nb - 1) * D);
         }
         for (int e = tid; e < G * kMergeBatch; e += NT) {
             const int hh = e / kMergeBatch, j = e % kMergeBatch;
-            const float* mlh = p.ws_ml + ((ws_head0 + hh) * p.s_max + s0 + j) * 2;
-            s_ml[e] = j < nb ? load_coherent(mlh) : -INFINITY;
-            s_ll[e] = j < nb ? load_coherent(mlh + 1) : 0.f;
+            const float* mlh = p.ws_ml + ((ws_head0 + hh) * p.s_max + s0 + (j < nb ? j : nb - 1)) * 2;
+            const float m = load_coherent(mlh), l = load_coherent(mlh + 1);
+            s_ml[e] = j < nb ? m : -INFINITY;
+            s_ll[e] = j < nb ? l : 0.f;
         }
         __syncthreads();
         if (tid < G) {
@@ -784,14 +786,12 @@ __global__ void __launch_bounds__(kMfWaves * 64) decode_mfma_kernel(DecodeParams
         __syncthreads();
 #pragma unroll
         for (int k = 0; k < kMfPairsPerThread; ++k) {
-            const int pair = tid + k * NT;
-            if (pair < pairs) {
-                const int hh = pair / D;
-                float O = accO[k] * s_ll[hh * kMergeBatch];
+            const int pair = tid + k * NT < pairs ? tid + k * NT : pairs - 1;
+            const int hh = pair / D;
+            float O = accO[k] * s_ll[hh * kMergeBatch];
 #pragma unroll
-                for (int j = 0; j < kMergeBatch; ++j) O = fmaf(s_wt[hh * kMergeBatch + j], bo[k][j], O);
-                accO[k] = O;
-            }
+            for (int j = 0; j < kMergeBatch; ++j) O = fmaf(s_wt[hh * kMergeBatch + j], bo[k][j], O);
+            accO[k] = O;
         }
         __syncthreads();
     }
