@@ -84,6 +84,37 @@ def test_trainer_backward_small(hq, hkv, B, T, P, W, start, scale):
         np.testing.assert_allclose(delta[b], np.sum(as_f32(do[b]) * out[b], axis=-1), rtol=0, atol=1e-3)
 
 
+def random_bwd_case(case):
+    rng = np.random.default_rng(7000 + case)
+    hkv = int(rng.integers(1, 3))
+    g = int(rng.integers(1, 9))
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(1, 401))
+    P = int(rng.integers(0, 301))
+    W = int(rng.integers(1, 301))
+    start = 0 if rng.random() < 0.5 else int(rng.integers(1, 2001))
+    scale = 3.0 if rng.random() < 0.5 else 1.0
+    return hkv * g, hkv, B, T, P, W, start, scale
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_trainer_backward_random(case):
+    """Seeded random shapes (group size 1 to 8, one or two kv heads, batch 1
+    or 2, T up to 400, any P and W up to 300, a chunk start of 0 or not)."""
+    hq, hkv, B, T, P, W, start, scale = random_bwd_case(case)
+    note(f"backward random {case}: hq={hq} hkv={hkv} B={B} T={T} P={P} W={W} start={start} s={scale}")
+    d = 128
+    pos, q, k, v, do = bwd_inputs(300 + case, B, start, T, hq, hkv, d, scale)
+    dq, dk, dv, delta, out = run_bwd(q, k, v, do, P, W, start)
+    for b in range(B):
+        rq, rk, rv = oracle.attention_bwd(as_f32(q[b]), pos, as_f32(k[b]), as_f32(v[b]), pos, as_f32(do[b]),
+                                          P, W, 1.0 / math.sqrt(d), threads=16)
+        check("dq", dq[b], rq)
+        check("dk", dk[b], rk)
+        check("dv", dv[b], rv)
+        np.testing.assert_allclose(delta[b], np.sum(as_f32(do[b]) * out[b], axis=-1), rtol=0, atol=1e-3)
+
+
 def test_trainer_backward_qwen_config():
     """Batch 8, 8192 tokens, P=256, W=2048, Hq=16, Hkv=8, d=128, bf16 (the
     trainer shape the benchmark times): dq on sampled queries of every batch
