@@ -23,6 +23,8 @@ ps = pytest.importorskip("prefix_sliding_kv_amd")
     (DT_BF16, 128, -1, 1e6),     # Reset PE step: every retained window key moves one position back
     (DT_BF16, 128, 300, 1e4),
     (DT_F32, 64, -7, 1e4),
+    (DT_BF16, 64, 5, 1e4),
+    (DT_F32, 128, -1, 1e6),
 ])
 def test_rerotate_window_keys(dtype, d, delta, base):
     note(f"rerotate dt={dtype} d={d} delta={delta} base={base}")
@@ -87,7 +89,8 @@ def test_rerotate_argument_checks():
     cache.close()
 
 
-@pytest.mark.parametrize("dtype,d,base", [(DT_BF16, 128, 1e6), (DT_F32, 64, 1e4)])
+@pytest.mark.parametrize("dtype,d,base", [(DT_BF16, 128, 1e6), (DT_F32, 64, 1e4), (DT_BF16, 64, 1e4),
+                                          (DT_F32, 128, 1e6)])
 def test_append_with_fused_rope(dtype, d, base):
     """ps_kv_append_rope against ps_kv_append_evict of the same unrotated keys:
     V rows and the slot map must be identical, and each K row must be the
