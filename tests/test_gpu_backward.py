@@ -4,7 +4,7 @@ attention, bf16 MFMA path) against the CPU oracle's float64 gradient.
 The backward takes the forward's output and log-sum-exp from the GPU forward
 of the same inputs and an upstream gradient dout drawn from the seeded
 generator.  Tolerance: the bf16 operands of the four products (P, dS, and the
-bf16 inputs and outputs) carry a relative rounding of 2^-9, so every gradient
+bf16 inputs and outputs) carry a relative rounding of at most 2^-8, so every gradient
 is compared element by element with max-abs error <= 2e-2 * max(1, max|ref|)
 of its tensor, and its Frobenius error must stay below 1e-2 * max(1, |ref|).  A
 dropped or leaked key, a wrong head or a missing scale moves some element by
