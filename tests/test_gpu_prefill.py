@@ -78,6 +78,38 @@ def test_trainer_forward_small(dtype, d, hq, hkv, B, T, P, W, scale):
         np.testing.assert_allclose(got_lse[b], ref_lse, rtol=0, atol=lse_tol(dtype) * (1 + scale * scale))
 
 
+def random_trainer_case(case):
+    rng = np.random.default_rng(3000 + case)
+    dtype = DT_BF16 if rng.random() < 0.75 else DT_F32
+    d = 128 if rng.random() < 0.75 else 64
+    hkv = int(rng.integers(1, 3))
+    g = int(rng.integers(1, 9))
+    B = int(rng.integers(1, 3))
+    T = int(rng.integers(1, 401))
+    P = int(rng.integers(0, 301))
+    W = int(rng.integers(1, 301))
+    start = 0 if rng.random() < 0.5 else int(rng.integers(1, 2001))
+    scale = 3.0 if dtype == DT_BF16 and rng.random() < 0.5 else 1.0
+    return dtype, d, hkv * g, hkv, B, T, P, W, start, scale
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_trainer_forward_random(case):
+    """Seeded random shapes in trainer mode: dtype, head dim, group size 1 to
+    8, batch 1 or 2, T up to 400, any P and W up to 300, chunk start 0 or not."""
+    dtype, d, hq, hkv, B, T, P, W, start, scale = random_trainer_case(case)
+    seed, base = 400 + case, 1e4
+    note(f"trainer random {case}: dt={dtype} d={d} hq={hq} hkv={hkv} B={B} T={T} P={P} W={W} start={start} "
+         f"s={scale}")
+    pos, q, k, v = chunk_inputs(seed, 0, B, start, T, hq, hkv, d, base, dtype, scale)
+    got, got_lse = run_trainer(q, k, v, P, W, start, dtype)
+    for b in range(B):
+        ref, ref_lse = trainer_reference(q, k, v, pos, P, W, d, b, np.arange(T))
+        err = float(np.max(np.abs(got[b] - ref)))
+        assert err <= tol(dtype), (b, err)
+        np.testing.assert_allclose(got_lse[b], ref_lse, rtol=0, atol=lse_tol(dtype) * (1 + scale * scale))
+
+
 @pytest.mark.parametrize("dtype,d,hq,hkv,P,W,start,T,scale", [
     (DT_BF16, 128, 4, 2, 30, 200, 1000, 300, 3.0),   # ring wrapped, window reaches into the ring
     (DT_BF16, 128, 4, 2, 30, 200, 130, 100, 3.0),    # ring not full yet
