@@ -90,9 +90,9 @@ def lse_tol(dtype):
     """Max-abs bar for the log-sum-exp.  The bf16 prefill sums probabilities
     after rounding them to bf16 (8 significant bits, relative error at most
     2^-8 each), so the row sum l is off by at most 2^-8 relative and ln l by
-    at most -ln(1 - 2^-8) = 3.9e-3, however few keys are visible; fp32 score
-    and exponential rounding add far less at unit input scale (tests of
-    scaled inputs multiply the bar by 1 + scale^2)."""
+    at most -ln(1 - 2^-8) = 3.9e-3, however few keys are visible and whatever
+    the input scale (a relative bound on every term); the fp32 score and
+    exponential rounding adds orders of magnitude less."""
     return 4e-3 if dtype == DT_BF16 else 1e-5
 
 

@@ -46,14 +46,17 @@ def check_cache_map(c, layer, row, P, W, last, seed, seq_id, hkv, d, base, dtype
 
 
 # --------------------------------------------------------------- tiny decode
-@pytest.mark.parametrize("fused", [False, True])
-@pytest.mark.parametrize("split_rows", [0, 16])
-def test_tiny_fp32_decode_every_step(fused, split_rows):
+@pytest.mark.parametrize("fused,split_rows,seed", [
+    (False, 0, 0), (True, 0, 0), (False, 16, 0), (True, 16, 0),
+    (True, 0, 1), (False, 0, 2), (True, 16, 3), (False, 16, 4),
+])
+def test_tiny_fp32_decode_every_step(fused, split_rows, seed):
     """1 layer, batch 1, Hq=2, Hkv=1, d=64, fp32, P=8, W=16; positions 0..71
     appended one at a time, a decode query after every append (64 generated
-    steps after the prefix).  Cache map checked after every append."""
-    seed, P, W, hq, hkv, d, base = 0, 8, 16, 2, 1, 64, 1e4
-    note(f"tiny fp32 decode fused={fused} split={split_rows}")
+    steps after the prefix).  Cache map checked after every append.  Seeds
+    0-4."""
+    P, W, hq, hkv, d, base = 8, 16, 2, 1, 64, 1e4
+    note(f"tiny fp32 decode fused={fused} split={split_rows} seed={seed}")
     c = new_cache(1, 1, hq, hkv, d, P, W, DT_F32)
     if split_rows:
         ps.ps_cache_set_decode_split(c.handle, split_rows)
@@ -113,12 +116,17 @@ def test_poisoned_tokens_leave_no_trace_after_eviction():
 
 
 # ----------------------------------------------------- Qwen3-1.7B-shaped decode
-@pytest.mark.parametrize("L,layers", [(8192, [0, 27]), (32768, [5]), (131072, list(range(28)))])
-def test_qwen_shape_decode(L, layers):
+@pytest.mark.parametrize("L,layers,seed", [
+    (8192, [0, 27], 0), (32768, [5], 0), (131072, list(range(28)), 0),
+    (131072, [3, 20], 1), (8192, [11], 2), (32768, [26], 3), (131072, [0, 14], 4),
+])
+def test_qwen_shape_decode(L, layers, seed):
     """28-layer cache, Hq=16, Hkv=8, d=128, bf16, P=100, W=4096, RoPE base 1e6;
-    one fused decode step at position L-1 on the listed layers."""
-    seed, P, W, hq, hkv, d, base = 0, 100, 4096, 16, 8, 128, 1e6
-    note(f"qwen decode L={L} layers={len(layers)}")
+    one fused decode step at position L-1 on the listed layers, seeds 0-4.
+    The oracle's key list also holds evicted middle positions (including the
+    one the step's own append evicts), which it must skip."""
+    P, W, hq, hkv, d, base = 100, 4096, 16, 8, 128, 1e6
+    note(f"qwen decode L={L} layers={len(layers)} seed={seed}")
     c = new_cache(28, 1, hq, hkv, d, P, W, DT_BF16, poison=False)
     i = L - 1
     scale = 1.0 / math.sqrt(d)
@@ -131,13 +139,41 @@ def test_qwen_shape_decode(L, layers):
         lse = torch.empty(1, hq, device="cuda")
         ps.ps_decode_step(c.handle, layer, seq_batch(ps, [0], [P], [i]), q, k, v, out, lse, scale)
         torch.cuda.synchronize()
-        ref, ref_lse = decode_reference(seed, layer, 0, i, P, W, hq, hkv, d, base, DT_BF16)
+        rng = np.random.default_rng(seed * 100 + layer)
+        evicted = np.concatenate([rng.integers(P, i - W + 1, 300), [P, i - W]])
+        ref, ref_lse = decode_reference(seed, layer, 0, i, P, W, hq, hkv, d, base, DT_BF16,
+                                        extra_positions=evicted)
         got = dev_to_f32(out)[0]
         assert np.max(np.abs(got - ref)) <= tol(DT_BF16), (layer, np.max(np.abs(got - ref)))
         np.testing.assert_allclose(dev_to_f32(lse)[0], ref_lse, rtol=0, atol=lse_tol(DT_BF16))
     # retained set is the pages' bound and the cache map is exact
     assert len(oracle.retained_positions(i, P, W)) == 4196
     check_cache_map(c, layers[-1], 0, P, W, i, seed, 0, hkv, d, base, DT_BF16)
+
+
+@pytest.mark.parametrize("split", [0, 16, 32, 64, 128, 256])
+def test_fp32_decode_over_4196_keys(split):
+    """fp32 debug path at the decode configuration's key count: Hq=16, Hkv=8,
+    d=128, P=100, W=4096, query at position 131071 (4196 retained keys), one
+    fused step per split size; output and log-sum-exp within 1e-5 of the
+    oracle."""
+    seed, P, W, hq, hkv, d, base = 3, 100, 4096, 16, 8, 128, 1e6
+    note(f"fp32 decode 4196 keys split={split}")
+    c = new_cache(1, 1, hq, hkv, d, P, W, DT_F32)
+    ps.ps_cache_set_decode_split(c.handle, split)
+    i = 131071
+    fill_retained(ps, c, 0, 0, P, W, i - 1, seed, 0, hkv, d, base, DT_F32)
+    q = to_dev(gen(seed, synth.Q, 0, 0, [i], hq, d, base, DT_F32))
+    k = to_dev(gen(seed, synth.K, 0, 0, [i], hkv, d, base, DT_F32))
+    v = to_dev(gen(seed, synth.V, 0, 0, [i], hkv, d, base, DT_F32))
+    out = torch.empty(1, hq, d, device="cuda")
+    lse = torch.empty(1, hq, device="cuda")
+    ps.ps_decode_step(c.handle, 0, seq_batch(ps, [0], [P], [i]), q, k, v, out, lse, 1.0 / math.sqrt(d))
+    torch.cuda.synchronize()
+    ref, ref_lse = decode_reference(seed, 0, 0, i, P, W, hq, hkv, d, base, DT_F32)
+    np.testing.assert_allclose(dev_to_f32(out)[0], ref, rtol=0, atol=tol(DT_F32))
+    np.testing.assert_allclose(dev_to_f32(lse)[0], ref_lse, rtol=0, atol=lse_tol(DT_F32))
+    c.close()
 
 
 # -------------------------------------------------------- batched ragged decode
@@ -151,18 +187,22 @@ def ragged_batch(seed, n=64, W=4096):
     return P, L
 
 
-@pytest.mark.parametrize("fused", [True, False])
-def test_ragged_batched_decode(fused):
+@pytest.mark.parametrize("fused,seed,layers", [
+    (True, 1, (0, 27)), (False, 1, (0, 27)),
+    (True, 0, (9,)), (False, 2, (17,)), (True, 3, (27,)), (True, 4, (2,)),
+])
+def test_ragged_batched_decode(fused, seed, layers):
     """64 sequences, per-sequence P ~ U[64,512], length ~ U[4K,128K] with four
     not yet sliding, W=4096, 28-layer cache; one decode step per sequence on
-    layers 0 and 27 (the far end of the buffer); rows permuted."""
-    seed, W, hq, hkv, d, base = 1, 4096, 16, 8, 128, 1e6
+    the listed layers (27 is the far end of the buffer); rows permuted.
+    Seeds 0-4 (each seed draws its own P and L)."""
+    W, hq, hkv, d, base = 4096, 16, 8, 128, 1e6
     P, L = ragged_batch(seed, 64, W)
-    rows = np.random.default_rng(7).permutation(64)
-    note(f"ragged decode fused={fused}")
+    rows = np.random.default_rng(7 + seed).permutation(64)
+    note(f"ragged decode fused={fused} seed={seed}")
     c = ps.Cache(28, 64, hq, hkv, d, 512, W, DT_BF16)
     scale = 1.0 / math.sqrt(d)
-    for layer in (0, 27):
+    for layer in layers:
         for s in range(64):
             fill_retained(ps, c, layer, int(rows[s]), int(P[s]), W, int(L[s]) - 2, seed, s, hkv, d, base,
                           DT_BF16)

@@ -281,17 +281,35 @@ def test_tile_class_matches_attention_support():
         keep = []
         for kt in range(0, L, B):
             c = oracle.tile_class(i0, i1, kt, kt + B - 1, P, W)
-            for i in range(i0, i1 + 1):
-                vis = [oracle.visible(i, j, P, W) for j in range(kt, kt + B)]
-                if c == oracle.SKIP:
-                    assert not any(vis)
-                elif c == oracle.FULL:
-                    assert all(vis)
             if c != oracle.SKIP:
                 keep.extend(range(kt, kt + B))
         a, _ = oracle.attention(q[i0:i1 + 1], pos[i0:i1 + 1], k, v, pos, P, W)
         b, _ = oracle.attention(q[i0:i1 + 1], pos[i0:i1 + 1], k[keep], v[keep], pos[keep], P, W)
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("P,W,L", [(12, 20, 96), (0, 7, 60), (30, 5, 80), (3, 64, 70), (9, 1, 50)])
+def test_tile_class_both_ways_against_cache_simulation(P, W, L):
+    """Every class in both directions, against the process simulation of the
+    pages' cache (not the oracle's own rule): SKIP iff no (query, key) pair of
+    the tile is retained, FULL iff every pair is, MASKED iff some are and some
+    are not.  Tiles of several shapes and unaligned offsets."""
+    retained = simulate_retained(L, P, W)
+    rng = np.random.default_rng(P * 1000 + W)
+    seen = collections.Counter()
+    tiles = [(i0, bi, j0, bj) for bi in (1, 4, 8) for bj in (1, 5, 8)
+             for i0 in range(0, L - bi + 1, bi) for j0 in range(0, L - bj + 1, bj)]
+    tiles += [tuple(int(x) for x in (rng.integers(0, L - 10), rng.integers(1, 11),
+                                     rng.integers(0, L - 10), rng.integers(1, 11))) for _ in range(300)]
+    for i0, bi, j0, bj in tiles:
+        i1, j1 = i0 + bi - 1, j0 + bj - 1
+        n_vis = sum(j in retained[i] for i in range(i0, i1 + 1) for j in range(j0, j1 + 1))
+        expect = oracle.SKIP if n_vis == 0 else (oracle.FULL if n_vis == bi * bj else oracle.MASKED)
+        got = oracle.tile_class(i0, i1, j0, j1, P, W)
+        assert got == expect, (i0, i1, j0, j1, n_vis)
+        seen[got] += 1
+    # the sample exercises every class
+    assert seen[oracle.SKIP] and seen[oracle.FULL] and seen[oracle.MASKED], seen
 
 
 # ------------------------------------------------------------- generator
