@@ -141,7 +141,8 @@ enum ps_check_flag {
     PS_CHECK_DUPLICATE_ROW = 1u << 1,  /* two sequences of one call on the same row */
     PS_CHECK_PREFIX_BLOCK = 1u << 2,   /* a prefix block outside [0, prefix_blocks) */
     PS_CHECK_PREFIX_LEN = 1u << 3,     /* a prefix length outside [0, prefix_cap] */
-    PS_CHECK_POSITION = 1u << 4,       /* a negative position */
+    PS_CHECK_POSITION = 1u << 4,       /* a position below 0, or one whose call
+                                          reaches past 2^62 */
     PS_CHECK_SEQUENCE = 1u << 5,       /* a position that does not continue its row */
     PS_CHECK_SHARED_PREFIX = 1u << 6   /* one prefix block with two prefix lengths */
 };
@@ -241,8 +242,12 @@ int ps_kv_rerotate(ps_cache* cache, int32_t layer, const ps_seq_batch* batch, in
  * given (ragged chunks of a continuous batch): then sequence b's chunk starts
  * at starts[b] and its prefix length is prefix_lens[b] (or P when
  * prefix_lens is NULL).  Device-side preconditions of ragged chunks (not
- * checked): 0 <= starts[b], starts[b] + seq_len < 2^31, 0 <= prefix_lens[b]
- * (<= prefix_cap in cache mode).  Query i of the chunk attends to the visible
+ * checked): 0 <= starts[b] <= 2^62 - seq_len, 0 <= prefix_lens[b] (<=
+ * prefix_cap in cache mode).  Positions may take any value up to 2^62 (the
+ * chunk of a trace of any length): the kernels handle a chunk's positions in
+ * 32 bits in a frame of its own (counted from the chunk start in trainer
+ * mode; positions past the prefix moved down together in cache mode), which
+ * changes no visibility decision.  Query i of the chunk attends to the visible
  * keys among
  *   - the cached prefix rows [0, min(P, start_pos))          (cache mode)
  *   - the cached ring rows holding positions
@@ -296,7 +301,10 @@ typedef struct {
  * within the dtype's tolerance, far slower.
  * Errors of ps_prefill_attn: PS_ERR_INVALID (NULL or inconsistent arguments,
  * scale <= 0 or not finite), PS_ERR_UNSUPPORTED (head_dim other than 64 or
- * 128, a dtype other than bf16 / fp32, a chunk reaching position 2^31),
+ * 128, a dtype other than bf16 / fp32, start_pos + seq_len above 2^62, and
+ * -- the kernels' 32-bit frame -- in cache mode prefix_cap + W + seq_len
+ * >= 2^31 for ragged chunks, min(start_pos, P + W) + seq_len >= 2^31 for
+ * uniform ones),
  * PS_ERR_HIP. */
 
 int ps_prefill_attn(const ps_prefill_args* args, void* stream);
@@ -324,7 +332,8 @@ int ps_prefill_attn(const ps_prefill_args* args, void* stream);
  * Errors: PS_ERR_INVALID (NULL pointer, batch < 1, seq_len < 0, start_pos < 0,
  * prefix_len < 0, window < 1, n_q_heads not a multiple of n_kv_heads, scale
  * <= 0 or not finite), PS_ERR_UNSUPPORTED (dtype other than bf16, head_dim
- * other than 128, another GQA group, positions reaching 2^31), PS_ERR_HIP. */
+ * other than 128, another GQA group, start_pos + seq_len above 2^62),
+ * PS_ERR_HIP. */
 typedef struct {
     int32_t batch;          /* B >= 1 */
     int32_t seq_len;        /* T >= 0 (0: nothing to do) */

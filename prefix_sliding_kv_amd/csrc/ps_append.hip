@@ -184,7 +184,8 @@ __global__ void __launch_bounds__(256) check_kernel(CheckParams p) {
         if (!row_ok) f |= PS_CHECK_ROW;
         if (pr < 0 || pr >= p.prefix_blocks) f |= PS_CHECK_PREFIX_BLOCK;
         if (P < 0 || P > p.pcap) f |= PS_CHECK_PREFIX_LEN;
-        if (pos < 0) f |= PS_CHECK_POSITION;
+        // positions run up to 2^62 (far from int64 overflow of pos + length)
+        if (pos < 0 || pos > ((int64_t)1 << 62) - p.n_new) f |= PS_CHECK_POSITION;
         for (int o = 0; o < b; ++o) {
             const int32_t orow = p.rows[o];
             if (orow == row) f |= PS_CHECK_DUPLICATE_ROW;

@@ -10,6 +10,9 @@
 namespace {
 
 constexpr size_t kAlign = 256;
+// Largest position any call accepts: positions and position + length stay
+// far from int64 overflow.
+constexpr int64_t kMaxPos = (int64_t)1 << 62;
 constexpr float kLog2e = 1.4426950408889634f;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -348,8 +351,7 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
         return PS_ERR_INVALID;
     if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
     if (a->prefix_lens && !a->starts) return PS_ERR_INVALID;
-    // positions are handled as 32-bit tile-relative offsets inside the kernel
-    if (a->start_pos + (int64_t)a->seq_len >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
+    if (a->start_pos > kMaxPos - a->seq_len) return PS_ERR_UNSUPPORTED;
     int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim, dtype = a->dtype;
     const ps_cache* c = a->cache;
     if (c) {
@@ -371,6 +373,17 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     ps::PrefillParams p{};
     const int64_t P = a->prefix_len, W = a->window, S = a->start_pos, T = a->seq_len;
     const bool ragged = a->starts != nullptr;
+    // The kernels work on positions moved into the chunk's frame
+    // (ps::pos_frame), in 32 bits: every position there is below T (trainer
+    // mode) or min(S, P + W) + T (cache mode, P <= prefix_cap).  Ragged
+    // chunks are moved on the device.
+    const ps::PosFrame fr = ps::pos_frame(S, T, P, W, c == nullptr);
+    const int64_t lim = (int64_t)1 << 31;
+    if (ragged) {
+        if (c && (int64_t)c->desc.prefix_cap + W + T >= lim) return PS_ERR_UNSUPPORTED;
+    } else if (S - fr.shift + T >= lim) {
+        return PS_ERR_UNSUPPORTED;
+    }
     int nr = 0;
     if (c) {
         ps::PrefillCache& pc = p.cache;
@@ -390,7 +403,7 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
         if (!ragged) nr = ps::cache_key_runs(pc, S, P, p.runs);
         if (c->checks) {
             const int st = run_checks(c, a->layer, a->rows, a->prefix_rows, ragged ? a->prefix_lens : nullptr,
-                                      a->starts, P, S, a->batch, 0, ps::kCheckNext, stream);
+                                      a->starts, P, S, a->batch, a->seq_len, ps::kCheckNext, stream);
             if (st != PS_OK) return st;
             p.guard = c->check_flags;
         }
@@ -411,9 +424,16 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     p.seq_len = a->seq_len;
     p.hq = hq;
     p.hkv = hkv;
-    p.start_pos = S;
-    p.P = P;
-    p.W = W;
+    if (ragged) {  // each sequence's frame is taken on the device
+        p.start_pos = S;
+        p.P = P;
+        p.W = W;
+    } else {
+        ps::frame_runs(fr, p.runs, nr);
+        p.start_pos = S - fr.shift;
+        p.P = fr.P;
+        p.W = fr.W;
+    }
     p.q = a->q;
     p.out = a->out;
     p.lse = a->lse;
@@ -433,7 +453,10 @@ int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) {
     if (a->dtype != PS_BF16 || d != 128) return PS_ERR_UNSUPPORTED;
     const int group = hq / hkv;
     if (group < 1 || group > 8) return PS_ERR_UNSUPPORTED;
-    if (a->start_pos + (int64_t)a->seq_len >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
+    if (a->start_pos > kMaxPos - a->seq_len) return PS_ERR_UNSUPPORTED;
+    // positions in the chunk's frame (ps::pos_frame: counted from the chunk
+    // start) are 32-bit in the kernels
+    const ps::PosFrame fr = ps::pos_frame(a->start_pos, a->seq_len, a->prefix_len, a->window, true);
     // byte offsets of rows inside one sequence (plus one 64-row sub-tile past
     // its end) are 32-bit in the kernels
     if (((int64_t)a->seq_len + 64) * hq * d * 2 >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
@@ -448,7 +471,7 @@ int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) {
     r.seq_stride = T * hkv * d;
     r.head_stride = d;
     r.row_stride = (int64_t)hkv * d;
-    r.pos0 = a->start_pos;
+    r.pos0 = a->start_pos - fr.shift;
     r.n = T;
     r.rows = nullptr;
     p.f.n_runs = 1;
@@ -456,9 +479,9 @@ int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) {
     p.f.seq_len = a->seq_len;
     p.f.hq = hq;
     p.f.hkv = hkv;
-    p.f.start_pos = a->start_pos;
-    p.f.P = a->prefix_len;
-    p.f.W = a->window;
+    p.f.start_pos = a->start_pos - fr.shift;
+    p.f.P = fr.P;
+    p.f.W = fr.W;
     p.f.q = a->q;
     p.f.out = const_cast<void*>(a->out);
     p.f.lse = nullptr;

@@ -244,8 +244,56 @@ struct PrefillParams {
     const uint32_t* guard;  // checks on: the cache's flag word; the kernel does nothing while it is set
 };
 
-// Key runs of sequence b and its chunk start / prefix length.
-__device__ inline int seq_key_runs(const PrefillParams& p, int b, int64_t S, int64_t P, KeyRun* out) {
+// Positions enter the visibility rule only through j < P and i - W < j <= i,
+// so a chunk of queries at [S, S + T) gets the same decisions from smaller
+// numbers (its "frame"):
+//   * trainer mode (the chunk's own keys only): every position is counted
+//     from S, P becomes P - S clamped to [0, T] and W is clamped to T
+//     (a window longer than the chunk already holds every earlier key);
+//   * cache mode (keys are the retained ones, all in [0, S + T)): P and W
+//     beyond S + T decide nothing and are clamped to it, and when the chunk
+//     starts more than P + W tokens in, every position >= P moves down by
+//     S - W - P; differences between those positions are kept, every moved
+//     key stays at or above P, and each prefix key stays visible to every
+//     query, as it was.
+// Afterwards every position is below T (trainer) or min(S, P + W) + T
+// (cache), so a kernel may handle a chunk's positions in 32 bits at any
+// trace length.
+struct PosFrame {
+    int64_t P, W;
+    int64_t shift;     // subtracted from every position >= move_from
+    int64_t move_from;
+};
+__host__ __device__ inline PosFrame pos_frame(int64_t S, int64_t T, int64_t P, int64_t W, bool chunk_only) {
+    PosFrame f;
+    if (chunk_only) {
+        const int64_t p = P - S;
+        f.P = p < 0 ? 0 : (p > T ? T : p);
+        f.W = W < T ? W : T;
+        f.shift = S;
+        f.move_from = 0;
+        return f;
+    }
+    const int64_t end = S + T;
+    f.P = P < end ? P : end;
+    f.W = W < end ? W : end;
+    const int64_t sh = S - f.W - f.P;
+    f.shift = sh > 0 ? sh : 0;
+    f.move_from = f.P;
+    return f;
+}
+// Move the runs' positions into the frame.
+__host__ __device__ inline void frame_runs(const PosFrame& f, KeyRun* runs, int n) {
+    for (int r = 0; r < n; ++r)
+        if (runs[r].pos0 >= f.move_from) runs[r].pos0 -= f.shift;
+}
+
+// Key runs of sequence b, with positions in the frame f of its chunk start S
+// and prefix length P (S and P as the caller gave them: the ring slots follow
+// from those).  Uniform chunks arrive with runs and positions the host
+// already moved (their frame on the device is then the identity).
+__device__ inline int seq_key_runs(const PrefillParams& p, int b, int64_t S, int64_t P, const PosFrame& f,
+                                   KeyRun* out) {
     if (!p.starts) {
         for (int r = 0; r < p.n_runs; ++r) out[r] = p.runs[r];
         return p.n_runs;
@@ -253,6 +301,7 @@ __device__ inline int seq_key_runs(const PrefillParams& p, int b, int64_t S, int
     const int nr = p.cache_mode ? cache_key_runs(p.cache, S, P, out) : 0;
     out[nr] = p.runs[0];
     out[nr].pos0 = S;
+    frame_runs(f, out, nr + 1);
     return nr + 1;
 }
 hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParams& p,

@@ -328,18 +328,21 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     const int work = xcd_remap((int)blockIdx.x, n_qt * p.hkv * p.batch);
     const int qt = work % n_qt, g = (work / n_qt) % p.hkv, b = work / (n_qt * p.hkv);
 
-    // Positions are below 2^31 (the host rejects larger ones), so they are
-    // handled in 32 bits; P and W are clamped to 2^31 - 1, which changes no
-    // visibility decision for such positions.
-    // chunk start and prefix length of this sequence
-    const int64_t S = p.starts ? p.starts[b] : p.start_pos;
-    const int64_t Pb = p.plens ? (int64_t)p.plens[b] : p.P;
+    // Chunk start and prefix length of this sequence, in the frame of its
+    // chunk (pos_frame; the host moved uniform chunks already): there every
+    // position is below 2^31 (the host checks the bound), so positions are
+    // handled in 32 bits.
+    const int64_t S_abs = p.starts ? p.starts[b] : p.start_pos;
+    const int64_t P_abs = p.plens ? (int64_t)p.plens[b] : p.P;
+    const PosFrame fr = p.starts ? pos_frame(S_abs, p.seq_len, P_abs, p.W, !p.cache_mode)
+                                 : PosFrame{P_abs, p.W, 0, 0};
+    const int64_t S = S_abs - fr.shift, Pb = fr.P;
     const int t0 = qt * QP;                    // first chunk row of the tile
     const int t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
     const int i0 = (int)S + t0;
     const int i1 = (int)S + t_last;
-    const int P32 = Pb > 0x7FFFFFFF ? 0x7FFFFFFF : (int)Pb;
-    const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
+    const int P32 = (int)Pb;
+    const int w32 = (int)fr.W;
     const float c = p.scale_log2;                              // > 0 (checked on the host)
 
     // this lane's query: stacked row 32*wave + col.  G is the layout's head
@@ -365,8 +368,8 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     __shared__ RunView views[kMaxRuns];
     __shared__ KeyRun s_runs[kMaxRuns];
     if (tid == 0) {
-        const int n_runs = seq_key_runs(p, b, S, Pb, s_runs);
-        plan_walk<kBNB>(s_runs, n_runs, Pb, p.W, (int64_t)i0, (int64_t)i1, walk);
+        const int n_runs = seq_key_runs(p, b, S_abs, P_abs, fr, s_runs);
+        plan_walk<kBNB>(s_runs, n_runs, Pb, fr.W, (int64_t)i0, (int64_t)i1, walk);
         for (int r = 0; r < n_runs; ++r) {
             const KeyRun& run = s_runs[r];
             const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
@@ -598,8 +601,11 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
     const int qt = blockIdx.x, head = blockIdx.y, b = blockIdx.z;
     const int group = p.hq / p.hkv;
     const int g = head / group;
-    const int64_t S = p.starts ? p.starts[b] : p.start_pos;
-    const int64_t Pb = p.plens ? (int64_t)p.plens[b] : p.P;
+    const int64_t S_abs = p.starts ? p.starts[b] : p.start_pos;
+    const int64_t P_abs = p.plens ? (int64_t)p.plens[b] : p.P;
+    const PosFrame fr = p.starts ? pos_frame(S_abs, p.seq_len, P_abs, p.W, !p.cache_mode)
+                                 : PosFrame{P_abs, p.W, 0, 0};
+    const int64_t S = S_abs - fr.shift, Pb = fr.P, Wb = fr.W;
     const int64_t t0 = (int64_t)qt * 64;
     const int64_t t_last = (t0 + 64 < p.seq_len ? t0 + 64 : p.seq_len) - 1;
     const int64_t i0 = S + t0, i1 = S + t_last;
@@ -616,7 +622,7 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
     float m_run = -INFINITY, l_run = 0.f;
 
     __shared__ KeyRun s_runs[kMaxRuns];
-    if (tid == 0) plan_walk<kBN>(s_runs, seq_key_runs(p, b, S, Pb, s_runs), Pb, p.W, i0, i1, walk);
+    if (tid == 0) plan_walk<kBN>(s_runs, seq_key_runs(p, b, S_abs, P_abs, fr, s_runs), Pb, Wb, i0, i1, walk);
     __syncthreads();
     for (int rr = 0; rr < walk.n_ranges; ++rr) {
         const KeyRun& run = s_runs[walk.run[rr]];
@@ -627,7 +633,7 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
             const int64_t row0 = (int64_t)tile * kBN;
             const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
             const int64_t j0 = run.pos0 + row0;
-            const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j0 + nrows - 1, Pb, p.W);
+            const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j0 + nrows - 1, Pb, Wb);
             if (cls == kSkip) continue;
             for (int pass = 0; pass < 2; ++pass) {
                 float tmax = -INFINITY;
@@ -645,7 +651,7 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
                         const int64_t row = half * BR + r;
                         float acc = 0.f;
                         for (int e = 0; e < D; ++e) acc = fmaf(q[e], ks[r][e], acc);
-                        if (cls == kMasked && (row >= nrows || !visible(my_i, j0 + row, Pb, p.W))) acc = -INFINITY;
+                        if (cls == kMasked && (row >= nrows || !visible(my_i, j0 + row, Pb, Wb))) acc = -INFINITY;
                         if (pass == 0) {
                             tmax = fmaxf(tmax, acc);
                         } else {

@@ -134,7 +134,8 @@ def test_prefill_validation():
     assert call(scale=float("nan")) == ps.PS_ERR_INVALID
     assert call(scale=0.0) == ps.PS_ERR_INVALID
     assert call(scale=-0.1) == ps.PS_ERR_INVALID
-    assert call(start_pos=2**31 - 2, seq_len=4) == ps.PS_ERR_UNSUPPORTED  # positions are 32-bit in the kernel
+    assert call(start_pos=2**62 - 2, seq_len=4) == ps.PS_ERR_UNSUPPORTED  # positions end at 2^62
+    assert call(start_pos=2**40, seq_len=4) == ps.PS_ERR_INVALID      # past 2^31 is fine (null tensors)
     assert call(prefix_lens=8) == ps.PS_ERR_INVALID            # per-sequence P only with per-sequence starts
 
 
@@ -160,7 +161,7 @@ def test_prefill_bwd_rejects_bad_arguments_before_any_launch():
     assert call(dtype=ps.PS_F32) == ps.PS_ERR_UNSUPPORTED
     assert call(head_dim=64) == ps.PS_ERR_UNSUPPORTED
     assert call(n_q_heads=32, n_kv_heads=2) == ps.PS_ERR_UNSUPPORTED  # GQA 16
-    assert call(start_pos=(1 << 31) - 8) == ps.PS_ERR_UNSUPPORTED
+    assert call(start_pos=(1 << 62) - 8) == ps.PS_ERR_UNSUPPORTED  # positions end at 2^62
     assert call(dv=0) == ps.PS_ERR_INVALID
     assert call(delta=0) == ps.PS_ERR_INVALID
     # nothing to do: no pointer is touched
@@ -221,3 +222,53 @@ def test_header_is_plain_c_and_links(tmp_path, compiler, std):
     assert int(nbytes) == ps.ps_cache_bytes(ps.CacheDesc(28, 1, 16, 8, 128, 100, 4096, ps.PS_BF16, 0))
     assert int(status) == ps.PS_ERR_INVALID and text == ps.ps_status_str(ps.PS_ERR_INVALID)
     assert int(cls) == ps.ps_tile_class(100, 227, 0, 63, 100, 4096)
+
+
+def test_position_frame_keeps_every_visibility_decision(tmp_path):
+    """The prefill kernels take a chunk's positions in 32 bits, moved into a
+    frame of the chunk (the library's pos_frame).  For random chunks at
+    positions up to 2^62, every (query, key) pair the chunk can meet keeps
+    the oracle's visibility decision after the move, and every moved
+    position fits the bound the host enforces (below T in trainer mode,
+    below min(S, P + W) + T in cache mode)."""
+    import shutil
+    import subprocess
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "frame_cases"
+    r = subprocess.run(["g++", "-std=c++17", "-O1", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include",
+                        os.path.join(ROOT, "tests", "frame_cases.cpp"), "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    rng = random.Random(5)
+    cases = []
+    for _ in range(400):
+        T = rng.randint(1, 40)
+        P = rng.choice([0, rng.randint(0, 30), rng.randint(0, 2**62)])
+        W = rng.choice([1, rng.randint(1, 50), rng.randint(1, 2**62)])
+        S = rng.choice([0, rng.randint(0, 100), rng.randint(2**31 - 50, 2**31 + 50), rng.randint(0, 2**62 - 64)])
+        chunk_only = rng.random() < 0.5
+        if not chunk_only:  # cache mode: P is at most the prefix capacity
+            P = min(P, rng.randint(0, 60))
+            W = min(W, rng.randint(1, 80))
+        cases.append((S, T, P, W, int(chunk_only)))
+    out = subprocess.run([str(exe)], input="".join(f"{' '.join(map(str, c))}\n" for c in cases),
+                         capture_output=True, text=True, timeout=60).stdout.split("\n")
+    for (S, T, P, W, chunk_only), line in zip(cases, out):
+        fP, fW, shift, move_from = map(int, line.split())
+        move = lambda x: x - shift if x >= move_from else x
+        queries = range(S, S + T)
+        if chunk_only:
+            keys = list(range(S, S + T))
+        else:  # the retained keys before the chunk (a sample of the prefix and the window) and the chunk
+            pre = sorted({0, P - 1, P // 2} & set(range(min(S, P))))
+            lo = max(P, S - W)
+            win = sorted({lo, lo + 1, (lo + S) // 2, S - 1} & set(range(lo, S)))
+            keys = pre + win + list(range(S, S + T))
+        for i in queries:
+            for j in keys:
+                assert oracle.visible(i, j, P, W) == oracle.visible(move(i), move(j), fP, fW), \
+                    (S, T, P, W, chunk_only, i, j)
+        bound = T if chunk_only else min(S, P + W) + T
+        assert all(0 <= move(x) < max(bound, 1) for x in list(queries) + keys), (S, T, P, W, chunk_only)
+        assert 0 <= fP <= bound and 1 <= fW <= max(bound, W if not chunk_only else 0), (S, T, P, W, fP, fW)

@@ -69,6 +69,7 @@ def check(name, got, ref):
     (2, 1, 1, 190, 3, 1, 0, 3.0),        # W=1: prefix + self
     (2, 1, 1, 300, 400, 8, 0, 1.0),      # P > T: plain causal
     (4, 2, 1, 290, 30, 50, 1000, 3.0),   # chunk not starting at 0
+    (4, 2, 1, 290, 30, 50, 2**33 + 17, 3.0),  # positions past 2^31
     (2, 1, 1, 1, 0, 5, 0, 1.0),          # single token
     (6, 2, 1, 250, 12, 60, 0, 3.0),      # G=3 on the 4-head layout
     (10, 2, 1, 200, 7, 50, 0, 3.0),      # G=5 on the 8-head layout

@@ -211,3 +211,18 @@ def test_shared_prefix_block_with_two_lengths():
                    lambda: ps.ps_kv_append_evict(c.handle, 0, batch([0, 2], [8, 9], [0, 0], prows=[1, 1]), 1, k,
                                                  k))
     c.close()
+
+
+def test_ragged_chunk_reaching_past_2_62():
+    """A ragged chunk whose device-resident start puts its last token past
+    2^62 (the position domain's end) is flagged and blocked."""
+    note("checks: ragged chunk past 2^62")
+    c = new_cache()
+    q = torch.zeros(1, 8, HQ, D, device="cuda", dtype=torch.bfloat16)
+    kk = torch.zeros(1, 8, HKV, D, device="cuda", dtype=torch.bfloat16)
+    out = torch.full_like(q, 7.0)
+    expect_blocked(c, ps.PS_CHECK_POSITION, lambda: ps.ps_prefill_attn(
+        q, kk, kk, out, start_pos=0, prefix_len=4, window=W, scale=SCALE, cache=c.handle, layer=0,
+        rows=dev([1], torch.int32), starts=dev([2**62 - 4], torch.int64), prefix_lens=dev([4], torch.int32)))
+    assert torch.all(out == 7.0)
+    c.close()
