@@ -359,6 +359,23 @@ typedef struct {
 
 int ps_prefill_attn_bwd(const ps_prefill_bwd_args* args, void* stream);
 
+/* The same trainer backward for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation): identical arguments and results, except that args->delta must
+ * be NULL -- the Delta rows go to a device array the library owns, of
+ * PS_BWD_NOALLOC_MAX_ROWS fp32 rows (16 MiB), one per GPU, held until the
+ * process ends.  The call itself allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine); its first call on a device looks up that
+ * device's copy of the array.  Every call on one GPU shares the array, and
+ * each call overwrites the rows it uses before reading them, so nothing
+ * carries over from an earlier call; calls that overlap on one GPU (streams
+ * not ordered with each other) race on it.
+ * Errors: those of ps_prefill_attn_bwd, PS_ERR_INVALID for a non-NULL delta,
+ * PS_ERR_CAPACITY when batch * seq_len * n_q_heads exceeds
+ * PS_BWD_NOALLOC_MAX_ROWS, PS_ERR_HIP when the array cannot be found. */
+#define PS_BWD_NOALLOC_MAX_ROWS 4194304
+int ps_prefill_attn_bwd_noalloc(const ps_prefill_bwd_args* args, void* stream);
+
 /* Host-side pool of block indices with reference counts: the bookkeeping of
  * the block table.  A serving loop keeps one pool for window blocks (cache
  * rows, size max_seqs) and one for prefix blocks (size prefix_blocks); a

@@ -91,6 +91,7 @@ _SIGS = {
                                       ctypes.c_float, _vp]),
     "ps_prefill_attn": (ctypes.c_int, [ctypes.POINTER(_PrefillArgs), _vp]),
     "ps_prefill_attn_bwd": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), _vp]),
+    "ps_prefill_attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), _vp]),
     "ps_block_pool_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "ps_block_pool_destroy": (ctypes.c_int, [_vp]),
     "ps_block_alloc": (ctypes.c_int, [_vp, ctypes.POINTER(_i32)]),
@@ -318,6 +319,22 @@ def ps_prefill_attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, *, start_pos
                         k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
                         dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), scale)
     _check(lib.ps_prefill_attn_bwd(ctypes.byref(a), _stream(stream)), "ps_prefill_attn_bwd")
+
+
+PS_BWD_NOALLOC_MAX_ROWS = 4194304
+
+
+def ps_prefill_attn_bwd_noalloc(q, k, v, out, lse, dout, dq, dk, dv, *, start_pos: int, prefix_len: int,
+                                window: int, scale: float, stream=None) -> None:
+    """ps_prefill_attn_bwd without a delta workspace: the library keeps the
+    Delta rows in its own device array (B * T * Hq <= PS_BWD_NOALLOC_MAX_ROWS)."""
+    B, T, hq, d = q.shape
+    hkv = k.shape[2]
+    dtype = PS_BF16 if q.dtype == torch.bfloat16 else PS_F32
+    a = _PrefillBwdArgs(B, T, hq, hkv, d, dtype, start_pos, prefix_len, window, q.data_ptr(),
+                        k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), None, scale)
+    _check(lib.ps_prefill_attn_bwd_noalloc(ctypes.byref(a), _stream(stream)), "ps_prefill_attn_bwd_noalloc")
 
 
 class Cache:

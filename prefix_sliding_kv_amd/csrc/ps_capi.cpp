@@ -175,6 +175,70 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     return hip_status(ps::launch_decode(c->desc.dtype, c->desc.head_dim, group, rows, p, (hipStream_t)stream));
 }
 
+// Trainer backward: validation, then Delta, dK/dV and dQ on `stream`.  With
+// own_delta the Delta rows go to the library's own device array (the
+// allocation-free entry point) and args->delta must be NULL.
+int bwd_common(const ps_prefill_bwd_args* a, bool own_delta, void* stream) {
+    if (!a) return PS_ERR_INVALID;
+    if (own_delta && a->delta) return PS_ERR_INVALID;
+    if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1)
+        return PS_ERR_INVALID;
+    if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
+    const int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim;
+    if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
+    if (a->dtype != PS_BF16 || d != 128) return PS_ERR_UNSUPPORTED;
+    const int group = hq / hkv;
+    if (group < 1 || group > 8) return PS_ERR_UNSUPPORTED;
+    if (a->start_pos > kMaxPos - a->seq_len) return PS_ERR_UNSUPPORTED;
+    // positions in the chunk's frame (ps::pos_frame: counted from the chunk
+    // start) are 32-bit in the kernels
+    const ps::PosFrame fr = ps::pos_frame(a->start_pos, a->seq_len, a->prefix_len, a->window, true);
+    // byte offsets of rows inside one sequence (plus one 64-row sub-tile past
+    // its end) are 32-bit in the kernels
+    if (((int64_t)a->seq_len + 64) * hq * d * 2 >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
+    if (own_delta && (int64_t)a->batch * a->seq_len * hq > PS_BWD_NOALLOC_MAX_ROWS) return PS_ERR_CAPACITY;
+    if (a->seq_len == 0) return PS_OK;
+    if (!a->q || !a->k || !a->v || !a->out || !a->lse || !a->dout || !a->dq || !a->dk || !a->dv ||
+        (!own_delta && !a->delta))
+        return PS_ERR_INVALID;
+    float* delta = own_delta ? ps::static_delta() : a->delta;
+    if (!delta) return PS_ERR_HIP;
+    ps::BwdParams p{};
+    const int64_t T = a->seq_len;
+    ps::KeyRun& r = p.f.runs[0];
+    r.k = a->k;
+    r.v = a->v;
+    r.seq_stride = T * hkv * d;
+    r.head_stride = d;
+    r.row_stride = (int64_t)hkv * d;
+    r.pos0 = a->start_pos - fr.shift;
+    r.n = T;
+    r.rows = nullptr;
+    p.f.n_runs = 1;
+    p.f.batch = a->batch;
+    p.f.seq_len = a->seq_len;
+    p.f.hq = hq;
+    p.f.hkv = hkv;
+    p.f.start_pos = a->start_pos - fr.shift;
+    p.f.P = fr.P;
+    p.f.W = fr.W;
+    p.f.q = a->q;
+    p.f.out = const_cast<void*>(a->out);
+    p.f.lse = nullptr;
+    p.f.scale_log2 = a->scale * kLog2e;
+    p.dout = a->dout;
+    p.lse = a->lse;
+    p.delta_out = delta;
+    p.delta = delta;
+    p.dq = a->dq;
+    p.dk = a->dk;
+    p.dv = a->dv;
+    p.k = a->k;
+    p.v = a->v;
+    p.scale = a->scale;
+    return hip_status(ps::launch_prefill_bwd(group, p, (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -443,61 +507,9 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     return hip_status(ps::launch_prefill(dtype, d, group, p, (hipStream_t)stream));
 }
 
-int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) {
-    if (!a) return PS_ERR_INVALID;
-    if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1)
-        return PS_ERR_INVALID;
-    if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
-    const int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim;
-    if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
-    if (a->dtype != PS_BF16 || d != 128) return PS_ERR_UNSUPPORTED;
-    const int group = hq / hkv;
-    if (group < 1 || group > 8) return PS_ERR_UNSUPPORTED;
-    if (a->start_pos > kMaxPos - a->seq_len) return PS_ERR_UNSUPPORTED;
-    // positions in the chunk's frame (ps::pos_frame: counted from the chunk
-    // start) are 32-bit in the kernels
-    const ps::PosFrame fr = ps::pos_frame(a->start_pos, a->seq_len, a->prefix_len, a->window, true);
-    // byte offsets of rows inside one sequence (plus one 64-row sub-tile past
-    // its end) are 32-bit in the kernels
-    if (((int64_t)a->seq_len + 64) * hq * d * 2 >= ((int64_t)1 << 31)) return PS_ERR_UNSUPPORTED;
-    if (a->seq_len == 0) return PS_OK;
-    if (!a->q || !a->k || !a->v || !a->out || !a->lse || !a->dout || !a->dq || !a->dk || !a->dv || !a->delta)
-        return PS_ERR_INVALID;
-    ps::BwdParams p{};
-    const int64_t T = a->seq_len;
-    ps::KeyRun& r = p.f.runs[0];
-    r.k = a->k;
-    r.v = a->v;
-    r.seq_stride = T * hkv * d;
-    r.head_stride = d;
-    r.row_stride = (int64_t)hkv * d;
-    r.pos0 = a->start_pos - fr.shift;
-    r.n = T;
-    r.rows = nullptr;
-    p.f.n_runs = 1;
-    p.f.batch = a->batch;
-    p.f.seq_len = a->seq_len;
-    p.f.hq = hq;
-    p.f.hkv = hkv;
-    p.f.start_pos = a->start_pos - fr.shift;
-    p.f.P = fr.P;
-    p.f.W = fr.W;
-    p.f.q = a->q;
-    p.f.out = const_cast<void*>(a->out);
-    p.f.lse = nullptr;
-    p.f.scale_log2 = a->scale * kLog2e;
-    p.dout = a->dout;
-    p.lse = a->lse;
-    p.delta_out = a->delta;
-    p.delta = a->delta;
-    p.dq = a->dq;
-    p.dk = a->dk;
-    p.dv = a->dv;
-    p.k = a->k;
-    p.v = a->v;
-    p.scale = a->scale;
-    return hip_status(ps::launch_prefill_bwd(group, p, (hipStream_t)stream));
-}
+int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) { return bwd_common(a, false, stream); }
+
+int ps_prefill_attn_bwd_noalloc(const ps_prefill_bwd_args* a, void* stream) { return bwd_common(a, true, stream); }
 
 int ps_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P, int64_t W) {
     if (i1 < i0 || j1 < j0 || P < 0 || W < 1) return -1;

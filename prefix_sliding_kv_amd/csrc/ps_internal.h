@@ -322,5 +322,10 @@ struct BwdParams {
     float scale;
 };
 hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream);
+// The allocation-free backward's Delta rows: a device array of
+// PS_BWD_NOALLOC_MAX_ROWS floats the library owns (one copy per GPU, kept
+// until the process ends).  Returns this device's copy, its address taken
+// once per device, or nullptr if that fails.
+float* static_delta();
 
 }  // namespace ps

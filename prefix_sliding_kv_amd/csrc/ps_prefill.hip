@@ -28,6 +28,8 @@
 // thread per query row with 64-key tiles, the same walk and classification,
 // fp32 arithmetic; it serves fp32 inputs and the bf16 shapes the MFMA kernel
 // is not built for (head_dim 64, GQA groups other than 1, 2, 4, 8).
+#include <mutex>
+
 #include "ps_internal.h"
 
 namespace ps {
@@ -576,6 +578,13 @@ inline bool* lds_flag(int slot) {
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     return &flags[dev][slot];
 }
+
+// Delta rows of the allocation-free backward.  Each GPU holds its own copy of
+// this array at its own address.  On the host the name is only a stand-in
+// (passing it to a kernel would hand the kernel a host address), so host
+// code uses the device address hipGetSymbolAddress returns, taken once per
+// device with that device current.
+static __device__ __align__(256) float scratch[PS_BWD_NOALLOC_MAX_ROWS];
 
 // ----------------------------------------------------------------- plain path
 // One thread per query row of a 64-position tile of one q head; K/V tiles in
@@ -1288,6 +1297,20 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+float* static_delta() {
+    static std::mutex mu;
+    static float* ptr[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* addr = nullptr;
+        if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+        ptr[dev] = static_cast<float*>(addr);
+    }
+    return ptr[dev];
 }
 
 hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream) {
