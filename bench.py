@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the full-attention / vanilla-sliding-window comparison")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--r1-shape", action="store_true",
+                    help="also time the DeepSeek-R1-Distill-Qwen-7B attention shape (GQA 7)")
     return ap.parse_args()
 
 
@@ -224,9 +226,123 @@ def decode_bench(args, torch, ps, synth, np):
              "extra_us_per_layer": round((reset_ms - graph_ms) * 1e3 / LAYERS, 2),
              "turn_bytes_per_layer": W * HKV * D * 2 * 2}
     log(f"reset PE: {reset}")
+    phases = decode_phases(torch, ps, cache, batch, pos_t, q_all, k_all, v_all, out, scale, s_fixed, gstream,
+                           stream)
     cache.close()
     return dict(eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok, mean_launch_us=mean_launch_us,
-                flat=flat, reset_pe=reset)
+                flat=flat, reset_pe=reset, phases=phases)
+
+
+def decode_phases(torch, ps, cache, batch, pos_t, q_all, k_all, v_all, out, scale, s_fixed, gstream, stream):
+    """Phase timeline of the decode kernel in the replayed 28-layer step, from
+    the library's decode trace (s_memrealtime stamps, 10 ns, written by thread
+    0 of every workgroup).  Per launch, each phase ends when its last
+    workgroup passes it; times are from the launch's first workgroup start."""
+    n_wg = 17 * HKV
+    buf = torch.zeros(LAYERS, n_wg, 8, dtype=torch.int64, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    pos_t.fill_(TRACE - 1)
+
+    def traced_step():
+        ps.ps_cache_set_decode_trace(cache.handle, buf, LAYERS, n_wg)  # layer l writes slot l
+        for layer in range(LAYERS):
+            ps.ps_decode_step(cache.handle, layer, batch, q_all[layer][s_fixed:s_fixed + 1],
+                              k_all[layer][s_fixed:s_fixed + 1], v_all[layer][s_fixed:s_fixed + 1],
+                              out[layer], None, scale, gstream)
+
+    with torch.cuda.stream(gstream):
+        traced_step()  # one eager run before capture
+        with torch.cuda.graph(g, stream=gstream):
+            traced_step()
+    ps.ps_cache_set_decode_trace(cache.handle, None)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        pos_t.fill_(TRACE - 1)
+        g.replay()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for _ in range(50):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    traced_us = t0.elapsed_time(t1) / 50 * 1e3 / LAYERS
+    ts = buf.cpu().numpy().astype("float64") / 100.0  # microseconds
+    names = ["metadata in", "K rows scored", "V rows summed", "waves combined", "partial stored + acked",
+             "arrival counted", "merged"]
+    per = {n: [] for n in names}
+    gaps, spans = [], []
+    for layer in range(LAYERS):
+        t = ts[layer]
+        start = t[:, 0].min()
+        for c, n in enumerate(names, start=1):
+            col = t[:, c] if c < 7 else t[t[:, 7] > 0, 7]
+            per[n].append(col.max() - start)
+        spans.append(t[t[:, 7] > 0, 7].max() - start)
+        if layer + 1 < LAYERS:
+            gaps.append(ts[layer + 1][:, 0].min() - t[t[:, 7] > 0, 7].max())
+    med = lambda xs: round(float(sorted(xs)[len(xs) // 2]), 2)
+    res = {"note": "median over the 28 launches of one replayed step; each phase ends when the last workgroup "
+                   "passes it, microseconds from the launch's first workgroup start (s_memrealtime, 10 ns)",
+           "workgroups": n_wg, "phase_end_us": {n: med(v) for n, v in per.items()},
+           "first_start_to_merge_end_us": med(spans), "merge_end_to_next_start_us": med(gaps),
+           "traced_us_per_launch": round(traced_us, 3)}
+    log(f"decode phases: {res}")
+    return res
+
+
+def launch_floor(torch):
+    """The floor of one launch on this GPU, from the probe library (not part of
+    the attention library): an empty launch, and a plain read of 17,186,816
+    bytes (one decode launch's K/V bytes) by 136, 256 and 1024 workgroups, each
+    as 28 dependent launches over 28 distinct buffers replayed from a graph."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(os.path.dirname(os.path.abspath(__file__)), "prefix_sliding_kv_amd",
+                                   "libps_probe.so"))
+    lib.ps_probe_empty.argtypes = [ctypes.c_int32, ctypes.c_void_p]
+    lib.ps_probe_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    nbytes = 2 * HKV * D * (P + W) * 2
+    stride = (nbytes + 4095) // 4096 * 4096
+    src = torch.ones(LAYERS * stride, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1024, dtype=torch.int32, device="cuda")
+    gstream = torch.cuda.Stream()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def per_launch(launch):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(gstream):
+            launch(0)
+            with torch.cuda.graph(g, stream=gstream):
+                for layer in range(LAYERS):
+                    assert launch(layer) == 0
+        torch.cuda.synchronize()
+        for _ in range(20):
+            g.replay()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(200):
+            g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / 200 * 1e3 / LAYERS
+
+    res = {"bytes_per_launch": nbytes}
+    h = lambda: ctypes.c_void_p(gstream.cuda_stream)
+    res["empty_launch_us"] = round(per_launch(lambda l: lib.ps_probe_empty(136, h())), 3)
+    reads = {}
+    for n_wg in (136, 256, 1024):
+        us = per_launch(lambda l, n=n_wg: lib.ps_probe_stream_read(ctypes.c_void_p(src.data_ptr() + l * stride),
+                                                                     nbytes, n, ctypes.c_void_p(sink.data_ptr()),
+                                                                     h()))
+        reads[str(n_wg)] = {"us_per_launch": round(us, 3), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 /
+                                                                              HBM_PEAK_GBS, 4)}
+    res["stream_read"] = reads
+    best = min(r["us_per_launch"] for r in reads.values())
+    res["best_read_tok_s"] = round(1e6 / (best * LAYERS), 1)
+    log(f"launch floor: {res}")
+    del src
+    return res
 
 
 def baselines_bench(torch, ps):
@@ -743,6 +859,7 @@ def main():
     copy_gbs = copy_bandwidth(torch, calib_src, calib_dst)
     del calib_src, calib_dst
     dec = decode_bench(args, torch, ps, synth, np)
+    floor = launch_floor(torch)
     bytes_per_launch = 2 * HKV * D * (P + W) * 2
     achieved = bytes_per_launch / (dec["mean_launch_us"] * 1e-6) / 1e9
     traffic = decode_traffic()
@@ -752,7 +869,7 @@ def main():
     base_cmp = {} if args.no_baselines else baselines_bench(torch, ps)
     batched = {} if args.no_baselines else batched_bench(torch, ps, np)
     rollouts = {} if args.no_baselines else rollouts_bench(torch, ps, np)
-    r1 = {} if args.no_prefill else r1_distill_bench(torch, ps, np)
+    r1 = r1_distill_bench(torch, ps, np) if args.r1_shape else {}
     cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
     line = {
         "metric": METRIC,
@@ -777,6 +894,8 @@ def main():
                      "bytes_per_launch": bytes_per_launch, "mean_launch_us": round(dec["mean_launch_us"], 3),
                      "launch_timing": "HIP events around the hipGraph replay of 28 decode launches, / 28"},
         "step_hbm_frac": round(bytes_per_launch * LAYERS / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "decode_phases": dec["phases"],
+        "launch_floor": floor,
         "eager_tok_s": round(1e3 / dec["eager_ms"], 1),
         "flat_cost_tok_s": dec["flat"],
         "reset_pe": dec["reset_pe"],
@@ -784,7 +903,7 @@ def main():
         "baselines": base_cmp,
         "batched_decode": batched,
         "rollouts_decode": rollouts,
-        "r1_distill_qwen7b_shape": r1,
+        "r1_distill_qwen7b_shape": r1 or None,
         "hbm_copy": {"gbs": round(copy_gbs, 1),
                      "note": "device-to-device copy of 256 MiB, read + write bytes / time",
                      "decode_frac_of_copy": round(achieved / copy_gbs, 4),

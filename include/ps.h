@@ -162,6 +162,25 @@ int ps_cache_check_flags(ps_cache* cache, uint32_t* flags, int32_t clear, void* 
  * PS_ERR_UNSUPPORTED (a size the kernel is not built for). */
 int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
 
+/* Decode phase trace, a profiling aid (off by default).  With dev_buf
+ * non-NULL every later decode call on the cache (ps_decode_attn,
+ * ps_decode_step) runs the same decode kernel, at 256 key rows per split and
+ * without the non-temporal hint, with thread 0 of each workgroup writing
+ * s_memrealtime stamps (100 MHz) at eight points: entry, sequence metadata
+ * in, K rows in and scored, V rows summed, waves combined, partial stored and
+ * acknowledged, arrival counted, merge done (the last point is 0 for a
+ * workgroup that did not merge).  The k-th traced call (counted from this
+ * call) writes slot k mod n_launches of dev_buf, a device array
+ * [n_launches][max_wg][8] of uint64 the caller owns; a captured graph keeps
+ * the slot each call had at capture.  The stamps observe the kernel and skip
+ * none of its work; the waits they need cost a little time.  NULL turns the
+ * trace off.  While it is on, decode calls return PS_ERR_UNSUPPORTED for
+ * shapes other than bf16, head_dim 128, GQA 1, 2 or 4 (split size automatic
+ * or 256), or a launch of more than max_wg workgroups.
+ * Errors: PS_ERR_INVALID (NULL cache; n_launches or max_wg < 1 with a
+ * buffer). */
+int ps_cache_set_decode_trace(ps_cache* cache, uint64_t* dev_buf, int32_t n_launches, int32_t max_wg);
+
 /* Append n_new consecutive tokens per sequence to layer `layer`: token t of
  * sequence b has position pos[b] + t.  A position p < P goes to slot p of the
  * sequence's prefix block; p >= P goes to slot (p - P) mod W of its window

@@ -80,6 +80,7 @@ _SIGS = {
                                        ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
     "ps_cache_set_decode_split": (ctypes.c_int, [_vp, _i32]),
     "ps_cache_set_checks": (ctypes.c_int, [_vp, _i32]),
+    "ps_cache_set_decode_trace": (ctypes.c_int, [_vp, _vp, _i32, _i32]),
     "ps_cache_check_flags": (ctypes.c_int, [_vp, ctypes.POINTER(ctypes.c_uint32), _i32, _vp]),
     "ps_kv_append_evict": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, _vp]),
     "ps_kv_append_rope": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_SeqBatch), _i32, _vp, _vp, ctypes.c_float,
@@ -177,6 +178,15 @@ def ps_cache_set_decode_split(handle: int, rows_per_split: int) -> None:
 
 def ps_cache_set_checks(handle: int, on: bool) -> None:
     _check(lib.ps_cache_set_checks(ctypes.c_void_p(handle), int(bool(on))), "ps_cache_set_checks")
+
+
+def ps_cache_set_decode_trace(handle: int, buf, n_launches: int = 1, max_wg: int = 0) -> None:
+    """Decode phase trace on (buf: int64 CUDA tensor [n_launches][max_wg][8]) or off (buf None)."""
+    if buf is None:
+        _check(lib.ps_cache_set_decode_trace(ctypes.c_void_p(handle), None, 0, 0), "ps_cache_set_decode_trace")
+        return
+    _check(lib.ps_cache_set_decode_trace(ctypes.c_void_p(handle), ctypes.c_void_p(buf.data_ptr()), n_launches,
+                                         max_wg), "ps_cache_set_decode_trace")
 
 
 def ps_cache_check_flags(handle: int, clear: bool = False, stream=None) -> int:

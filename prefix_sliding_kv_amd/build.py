@@ -12,6 +12,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(PKG, "libprefix_sliding.so")
+# measurement probes for bench.py (floor of a launch), kept out of the library
+PROBE_SO = os.path.join(PKG, "libps_probe.so")
 SOURCES = ["ps_capi.cpp", "ps_blocks.cpp", "ps_append.hip", "ps_decode.hip", "ps_prefill.hip"]
 ARCH = os.environ.get("PS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -39,12 +41,12 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = SO + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    subprocess.check_call(cmd)
-    os.replace(tmp, SO)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + ["ps_probe.hip"]))
+    for so, parts in ((SO, objs[:-1]), (PROBE_SO, objs[-1:])):
+        tmp = so + ".tmp"
+        subprocess.check_call([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts])
+        os.replace(tmp, so)
     if verbose:
         print(f"built {SO}")
     return SO

@@ -160,6 +160,16 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     const int st = batch_checks(c, layer, batch, knew ? 1 : 0, knew ? ps::kCheckAppend : ps::kCheckQuery, stream);
     if (st != PS_OK) return st;
     const int group = c->desc.n_q_heads / c->desc.n_kv_heads;
+    if (c->trace) {
+        // traced launches: the 256-row split kernel with phase timestamps
+        if (c->desc.dtype != PS_BF16 || c->desc.head_dim != 128 || (group != 1 && group != 2 && group != 4) ||
+            (c->decode_rows != 0 && c->decode_rows != 256))
+            return PS_ERR_UNSUPPORTED;
+        if (ps::decode_grid(256, p) > c->trace_max_wg) return PS_ERR_UNSUPPORTED;
+        const int64_t slot = c->trace_calls++ % c->trace_launches;
+        p.trace = c->trace + (size_t)slot * c->trace_max_wg * ps::kDecodeTracePoints;
+        return hip_status(ps::launch_decode_traced(group, p, (hipStream_t)stream));
+    }
     if (c->decode_rows == 0 && c->desc.dtype == PS_BF16 && c->desc.head_dim == 128 && group >= 5) {
         // five or more heads per kv head: the matrix-core kernel (its own
         // split size; measured faster from G = 5 on, 2% slower at G = 4)
@@ -331,6 +341,16 @@ int ps_cache_set_decode_split(ps_cache* c, int32_t rows_per_split) {
     if (!c || rows_per_split < 0) return PS_ERR_INVALID;
     if (rows_per_split != 0 && !decode_rows_ok(c, rows_per_split)) return PS_ERR_UNSUPPORTED;
     c->decode_rows = rows_per_split;
+    return PS_OK;
+}
+
+int ps_cache_set_decode_trace(ps_cache* c, uint64_t* dev_buf, int32_t n_launches, int32_t max_wg) {
+    if (!c) return PS_ERR_INVALID;
+    if (dev_buf && (n_launches < 1 || max_wg < 1)) return PS_ERR_INVALID;
+    c->trace = dev_buf;
+    c->trace_launches = dev_buf ? n_launches : 0;
+    c->trace_max_wg = dev_buf ? max_wg : 0;
+    c->trace_calls = 0;
     return PS_OK;
 }
 

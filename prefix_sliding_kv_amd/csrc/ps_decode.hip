@@ -174,7 +174,12 @@ __device__ inline float rowgroup_max(float x) {
     return x;
 }
 
-template <typename T, int D, int G, int NW, int U, bool NTL>
+// Phase timestamp of a traced launch (thread 0 of each workgroup).
+__device__ inline void trace_mark(const DecodeParams& p, int point) {
+    p.trace[(size_t)blockIdx.x * kDecodeTracePoints + point] = __builtin_amdgcn_s_memrealtime();
+}
+
+template <typename T, int D, int G, int NW, int U, bool NTL, bool TRACE = false>
 __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     constexpr int NT = NW * 64;
     constexpr int VEC = Elem<T>::kPerVec;
@@ -198,6 +203,12 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // the hardware's round-robin deal puts them on one XCD (one L2); measured
     // 3% faster at batch 1 than the (split, kv head, sequence) grid.
     if (p.c.guard && *p.c.guard) return;  // checks on and a check failed
+    if constexpr (TRACE) {
+        if (threadIdx.x == 0) {
+            trace_mark(p, 0);
+            p.trace[(size_t)blockIdx.x * kDecodeTracePoints + 7] = 0;
+        }
+    }
     const int n_groups = p.n_seqs * p.c.hkv;
     const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
     const int g = group % p.c.hkv, b = group / p.c.hkv;
@@ -219,6 +230,12 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     const int64_t n = n_pre + n_ring;
     const int nsplit = (int)((n + R - 1) / R);
     if (split >= nsplit) return;
+    if constexpr (TRACE) {
+        if (tid == 0) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            trace_mark(p, 1);
+        }
+    }
 
     // Key row r of the sequence: r < n_pre is slot r of its prefix block,
     // else slot r - n_pre of its window block.  The choice is one select of a
@@ -274,6 +291,12 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
             s[u][hh] = valid[u] ? t : -INFINITY;
         }
 
+    if constexpr (TRACE) {
+        if (tid == 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            trace_mark(p, 2);
+        }
+    }
     // The split that owns the new token's slot also commits it to the cache
     // (after the loads above, so no wait on them is forced here).
     if (fused && split == 0 && tid < LPR) {
@@ -319,6 +342,9 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) og[hh][e] = rowgroup_sum<LPR>(og[hh][e]);
     }
+    if constexpr (TRACE) {
+        if (tid == 0) trace_mark(p, 3);
+    }
     if (rg == 0) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
@@ -346,6 +372,9 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     }
     __syncthreads();
 
+    if constexpr (TRACE) {
+        if (tid == 0) trace_mark(p, 4);
+    }
     const int64_t ws_head0 = (int64_t)b * p.hq + g * G;
     for (int idx = tid; idx < PAIRS; idx += NT) {
         const int hh = idx / D, dim = idx % D;
@@ -381,6 +410,9 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // device-scope fence would instead write back and invalidate the XCD's
     // whole L2 for every workgroup.
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if constexpr (TRACE) {
+        if (tid == 0) trace_mark(p, 5);
+    }
     __syncthreads();
     if (tid == 0) {
         uint32_t* t = p.tickets + ((int64_t)b * p.c.hkv + g) * kTicketStride;
@@ -389,6 +421,9 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         if (s_last) __hip_atomic_store(t, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
+    if constexpr (TRACE) {
+        if (tid == 0) trace_mark(p, 6);
+    }
     if (!s_last) return;
 
     // Merge the splits.  Thread t owns output (head, dim) = t % PAIRS and the
@@ -467,6 +502,13 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
             T* o = reinterpret_cast<T*>(p.out) + (ws_head0 + hh) * D + dim;
             *o = Elem<T>::from_float(O / L);
             if (p.lse && dim == 0) p.lse[ws_head0 + hh] = (M + log2f(L)) * kLn2;
+        }
+    }
+    if constexpr (TRACE) {
+        __syncthreads();
+        if (tid == 0) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            trace_mark(p, 7);
         }
     }
 }
@@ -812,6 +854,7 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
     constexpr int R = NW * (64 / (D / Elem<T>::kPerVec)) * U;
     const int64_t n_wg = ((p.rows_per_head + R - 1) / R) * (int64_t)p.c.hkv * p.n_seqs;
     if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
+    if (p.trace) return hipErrorNotSupported;  // traced launches: see launch_decode_traced
     hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U, NTL>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
@@ -874,6 +917,22 @@ hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
         hipLaunchKernelGGL(decode_mfma_kernel<true>, dim3((unsigned)n_wg), dim3(kMfWaves * 64), 0, stream, p);
     else
         hipLaunchKernelGGL(decode_mfma_kernel<false>, dim3((unsigned)n_wg), dim3(kMfWaves * 64), 0, stream, p);
+    return hipGetLastError();
+}
+
+int64_t decode_grid(int rows_per_split, const DecodeParams& p) {
+    return ((p.rows_per_head + rows_per_split - 1) / rows_per_split) * (int64_t)p.c.hkv * p.n_seqs;
+}
+
+hipError_t launch_decode_traced(int group, const DecodeParams& p, hipStream_t stream) {
+    const int64_t n_wg = decode_grid(256, p);
+    const dim3 grid((unsigned)n_wg), block(512);
+    switch (group) {
+        case 1: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 1, 8, 8, false, true>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 2, 8, 8, false, true>), grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 4, 8, 8, false, true>), grid, block, 0, stream, p); break;
+        default: return hipErrorNotSupported;
+    }
     return hipGetLastError();
 }
 

@@ -29,6 +29,10 @@ struct ps_cache {
     uint32_t* check_flags = nullptr;  // debug checks: sticky violation bits (own 256-byte line)
     int64_t* next_pos = nullptr;      // debug checks: [L][max_seqs] next position of each row, -1 unknown
     int32_t checks = 0;               // debug checks on
+    uint64_t* trace = nullptr;        // decode phase trace buffer (device), or null: tracing off
+    int32_t trace_launches = 0;       // launch slots in the trace buffer
+    int32_t trace_max_wg = 0;         // workgroups per launch slot
+    int64_t trace_calls = 0;          // decode calls traced so far (selects the slot)
 };
 
 namespace ps {
@@ -118,8 +122,19 @@ struct DecodeParams {
     int32_t s_max;
     int32_t n_seqs;
     int32_t stream_nt;     // nonzero: K/V loads carry the non-temporal hint
+    uint64_t* trace;       // non-null: phase timestamps, kDecodeTracePoints per workgroup
 };
+// Phase timestamps of a traced decode launch (s_memrealtime, 100 MHz), per
+// workgroup: entry, sequence metadata in, K rows in and scored, V rows summed,
+// waves combined, partial stored and acknowledged, arrival counted, merge
+// done (0 unless the workgroup merged).
+constexpr int kDecodeTracePoints = 8;
 
+// Workgroups of a decode launch with rows_per_split rows per split.
+int64_t decode_grid(int rows_per_split, const DecodeParams& p);
+// Traced decode (p.trace set): bf16, head_dim 128, GQA 1, 2 or 4, splits of
+// 256 rows, no non-temporal hint; other shapes return hipErrorNotSupported.
+hipError_t launch_decode_traced(int group, const DecodeParams& p, hipStream_t stream);
 // Launch decode attention; rows_per_split chosen by the caller (host).
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split,
                          const DecodeParams& p, hipStream_t stream);

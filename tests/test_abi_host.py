@@ -272,3 +272,7 @@ def test_position_frame_keeps_every_visibility_decision(tmp_path):
         bound = T if chunk_only else min(S, P + W) + T
         assert all(0 <= move(x) < max(bound, 1) for x in list(queries) + keys), (S, T, P, W, chunk_only)
         assert 0 <= fP <= bound and 1 <= fW <= max(bound, W if not chunk_only else 0), (S, T, P, W, fP, fW)
+
+
+def test_decode_trace_rejects_bad_arguments():
+    assert ps.lib.ps_cache_set_decode_trace(None, None, 0, 0) == ps.PS_ERR_INVALID

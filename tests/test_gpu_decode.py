@@ -400,3 +400,51 @@ def test_flat_cost_once_window_is_full():
         assert np.max(np.abs(dev_to_f32(out)[0] - ref)) <= tol(DT_BF16)
         assert len(oracle.retained_positions(i, P, W)) == P + W
         c.close()
+
+
+def test_decode_trace_observes_without_changing_results():
+    """The decode phase trace (a profiling aid) runs the same kernel: outputs
+    and cache bytes are bit-identical to an untraced step, every workgroup's
+    stamps rise phase by phase, and exactly one workgroup per kv head merges.
+    Shapes the traced kernel is not built for are refused."""
+    seed, P, W, hq, hkv, d, base = 8, 100, 4096, 16, 8, 128, 1e6
+    note("decode trace")
+    c = new_cache(1, 1, hq, hkv, d, P, W, DT_BF16, poison=False)
+    i = 9000
+    fill_retained(ps, c, 0, 0, P, W, i - 1, seed, 0, hkv, d, base, DT_BF16)
+    q = to_dev(gen(seed, synth.Q, 0, 0, [i], hq, d, base, DT_BF16))
+    k = to_dev(gen(seed, synth.K, 0, 0, [i], hkv, d, base, DT_BF16))
+    v = to_dev(gen(seed, synth.V, 0, 0, [i], hkv, d, base, DT_BF16))
+    b = seq_batch(ps, [0], [P], [i])
+    snap = c.buffer.clone()
+    outs, lses, bufs = [], [], []
+    n_wg = 17 * hkv
+    trace = torch.zeros(2, n_wg, 8, dtype=torch.int64, device="cuda")
+    for traced in (False, True):
+        c.buffer.copy_(snap)
+        if traced:
+            ps.ps_cache_set_decode_trace(c.handle, trace, 2, n_wg)
+        out = torch.empty(1, hq, d, device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty(1, hq, device="cuda")
+        ps.ps_decode_step(c.handle, 0, b, q, k, v, out, lse, 1.0 / math.sqrt(d))
+        torch.cuda.synchronize()
+        outs.append(out)
+        lses.append(lse)
+        bufs.append(c.buffer.clone())
+    ps.ps_cache_set_decode_trace(c.handle, None)
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+    assert torch.equal(lses[0], lses[1])
+    assert torch.equal(bufs[0], bufs[1])
+    t = trace[0].cpu().numpy()
+    assert np.all(np.diff(t[:, :7], axis=1) >= 0) and np.all(t[:, 0] > 0)
+    merged = t[:, 7] > 0
+    assert merged.sum() == hkv and np.all(t[merged, 7] >= t[merged, 6])
+    ref, _ = decode_reference(seed, 0, 0, i, P, W, hq, hkv, d, base, DT_BF16)
+    assert np.max(np.abs(dev_to_f32(outs[1])[0] - ref)) <= tol(DT_BF16)
+    c.close()
+    f = new_cache(1, 1, 4, 2, 64, 8, 16, DT_F32)
+    ps.ps_cache_set_decode_trace(f.handle, trace, 1, n_wg)
+    with pytest.raises(ps.PSError):
+        ps.ps_decode_attn(f.handle, 0, seq_batch(ps, [0], [8], [0]), torch.zeros(1, 4, 64, device="cuda"),
+                          torch.empty(1, 4, 64, device="cuda"), None, 0.125)
+    f.close()
