@@ -66,6 +66,8 @@ def parse():
     ap.add_argument("--no-baselines", action="store_true",
                     help="skip the full-attention / vanilla-sliding-window comparison")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-floor", action="store_true",
+                    help="skip the decode phase trace and the launch-floor probes (e.g. under hardware counters)")
     ap.add_argument("--r1-shape", action="store_true",
                     help="also time the DeepSeek-R1-Distill-Qwen-7B attention shape (GQA 7)")
     return ap.parse_args()
@@ -226,8 +228,8 @@ def decode_bench(args, torch, ps, synth, np):
              "extra_us_per_layer": round((reset_ms - graph_ms) * 1e3 / LAYERS, 2),
              "turn_bytes_per_layer": W * HKV * D * 2 * 2}
     log(f"reset PE: {reset}")
-    phases = decode_phases(torch, ps, cache, batch, pos_t, q_all, k_all, v_all, out, scale, s_fixed, gstream,
-                           stream)
+    phases = None if args.no_floor else decode_phases(torch, ps, cache, batch, pos_t, q_all, k_all, v_all, out,
+                                                        scale, s_fixed, gstream, stream)
     cache.close()
     return dict(eager_ms=eager_ms, graph_ms=graph_ms, graph_ok=graph_ok, mean_launch_us=mean_launch_us,
                 flat=flat, reset_pe=reset, phases=phases)
@@ -859,7 +861,7 @@ def main():
     copy_gbs = copy_bandwidth(torch, calib_src, calib_dst)
     del calib_src, calib_dst
     dec = decode_bench(args, torch, ps, synth, np)
-    floor = launch_floor(torch)
+    floor = None if args.no_floor else launch_floor(torch)
     bytes_per_launch = 2 * HKV * D * (P + W) * 2
     achieved = bytes_per_launch / (dec["mean_launch_us"] * 1e-6) / 1e9
     traffic = decode_traffic()
