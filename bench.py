@@ -510,7 +510,95 @@ def rollouts_bench(torch, ps, np):
             "achieved_gbs": round(gbs, 1), "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
         del g
         cache.close()
+    # the same rollouts in the paged layout (128-slot pages): the prompt's
+    # 8 pages shared by all, 32 private window pages each; and 8 problems of
+    # 8 rollouts whose prompts share their first 4 pages (a common system
+    # prompt) and, per problem, the next 4
+    pg, npre, nwin = 128, P // 128, W // 128
+    for name, groups in (("paged_shared_prefix", 1), ("paged_partial_sharing", 8)):
+        n_shared_pages = npre if groups == 1 else 4 + groups * 4
+        n_pages = n_shared_pages + n * nwin
+        cache = ps.Cache(LAYERS, n, HQ, HKV, D, P, W, ps.PS_BF16, page_size=pg, n_pages=n_pages)
+        for layer in range(LAYERS):
+            for t in cache.pages(layer):
+                t.normal_()
+        table = np.zeros((n, npre + nwin), dtype=np.int32)
+        for s_ in range(n):
+            if groups == 1:
+                table[s_, :npre] = np.arange(npre)
+            else:
+                table[s_, :4] = np.arange(4)
+                table[s_, 4:npre] = 4 + (s_ // (n // groups)) * 4 + np.arange(4)
+            table[s_, npre:] = n_shared_pages + s_ * nwin + np.arange(nwin)
+        rows = torch.arange(n, dtype=torch.int32, device="cuda")
+        batch = ps.SeqBatch(rows, torch.full((n,), P, dtype=torch.int32, device="cuda"),
+                            torch.tensor(Ls - 1, dtype=torch.int64, device="cuda"),
+                            page_table=torch.from_numpy(table).cuda())
+        q = torch.randn(LAYERS, n, HQ, D, device="cuda").to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ms = graph_ms_of(torch, lambda st: [ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None,
+                                                              1.0 / math.sqrt(D), st) for layer in range(LAYERS)])
+        row_bytes = 2 * HKV * D * 2
+        uniq = LAYERS * row_bytes * (n_shared_pages * pg + sum(min(W, int(L) - P) for L in Ls))
+        gbs = uniq / (ms * 1e-3) / 1e9
+        res[name] = {"ms_per_step": round(ms, 4), "tok_s": round(n * 1e3 / ms, 1), "unique_bytes_per_step": uniq,
+                     "cache_kv_bytes": LAYERS * row_bytes * n_pages * pg, "achieved_gbs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        cache.close()
     log(f"rollouts of one prompt: {res}")
+    return res
+
+
+def graph_ms_of(torch, launch, reps=20):
+    """ms per replay of a graph capturing launch(stream) (after one eager run)."""
+    stream = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(gs):
+        launch(gs)
+        with torch.cuda.graph(g, stream=gs):
+            launch(gs)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def paged_batch1_bench(torch, ps, np):
+    """The decode metric's shape (batch 1, 28 layers, P=100, W=4096, 128K
+    trace) on the paged layout (128-slot pages, prefix capacity 128, pages
+    in scattered order): attention-only step time beside the block layout's."""
+    pcap, pg = 128, 128
+    res = {"workload": "batch 1, 28 layers, Hq=16, Hkv=8, d=128, P=100, W=4096, query at 131071, attention only"}
+    rng = np.random.default_rng(5)
+    for name in ("block", "paged"):
+        paged = name == "paged"
+        pps = pcap // pg + W // pg
+        cache = (ps.Cache(LAYERS, 1, HQ, HKV, D, pcap, W, ps.PS_BF16, page_size=pg, n_pages=2 * pps) if paged
+                 else ps.Cache(LAYERS, 1, HQ, HKV, D, P, W, ps.PS_BF16))
+        for layer in range(LAYERS):
+            for t in (cache.pages(layer) if paged else cache.blocks(layer)):
+                t.normal_()
+        table = torch.from_numpy(rng.permutation(2 * pps)[:pps].astype(np.int32)[None]).cuda() if paged else None
+        batch = ps.SeqBatch(torch.zeros(1, dtype=torch.int32, device="cuda"),
+                            torch.full((1,), P, dtype=torch.int32, device="cuda"),
+                            torch.full((1,), TRACE - 1, dtype=torch.int64, device="cuda"), page_table=table)
+        q = torch.randn(LAYERS, 1, HQ, D, device="cuda").to(torch.bfloat16)
+        out = torch.empty_like(q)
+        ms = graph_ms_of(torch, lambda st: [ps.ps_decode_attn(cache.handle, layer, batch, q[layer], out[layer], None,
+                                                              1.0 / math.sqrt(D), st) for layer in range(LAYERS)],
+                         reps=100)
+        res[name] = {"ms_per_step": round(ms, 4), "tok_s": round(1e3 / ms, 1),
+                     "us_per_layer": round(ms * 1e3 / LAYERS, 3)}
+        cache.close()
+    log(f"paged layout at batch 1: {res}")
     return res
 
 
@@ -871,6 +959,7 @@ def main():
     base_cmp = {} if args.no_baselines else baselines_bench(torch, ps)
     batched = {} if args.no_baselines else batched_bench(torch, ps, np)
     rollouts = {} if args.no_baselines else rollouts_bench(torch, ps, np)
+    paged1 = {} if args.no_baselines else paged_batch1_bench(torch, ps, np)
     r1 = r1_distill_bench(torch, ps, np) if args.r1_shape else {}
     cpu = None if args.no_cpu else cpu_baseline(np, args.cpu_seconds)
     line = {
@@ -905,6 +994,7 @@ def main():
         "baselines": base_cmp,
         "batched_decode": batched,
         "rollouts_decode": rollouts,
+        "paged_decode_batch1": paged1,
         "r1_distill_qwen7b_shape": r1 or None,
         "hbm_copy": {"gbs": round(copy_gbs, 1),
                      "note": "device-to-device copy of 256 MiB, read + write bytes / time",

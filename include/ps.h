@@ -66,7 +66,22 @@ typedef enum { PS_BF16 = 0, PS_F32 = 1 } ps_dtype;
  * prompt keep one copy of the pinned prefix (the explainer notes the policy
  * is orthogonal to paged memory management and can be combined with it).
  * A sequence's size is bounded by P + W tokens no matter how long the trace
- * grows (njhaofan.com, same section as above). */
+ * grows (njhaofan.com, same section as above).
+ *
+ * Paged layout (page_size > 0): the explainer's remark that the policy sits
+ * on top of paged memory management and combines with it (papers.ananclaw.com,
+ * section "对工程落地的启发"), taken literally.  Each layer then holds one pool
+ * of n_pages pages of page_size slots per kv head, and every sequence names
+ * its pages in a page table: entry j < prefix_cap / page_size is the page of
+ * its prefix slots [j * page_size, (j + 1) * page_size), entry
+ * prefix_cap / page_size + j the page of its window (ring) slots
+ * [j * page_size, (j + 1) * page_size).  Pages are allocated and shared by
+ * the caller (ps_block_pool counts references): sequences whose prompts
+ * begin with the same page_size-aligned run of tokens may point at the same
+ * prefix pages for it, and each keeps private pages for the rest of its
+ * prefix and for its window.  page_size is a power of two >= 128 (the
+ * prefill kernels' key tile) that divides prefix_cap and W, and a sequence
+ * has at most 256 pages (prefix_cap + W <= 256 * page_size). */
 typedef struct {
     int32_t n_layers;       /* >= 1 */
     int32_t max_seqs;       /* >= 1: window blocks (sequence rows) */
@@ -76,7 +91,9 @@ typedef struct {
     int32_t prefix_cap;     /* largest prefix length P any sequence may use, >= 0 */
     int32_t window;         /* W >= 1 */
     int32_t dtype;          /* ps_dtype of K, V, queries and outputs */
-    int32_t prefix_blocks;  /* prefix blocks, >= 0; 0 means max_seqs (one per row) */
+    int32_t prefix_blocks;  /* prefix blocks, >= 0; 0 means max_seqs (one per row); 0 when paged */
+    int32_t page_size;      /* 0: block layout; else slots per page of the paged layout */
+    int32_t n_pages;        /* paged layout: pages in each layer's pool (>= 1), else 0 */
 } ps_cache_desc;
 
 typedef struct ps_cache ps_cache; /* opaque host handle */
@@ -86,7 +103,12 @@ typedef struct ps_cache ps_cache; /* opaque host handle */
  * [0, max_seqs); prefix_rows values in [0, prefix_blocks); 0 <= prefix_len[b]
  * <= prefix_cap; pos[b] >= 0.  Sequences that share a prefix block have the
  * same prefix_len; its rows are appended once (by any one of them) and only
- * read afterwards. */
+ * read afterwards.  Paged layout: page_table is required and prefix_rows
+ * unused; rows still name each sequence's slot in [0, max_seqs) (the debug
+ * checks follow positions per slot); every table entry lies in [0, n_pages);
+ * a page shared by several sequences holds the same prefix tokens for each,
+ * is appended once and only read afterwards; pages of different sequences'
+ * windows are distinct. */
 typedef struct {
     int32_t n;                  /* number of sequences in the call, 1..max_seqs */
     const int32_t* rows;        /* device: window block (cache row) of each sequence */
@@ -96,6 +118,8 @@ typedef struct {
     const int32_t* prefix_rows; /* device: prefix block of each sequence, or NULL:
                                    prefix block = rows[b] (requires prefix_blocks
                                    == max_seqs) */
+    const int32_t* page_table;  /* device [n][prefix_cap / page_size + W / page_size]:
+                                   paged layout only (else NULL) */
 } ps_seq_batch;
 
 /* Bytes of device memory a cache with this shape needs (K and V for every
@@ -115,13 +139,21 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
 /* Free the host handle.  The device buffer stays the caller's.  NULL is a no-op. */
 int ps_cache_destroy(ps_cache* cache);
 
+/* Device addresses of layer `layer`'s K and V page pools in the paged layout:
+ * [n_pages][n_kv_heads][page_size][head_dim] (cache dtype); slot s of a page
+ * holds the prefix or ring slot the page table assigns it.  Errors:
+ * PS_ERR_INVALID (NULL, layer out of range), PS_ERR_UNSUPPORTED (block
+ * layout). */
+int ps_cache_pages(const ps_cache* cache, int32_t layer, void** k_pages, void** v_pages);
+
 /* Device addresses of layer `layer`'s K and V pools.  Layouts (cache dtype):
  *   prefix pools  [prefix_blocks][n_kv_heads][prefix_cap][head_dim]
  *   window pools  [max_seqs][n_kv_heads][window][head_dim]
  * Slot s of a prefix block holds prefix position s; slot r of a window block
  * holds the token at the position p >= P with (p - P) mod W == r that was
  * appended last.  For inspection and snapshot / restore (a plain device copy
- * of the whole buffer restores a cache).  Errors: PS_ERR_INVALID. */
+ * of the whole buffer restores a cache).  Errors: PS_ERR_INVALID,
+ * PS_ERR_UNSUPPORTED (paged layout: see ps_cache_pages). */
 int ps_cache_blocks(const ps_cache* cache, int32_t layer, void** k_prefix, void** v_prefix,
                     void** k_window, void** v_window);
 
@@ -144,7 +176,8 @@ enum ps_check_flag {
     PS_CHECK_POSITION = 1u << 4,       /* a position below 0, or one whose call
                                           reaches past 2^62 */
     PS_CHECK_SEQUENCE = 1u << 5,       /* a position that does not continue its row */
-    PS_CHECK_SHARED_PREFIX = 1u << 6   /* one prefix block with two prefix lengths */
+    PS_CHECK_SHARED_PREFIX = 1u << 6,  /* one prefix block with two prefix lengths */
+    PS_CHECK_PAGE = 1u << 7            /* a page table entry outside [0, n_pages) */
 };
 
 /* Turn the checks on (on != 0) or off.  Errors: PS_ERR_INVALID (NULL). */
@@ -311,6 +344,8 @@ typedef struct {
                                    chunks), or NULL: start_pos for every sequence */
     const int32_t* prefix_lens; /* device [B] prefix length of each sequence, or
                                    NULL: prefix_len; only together with starts */
+    const int32_t* page_table;  /* paged cache: device [B][pages per sequence] page
+                                   table (see ps_seq_batch), else NULL */
 } ps_prefill_args;
 
 /* bf16 with head_dim 128 and a GQA group of 1 to 8 runs on the MFMA kernel

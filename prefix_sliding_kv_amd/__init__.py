@@ -25,7 +25,7 @@ PS_OK, PS_ERR_INVALID, PS_ERR_UNSUPPORTED, PS_ERR_CAPACITY, PS_ERR_HIP = range(5
 PS_BF16, PS_F32 = 0, 1
 # bits of the debug-check flag word (ps_check_flag)
 (PS_CHECK_ROW, PS_CHECK_DUPLICATE_ROW, PS_CHECK_PREFIX_BLOCK, PS_CHECK_PREFIX_LEN, PS_CHECK_POSITION,
- PS_CHECK_SEQUENCE, PS_CHECK_SHARED_PREFIX) = (1 << i for i in range(7))
+ PS_CHECK_SEQUENCE, PS_CHECK_SHARED_PREFIX, PS_CHECK_PAGE) = (1 << i for i in range(8))
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprefix_sliding.so")
@@ -40,12 +40,12 @@ class CacheDesc(ctypes.Structure):
                 ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("prefix_cap", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("prefix_blocks", ctypes.c_int32)]
+                ("prefix_blocks", ctypes.c_int32), ("page_size", ctypes.c_int32), ("n_pages", ctypes.c_int32)]
 
 
 class _SeqBatch(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("rows", ctypes.c_void_p), ("prefix_len", ctypes.c_void_p),
-                ("pos", ctypes.c_void_p), ("prefix_rows", ctypes.c_void_p)]
+                ("pos", ctypes.c_void_p), ("prefix_rows", ctypes.c_void_p), ("page_table", ctypes.c_void_p)]
 
 
 class _PrefillArgs(ctypes.Structure):
@@ -57,7 +57,7 @@ class _PrefillArgs(ctypes.Structure):
                 ("rows", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("scale", ctypes.c_float), ("prefix_rows", ctypes.c_void_p), ("starts", ctypes.c_void_p),
-                ("prefix_lens", ctypes.c_void_p)]
+                ("prefix_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p)]
 
 
 class _PrefillBwdArgs(ctypes.Structure):
@@ -78,6 +78,7 @@ _SIGS = {
     "ps_cache_destroy": (ctypes.c_int, [_vp]),
     "ps_cache_blocks": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                        ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "ps_cache_pages": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
     "ps_cache_set_decode_split": (ctypes.c_int, [_vp, _i32]),
     "ps_cache_set_checks": (ctypes.c_int, [_vp, _i32]),
     "ps_cache_set_decode_trace": (ctypes.c_int, [_vp, _vp, _i32, _i32]),
@@ -243,19 +244,25 @@ class BlockPool:
 class SeqBatch:
     """Device-resident per-sequence metadata: window blocks (cache rows, int32),
     prefix lengths (int32), positions (int64) and optionally prefix blocks
-    (int32; None = each sequence's own row), each a CUDA tensor of length n."""
+    (int32; None = each sequence's own row), each a CUDA tensor of length n;
+    for a paged cache, the page table (int32 [n][pages per sequence])."""
 
     def __init__(self, rows: torch.Tensor, prefix_len: torch.Tensor, pos: torch.Tensor,
-                 prefix_rows: torch.Tensor | None = None):
+                 prefix_rows: torch.Tensor | None = None, page_table: torch.Tensor | None = None):
         assert rows.dtype == torch.int32 and prefix_len.dtype == torch.int32 and pos.dtype == torch.int64
         assert rows.is_cuda and prefix_len.is_cuda and pos.is_cuda
         assert rows.numel() == prefix_len.numel() == pos.numel()
         if prefix_rows is not None:
             assert prefix_rows.dtype == torch.int32 and prefix_rows.is_cuda
             assert prefix_rows.numel() == rows.numel()
+        if page_table is not None:
+            assert page_table.dtype == torch.int32 and page_table.is_cuda and page_table.is_contiguous()
+            assert page_table.dim() == 2 and page_table.shape[0] == rows.numel()
         self.rows, self.prefix_len, self.pos, self.prefix_rows = rows, prefix_len, pos, prefix_rows
+        self.page_table = page_table
         self._c = _SeqBatch(rows.numel(), rows.data_ptr(), prefix_len.data_ptr(), pos.data_ptr(),
-                            prefix_rows.data_ptr() if prefix_rows is not None else None)
+                            prefix_rows.data_ptr() if prefix_rows is not None else None,
+                            page_table.data_ptr() if page_table is not None else None)
 
     @property
     def n(self) -> int:
@@ -294,7 +301,7 @@ def ps_decode_step(handle: int, layer: int, batch: SeqBatch, q, k_new, v_new, ou
 def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: int, scale: float,
                     lse=None, cache: int | None = None, layer: int = 0, rows=None,
                     prefix_rows=None, starts=None, prefix_lens=None, dtype: int | None = None,
-                    stream=None) -> None:
+                    stream=None, page_table=None) -> None:
     """q/out [B][T][Hq][d], k/v [B][T][Hkv][d] CUDA tensors; ``cache`` None means
     trainer mode (self-attention over the given tokens only).  ``starts``
     (int64 [B]) and ``prefix_lens`` (int32 [B]) give ragged chunks: per-sequence
@@ -309,7 +316,8 @@ def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: in
                      out.data_ptr(), lse.data_ptr() if lse is not None else 0, scale,
                      prefix_rows.data_ptr() if prefix_rows is not None else 0,
                      starts.data_ptr() if starts is not None else 0,
-                     prefix_lens.data_ptr() if prefix_lens is not None else 0)
+                     prefix_lens.data_ptr() if prefix_lens is not None else 0,
+                     page_table.data_ptr() if page_table is not None else 0)
     if starts is not None:
         assert starts.dtype == torch.int64 and starts.numel() == B
     if prefix_lens is not None:
@@ -352,9 +360,10 @@ class Cache:
     the library only carves it)."""
 
     def __init__(self, n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window,
-                 dtype=PS_BF16, device="cuda", stream=None, prefix_blocks: int = 0):
+                 dtype=PS_BF16, device="cuda", stream=None, prefix_blocks: int = 0, page_size: int = 0,
+                 n_pages: int = 0):
         self.desc = CacheDesc(n_layers, max_seqs, n_q_heads, n_kv_heads, head_dim, prefix_cap, window, dtype,
-                              prefix_blocks)
+                              prefix_blocks, page_size, n_pages)
         nbytes = ps_cache_bytes(self.desc)
         if nbytes == 0:
             raise PSError(PS_ERR_INVALID, "ps_cache_bytes")
@@ -382,6 +391,28 @@ class Cache:
             out.append(self.buffer[off:off + n * esz].view(self.dtype).view(shape))
         return tuple(out)
 
+    @property
+    def paged(self) -> bool:
+        return self.desc.page_size > 0
+
+    @property
+    def pages_per_seq(self) -> int:
+        d = self.desc
+        return (d.prefix_cap + d.window) // d.page_size if d.page_size else 0
+
+    def pages(self, layer: int):
+        """Views of a paged cache's page pools: (k, v) [n_pages][Hkv][page_size][d]."""
+        d = self.desc
+        esz = 2 if d.dtype == PS_BF16 else 4
+        kp, vp = ctypes.c_void_p(), ctypes.c_void_p()
+        _check(lib.ps_cache_pages(ctypes.c_void_p(self.handle), layer, ctypes.byref(kp), ctypes.byref(vp)),
+               "ps_cache_pages")
+        shape = (d.n_pages, d.n_kv_heads, d.page_size, d.head_dim)
+        n = shape[0] * shape[1] * shape[2] * shape[3]
+        base = self.buffer.data_ptr()
+        return tuple(self.buffer[p - base:p - base + n * esz].view(self.dtype).view(shape)
+                     for p in (kp.value, vp.value))
+
     def seq_kv(self, layer: int, row: int, prefix_row: int | None = None):
         """Copies of one sequence's K and V slots, [Hkv][prefix_cap+W][d]: the
         prefix block's slots followed by the window block's."""
@@ -392,7 +423,7 @@ class Cache:
     def fill_(self, value: float) -> None:
         """Set every K/V slot of every layer (not the workspace) to ``value``."""
         for layer in range(self.desc.n_layers):
-            for t in self.blocks(layer):
+            for t in (self.pages(layer) if self.paged else self.blocks(layer)):
                 t.fill_(value)
 
     def close(self):

@@ -41,13 +41,13 @@ __global__ void __launch_bounds__(256) append_kernel(AppendParams p, int pieces_
         const int64_t last = p.pos[b] + p.n_new - 1;
         char* kd;
         char* vd;
-        if (pos < P) {  // slot pos of the prefix block
-            const int64_t row = ((int64_t)p.c.prows[b] * p.c.hkv + g) * p.c.pcap + pos;
+        if (pos < P) {  // prefix slot pos
+            const int64_t row = prefix_row(p.c, b, g, pos);
             kd = static_cast<char*>(p.c.kpre) + row * row_bytes;
             vd = static_cast<char*>(p.c.vpre) + row * row_bytes;
-        } else {        // slot (pos - P) mod W of the window block
+        } else {        // ring slot (pos - P) mod W
             if (pos <= last - p.c.window) continue;  // overwritten later in this same call
-            const int64_t row = ((int64_t)p.c.rows[b] * p.c.hkv + g) * p.c.window + (pos - P) % p.c.window;
+            const int64_t row = ring_row(p.c, b, g, (pos - P) % p.c.window);
             kd = static_cast<char*>(p.c.kwin) + row * row_bytes;
             vd = static_cast<char*>(p.c.vwin) + row * row_bytes;
         }
@@ -86,12 +86,12 @@ __global__ void __launch_bounds__(256) append_rope_kernel(AppendParams p, RopeFr
         T* kd;
         T* vd;
         if (pos < P) {
-            const int64_t row = ((int64_t)p.c.prows[b] * p.c.hkv + g) * p.c.pcap + pos;
+            const int64_t row = prefix_row(p.c, b, g, pos);
             kd = static_cast<T*>(p.c.kpre) + row * D;
             vd = static_cast<T*>(p.c.vpre) + row * D;
         } else {
             if (pos <= last - p.c.window) continue;  // overwritten later in this same call
-            const int64_t row = ((int64_t)p.c.rows[b] * p.c.hkv + g) * p.c.window + (pos - P) % p.c.window;
+            const int64_t row = ring_row(p.c, b, g, (pos - P) % p.c.window);
             kd = static_cast<T*>(p.c.kwin) + row * D;
             vd = static_cast<T*>(p.c.vwin) + row * D;
         }
@@ -151,11 +151,10 @@ __global__ void __launch_bounds__(256) rerotate_kernel(RerotateParams p) {
         cs[i] = p.cs[8 * j + i];
         sn[i] = p.sn[8 * j + i];
     }
-    T* head = static_cast<T*>(p.c.kwin) + ((int64_t)p.c.rows[b] * p.c.hkv + g) * p.c.window * D;
     for (int64_t k = (int64_t)blockIdx.x * RPW + rsub; k < count; k += (int64_t)gridDim.x * RPW) {
         const int64_t t = lo + k;
         const int64_t slot = (t - P) % p.c.window;
-        T* row = head + slot * D;
+        T* row = static_cast<T*>(p.c.kwin) + ring_row(p.c, b, g, slot) * D;
         T a[8], c[8];
         __builtin_memcpy(a, row + 8 * j, sizeof(a));
         __builtin_memcpy(c, row + 8 * j + D / 2, sizeof(c));
@@ -182,16 +181,21 @@ __global__ void __launch_bounds__(256) check_kernel(CheckParams p) {
         uint32_t f = 0;
         const bool row_ok = row >= 0 && row < p.max_seqs;
         if (!row_ok) f |= PS_CHECK_ROW;
-        if (pr < 0 || pr >= p.prefix_blocks) f |= PS_CHECK_PREFIX_BLOCK;
+        if (!p.pages && (pr < 0 || pr >= p.prefix_blocks)) f |= PS_CHECK_PREFIX_BLOCK;
         if (P < 0 || P > p.pcap) f |= PS_CHECK_PREFIX_LEN;
         // positions run up to 2^62 (far from int64 overflow of pos + length)
         if (pos < 0 || pos > ((int64_t)1 << 62) - p.n_new) f |= PS_CHECK_POSITION;
+        if (p.pages)  // paged layout: every page the sequence may touch lies in the pool
+            for (int j = 0; j < p.pages_per_seq; ++j) {
+                const int32_t pg = p.pages[(int64_t)b * p.pages_per_seq + j];
+                if (pg < 0 || pg >= p.n_pages) f |= PS_CHECK_PAGE;
+            }
         for (int o = 0; o < b; ++o) {
             const int32_t orow = p.rows[o];
             if (orow == row) f |= PS_CHECK_DUPLICATE_ROW;
             const int32_t opr = p.prows ? p.prows[o] : orow;
             const int64_t oP = p.plen ? (int64_t)p.plen[o] : p.plen_scalar;
-            if (opr == pr && oP != P) f |= PS_CHECK_SHARED_PREFIX;
+            if (!p.pages && opr == pr && oP != P) f |= PS_CHECK_SHARED_PREFIX;
         }
         if (row_ok && p.mode != kCheckNone) {
             const int64_t nx = p.next_pos[row];

@@ -22,7 +22,13 @@ bool desc_ok(const ps_cache_desc* d) {
     if (d->n_layers < 1 || d->max_seqs < 1 || d->n_q_heads < 1 || d->n_kv_heads < 1) return false;
     if (d->n_q_heads % d->n_kv_heads != 0) return false;
     if (d->prefix_cap < 0 || d->window < 1 || d->prefix_blocks < 0) return false;
-    return true;
+    if (d->page_size == 0) return d->n_pages == 0;
+    // paged layout: a power of two >= 128 dividing prefix_cap and W, at most
+    // 256 pages per sequence, and no prefix blocks
+    const int pg = d->page_size;
+    if (pg < 128 || (pg & (pg - 1)) != 0 || d->prefix_cap % pg != 0 || d->window % pg != 0) return false;
+    if (d->n_pages < 1 || d->prefix_blocks != 0) return false;
+    return (int64_t)d->prefix_cap / pg + d->window / pg <= 256;
 }
 
 bool desc_supported(const ps_cache_desc* d) {
@@ -45,9 +51,15 @@ Layout layout_of(const ps_cache_desc* d) {
     Layout l{};
     l.elem = d->dtype == PS_BF16 ? 2 : 4;
     l.rows_per_head = (int64_t)d->prefix_cap + d->window;
-    l.prefix_blocks = d->prefix_blocks > 0 ? d->prefix_blocks : d->max_seqs;
-    l.pre_layer_bytes = align_up((size_t)l.prefix_blocks * d->n_kv_heads * d->prefix_cap * d->head_dim * l.elem);
-    l.win_layer_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * d->window * d->head_dim * l.elem);
+    if (d->page_size > 0) {  // paged: one page pool per layer (the "prefix" pool), no window pool
+        l.prefix_blocks = 0;
+        l.pre_layer_bytes = align_up((size_t)d->n_pages * d->n_kv_heads * d->page_size * d->head_dim * l.elem);
+        l.win_layer_bytes = 0;
+    } else {
+        l.prefix_blocks = d->prefix_blocks > 0 ? d->prefix_blocks : d->max_seqs;
+        l.pre_layer_bytes = align_up((size_t)l.prefix_blocks * d->n_kv_heads * d->prefix_cap * d->head_dim * l.elem);
+        l.win_layer_bytes = align_up((size_t)d->max_seqs * d->n_kv_heads * d->window * d->head_dim * l.elem);
+    }
     l.pre_bytes = l.pre_layer_bytes * (size_t)d->n_layers;
     l.win_bytes = l.win_layer_bytes * (size_t)d->n_layers;
     l.s_max = (int32_t)((l.rows_per_head + ps::kMinSplitRows - 1) / ps::kMinSplitRows);
@@ -67,6 +79,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PS_OK : PS_ERR_HIP; }
 // prefix block per row.
 bool batch_ok(const ps_cache* c, const ps_seq_batch* b) {
     if (!b || b->n < 1 || b->n > c->desc.max_seqs || !b->rows || !b->prefix_len || !b->pos) return false;
+    if (c->page_size) return b->page_table != nullptr;  // paged: the page table names every slot's page
+    if (b->page_table) return false;
     return b->prefix_rows || c->prefix_blocks == c->desc.max_seqs;
 }
 
@@ -83,14 +97,24 @@ ps::CacheLayer cache_layer(const ps_cache* c, int32_t layer, const ps_seq_batch*
     v.prows = b->prefix_rows ? b->prefix_rows : b->rows;
     v.v_off = c->v_pre - c->k_pre;  // == v_win - k_win (see ps_cache_create)
     v.guard = c->checks ? c->check_flags : nullptr;
+    if (c->page_size) {  // one page pool serves prefix and window slots
+        v.kwin = v.kpre;
+        v.vwin = v.vpre;
+        v.pages = b->page_table;
+        v.pages_per_seq = c->pages_per_seq;
+        v.page_shift = c->page_shift;
+    }
     return v;
 }
 
 // Debug checks of a call's per-sequence arguments, enqueued before its kernels.
 int run_checks(const ps_cache* c, int32_t layer, const int32_t* rows, const int32_t* prows, const int32_t* plen,
                const int64_t* pos, int64_t plen_scalar, int64_t pos_scalar, int32_t n, int32_t n_new, int32_t mode,
-               void* stream) {
+               void* stream, const int32_t* pages = nullptr) {
     ps::CheckParams p{};
+    p.pages = pages;
+    p.pages_per_seq = c->pages_per_seq;
+    p.n_pages = c->n_pages;
     p.rows = rows;
     p.prows = prows;
     p.plen = plen;
@@ -110,7 +134,8 @@ int run_checks(const ps_cache* c, int32_t layer, const int32_t* rows, const int3
 
 int batch_checks(const ps_cache* c, int32_t layer, const ps_seq_batch* b, int32_t n_new, int32_t mode, void* stream) {
     if (!c->checks) return PS_OK;
-    return run_checks(c, layer, b->rows, b->prefix_rows, b->prefix_len, b->pos, 0, 0, b->n, n_new, mode, stream);
+    return run_checks(c, layer, b->rows, b->prefix_rows, b->prefix_len, b->pos, 0, 0, b->n, n_new, mode, stream,
+                      b->page_table);
 }
 
 // Rows per decode split.  A decode launch is short (tens of MB at batch 1),
@@ -160,6 +185,13 @@ int decode_common(ps_cache* c, int32_t layer, const ps_seq_batch* batch, const v
     const int st = batch_checks(c, layer, batch, knew ? 1 : 0, knew ? ps::kCheckAppend : ps::kCheckQuery, stream);
     if (st != PS_OK) return st;
     const int group = c->desc.n_q_heads / c->desc.n_kv_heads;
+    if (c->page_size) {
+        // paged layout: the vector kernel with 8 waves and 8 rows per lane
+        const int rows = 64 * ps::decode_rows_per_load(c->desc.dtype, c->desc.head_dim);
+        if (c->trace || (c->decode_rows != 0 && c->decode_rows != rows)) return PS_ERR_UNSUPPORTED;
+        p.stream_nt = ps::decode_grid(rows, p) >= 1024;
+        return hip_status(ps::launch_decode(c->desc.dtype, c->desc.head_dim, group, rows, p, (hipStream_t)stream));
+    }
     if (c->trace) {
         // traced launches: the 256-row split kernel with phase timestamps
         if (c->desc.dtype != PS_BF16 || c->desc.head_dim != 128 || (group != 1 && group != 2 && group != 4) ||
@@ -274,6 +306,11 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
     c->elem_bytes = l.elem;
     c->rows_per_head = l.rows_per_head;
     c->prefix_blocks = l.prefix_blocks;
+    c->page_size = desc->page_size;
+    c->n_pages = desc->n_pages;
+    c->page_shift = 0;
+    while (c->page_size && (1 << c->page_shift) < c->page_size) ++c->page_shift;
+    c->pages_per_seq = c->page_size ? desc->prefix_cap / c->page_size + desc->window / c->page_size : 0;
     c->pre_layer_bytes = l.pre_layer_bytes;
     c->win_layer_bytes = l.win_layer_bytes;
     // K pools, then V pools in the same order: a V slot lies at one fixed
@@ -283,6 +320,8 @@ int ps_cache_create(const ps_cache_desc* desc, void* dev_mem, size_t bytes, void
     c->k_win = c->k_pre + l.pre_bytes;
     c->v_pre = c->k_win + l.win_bytes;
     c->v_win = c->v_pre + l.pre_bytes;
+    // (paged: win_bytes is 0, and the kernels address window slots in the
+    // page pool, see cache_layer)
     char* ws = c->v_win + l.win_bytes;
     c->ws_o = reinterpret_cast<float*>(ws);
     c->ws_ml = reinterpret_cast<float*>(ws + l.ws_o_bytes);
@@ -311,10 +350,19 @@ int ps_cache_destroy(ps_cache* cache) {
     return PS_OK;
 }
 
+int ps_cache_pages(const ps_cache* c, int32_t layer, void** k_pages, void** v_pages) {
+    if (!c || !k_pages || !v_pages || layer < 0 || layer >= c->desc.n_layers) return PS_ERR_INVALID;
+    if (!c->page_size) return PS_ERR_UNSUPPORTED;
+    *k_pages = c->k_pre + (size_t)layer * c->pre_layer_bytes;
+    *v_pages = c->v_pre + (size_t)layer * c->pre_layer_bytes;
+    return PS_OK;
+}
+
 int ps_cache_blocks(const ps_cache* c, int32_t layer, void** k_prefix, void** v_prefix, void** k_window,
                     void** v_window) {
     if (!c || !k_prefix || !v_prefix || !k_window || !v_window || layer < 0 || layer >= c->desc.n_layers)
         return PS_ERR_INVALID;
+    if (c->page_size) return PS_ERR_UNSUPPORTED;
     *k_prefix = c->k_pre + (size_t)layer * c->pre_layer_bytes;
     *v_prefix = c->v_pre + (size_t)layer * c->pre_layer_bytes;
     *k_window = c->k_win + (size_t)layer * c->win_layer_bytes;
@@ -435,6 +483,7 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
         return PS_ERR_INVALID;
     if (!isfinite(a->scale) || !(a->scale > 0.f)) return PS_ERR_INVALID;
     if (a->prefix_lens && !a->starts) return PS_ERR_INVALID;
+    if (!a->cache && a->page_table) return PS_ERR_INVALID;
     if (a->start_pos > kMaxPos - a->seq_len) return PS_ERR_UNSUPPORTED;
     int hq = a->n_q_heads, hkv = a->n_kv_heads, d = a->head_dim, dtype = a->dtype;
     const ps_cache* c = a->cache;
@@ -445,7 +494,12 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
             dtype != c->desc.dtype)
             return PS_ERR_INVALID;
         if (a->window != c->desc.window || a->prefix_len > c->desc.prefix_cap) return PS_ERR_INVALID;
-        if (!a->prefix_rows && c->prefix_blocks != c->desc.max_seqs) return PS_ERR_INVALID;
+        if (c->page_size) {
+            if (!a->page_table) return PS_ERR_INVALID;
+        } else {
+            if (a->page_table) return PS_ERR_INVALID;
+            if (!a->prefix_rows && c->prefix_blocks != c->desc.max_seqs) return PS_ERR_INVALID;
+        }
     }
     if (hq < 1 || hkv < 1 || hq % hkv != 0) return PS_ERR_INVALID;
     if (dtype != PS_BF16 && dtype != PS_F32) return PS_ERR_UNSUPPORTED;
@@ -482,12 +536,19 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
         pc.elem_bytes = (int32_t)c->elem_bytes;
         pc.rows = a->rows;
         pc.prows = a->prefix_rows ? a->prefix_rows : a->rows;
+        if (c->page_size) {
+            pc.kwin = pc.kpre;
+            pc.vwin = pc.vpre;
+            pc.pages = a->page_table;
+            pc.pages_per_seq = c->pages_per_seq;
+            pc.page_shift = c->page_shift;
+        }
         p.cache_mode = 1;
         // uniform chunks: the cached runs are the same for every sequence
         if (!ragged) nr = ps::cache_key_runs(pc, S, P, p.runs);
         if (c->checks) {
             const int st = run_checks(c, a->layer, a->rows, a->prefix_rows, ragged ? a->prefix_lens : nullptr,
-                                      a->starts, P, S, a->batch, a->seq_len, ps::kCheckNext, stream);
+                                      a->starts, P, S, a->batch, a->seq_len, ps::kCheckNext, stream, a->page_table);
             if (st != PS_OK) return st;
             p.guard = c->check_flags;
         }

@@ -179,7 +179,12 @@ __device__ inline void trace_mark(const DecodeParams& p, int point) {
     p.trace[(size_t)blockIdx.x * kDecodeTracePoints + point] = __builtin_amdgcn_s_memrealtime();
 }
 
-template <typename T, int D, int G, int NW, int U, bool NTL, bool TRACE = false>
+// PAGED: the paged cache layout.  The split rows are then fixed logical rows
+// of the sequence -- [0, pcap) its prefix slots, [pcap, pcap + W) its ring
+// slots, valid while filled -- so the page of a row is table entry
+// row / page, known before the sequence metadata arrives; a wave's rows
+// (U * RPW consecutive rows, at most 128) lie in one page.
+template <typename T, int D, int G, int NW, int U, bool NTL, bool TRACE = false, bool PAGED = false>
 __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     constexpr int NT = NW * 64;
     constexpr int VEC = Elem<T>::kPerVec;
@@ -218,7 +223,14 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // Metadata and queries first: independent loads, issued together.
     const int64_t P = p.plen[b];
     const int64_t i = p.pos[b];
-    const int64_t crow = p.c.rows[b], prow = p.c.prows[b];
+    const int64_t crow = PAGED ? 0 : p.c.rows[b], prow = PAGED ? 0 : p.c.prows[b];
+    // paged: the page of this wave's rows (independent of the metadata)
+    const int64_t wave_row0 = (int64_t)split * R + (int64_t)wave * U * RPW;
+    // (a wave wholly past the last row reads entry 0; its loads are masked off)
+    const int64_t wave_page =
+        PAGED ? (int64_t)p.c.pages[(int64_t)b * p.c.pages_per_seq +
+                                   (wave_row0 < p.rows_per_head ? (wave_row0 >> p.c.page_shift) : 0)]
+              : 0;
     Vec16 qraw[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -228,7 +240,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     int64_t n_ring = i - P + 1;
     n_ring = n_ring < 0 ? 0 : (n_ring > p.c.window ? (int64_t)p.c.window : n_ring);
     const int64_t n = n_pre + n_ring;
-    const int nsplit = (int)((n + R - 1) / R);
+    const int nsplit = PAGED ? (int)((p.rows_per_head + R - 1) / R) : (int)((n + R - 1) / R);
     if (split >= nsplit) return;
     if constexpr (TRACE) {
         if (tid == 0) {
@@ -252,8 +264,18 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     int64_t new_r = i;  // key row of the new token
     if (fused && i >= P) {
         const int64_t off = i - P;
-        new_r = n_pre + (off < 0x7FFFFFFF ? (int64_t)((uint32_t)off % (uint32_t)p.c.window) : off % p.c.window);
+        new_r = (PAGED ? (int64_t)p.c.pcap : n_pre) +
+                (off < 0x7FFFFFFF ? (int64_t)((uint32_t)off % (uint32_t)p.c.window) : off % p.c.window);
     }
+    // paged: the new token's page, for the commit below
+    const int64_t new_page =
+        PAGED && fused && split == 0 && tid < LPR ? (int64_t)p.c.pages[(int64_t)b * p.c.pages_per_seq + (new_r >> p.c.page_shift)]
+                                                  : 0;
+    const int64_t page_mask = PAGED ? ((int64_t)1 << p.c.page_shift) - 1 : 0;
+    // paged row r -> byte address of its K row
+    auto paged_k = [&](int64_t page, int64_t r) -> const char* {
+        return static_cast<const char*>(p.c.kpre) + (((page * p.c.hkv + g) << p.c.page_shift) + (r & page_mask)) * kRowBytes;
+    };
     const T* knew_row = fused ? reinterpret_cast<const T*>(p.knew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
     const T* vnew_row = fused ? reinterpret_cast<const T*>(p.vnew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
 
@@ -266,6 +288,20 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t r = r0 + (int64_t)(wave * U + u) * RPW + rg;
+        if constexpr (PAGED) {
+            // unfilled slots are never read: their loads are masked off
+            valid[u] = r < p.c.pcap ? r < n_pre : (r - p.c.pcap < n_ring);
+            const bool is_new = fused && r == new_r;
+            const T* kp = is_new ? knew_row : reinterpret_cast<const T*>(paged_k(wave_page, r));
+            const T* vp = is_new ? vnew_row : reinterpret_cast<const T*>(paged_k(wave_page, r) + v_off);
+            kr[u] = Vec16{{0, 0, 0, 0}};
+            vr[u] = Vec16{{0, 0, 0, 0}};
+            if (valid[u]) {
+                kr[u] = load16_stream<NTL>(kp + sub * VEC);
+                vr[u] = load16_stream<NTL>(vp + sub * VEC);
+            }
+            continue;
+        }
         valid[u] = r < n;
         r = valid[u] ? r : n - 1;
         const bool is_new = fused && r == new_r;
@@ -300,7 +336,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // The split that owns the new token's slot also commits it to the cache
     // (after the loads above, so no wait on them is forced here).
     if (fused && split == 0 && tid < LPR) {
-        const char* ka = (new_r < n_pre ? kpre_a : kwin_a) + new_r * kRowBytes;
+        const char* ka = PAGED ? paged_k(new_page, new_r) : (new_r < n_pre ? kpre_a : kwin_a) + new_r * kRowBytes;
         T* kd = const_cast<T*>(reinterpret_cast<const T*>(ka)) + tid * VEC;
         T* vd = const_cast<T*>(reinterpret_cast<const T*>(ka + v_off)) + tid * VEC;
         *reinterpret_cast<Vec16*>(kd) = load16(knew_row + tid * VEC);
@@ -855,6 +891,14 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
     const int64_t n_wg = ((p.rows_per_head + R - 1) / R) * (int64_t)p.c.hkv * p.n_seqs;
     if (n_wg > 0x7FFFFFFF) return hipErrorInvalidValue;
     if (p.trace) return hipErrorNotSupported;  // traced launches: see launch_decode_traced
+    if (p.c.pages) {  // paged layout: built for the 8-wave, 8-rows-per-lane split only
+        if constexpr (NW == 8 && U == 8)
+            hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U, NTL, false, true>), dim3((unsigned)n_wg), dim3(NW * 64),
+                               0, stream, p);
+        else
+            return hipErrorNotSupported;
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL((decode_kernel<T, D, G, NW, U, NTL>), dim3((unsigned)n_wg), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }

@@ -14,10 +14,14 @@ struct ps_cache {
     size_t bytes = 0;
     size_t elem_bytes = 0;       // 2 (bf16) or 4 (f32)
     int64_t rows_per_head = 0;   // prefix_cap + window: the most keys one sequence can hold
-    int32_t prefix_blocks = 0;   // prefix pool size (blocks)
+    int32_t prefix_blocks = 0;   // prefix pool size (blocks); paged layout: 0
+    int32_t page_size = 0;       // paged layout: slots per page (power of two >= 128), else 0
+    int32_t page_shift = 0;      // log2(page_size)
+    int32_t pages_per_seq = 0;   // paged layout: prefix_cap / page_size + window / page_size
+    int32_t n_pages = 0;         // paged layout: pages in the pool of each layer
     size_t pre_layer_bytes = 0;  // bytes of one layer's K (or V) prefix pool
     size_t win_layer_bytes = 0;  // bytes of one layer's K (or V) window pool
-    char* k_pre = nullptr;       // [L][prefix_blocks][Hkv][Pcap][d]
+    char* k_pre = nullptr;       // [L][prefix_blocks][Hkv][Pcap][d]; paged: page pool [L][n_pages][Hkv][page][d]
     char* v_pre = nullptr;
     char* k_win = nullptr;       // [L][max_seqs][Hkv][W][d]
     char* v_win = nullptr;
@@ -40,9 +44,13 @@ namespace ps {
 constexpr int kMinSplitRows = 16;  // smallest rows-per-split the workspace is sized for
 constexpr int kTicketStride = 64;  // u32 words between arrival counters: one counter per 256-byte line
 
-// A layer of the cache as the kernels address it: prefix block b, kv head g
-// starts at kpre + (b * hkv + g) * pcap rows; window block r, kv head g at
-// kwin + (r * hkv + g) * window rows.
+// A layer of the cache as the kernels address it.  Block layout: prefix
+// block b, kv head g starts at kpre + (b * hkv + g) * pcap rows; window block
+// r, kv head g at kwin + (r * hkv + g) * window rows.  Paged layout (pages
+// non-null): kpre == kwin is the page pool [n_pages][hkv][page][d]; entry j
+// of a sequence's page table row is the page holding its prefix slots
+// [j page, (j + 1) page) for j < pcap / page, and its ring slots
+// [(j - pcap / page) page, ...) after that.
 struct CacheLayer {
     void* kpre;
     void* vpre;
@@ -50,11 +58,33 @@ struct CacheLayer {
     void* vwin;
     int32_t hkv;
     int32_t pcap, window;
-    const int32_t* rows;   // window block of each sequence of the batch
-    const int32_t* prows;  // prefix block of each sequence of the batch
+    const int32_t* rows;   // window block of each sequence (paged: the sequence's slot for the checks)
+    const int32_t* prows;  // prefix block of each sequence of the batch (block layout)
     int64_t v_off;         // bytes from a K slot to its V slot: vpre - kpre == vwin - kwin
     const uint32_t* guard; // checks on: the cache's flag word; a kernel does nothing while it is set
+    const int32_t* pages;  // paged layout: page table [n][pages_per_seq], else null
+    int32_t pages_per_seq;
+    int32_t page_shift;    // log2(page size)
 };
+
+// Row index (in rows of d elements, from kpre / vpre) of prefix slot s of
+// sequence b, kv head g.
+__host__ __device__ inline int64_t prefix_row(const CacheLayer& c, int b, int g, int64_t s) {
+    if (c.pages) {
+        const int64_t page = c.pages[(int64_t)b * c.pages_per_seq + (s >> c.page_shift)];
+        return ((page * c.hkv + g) << c.page_shift) + (s & ((1 << c.page_shift) - 1));
+    }
+    return ((int64_t)c.prows[b] * c.hkv + g) * c.pcap + s;
+}
+// Row index (from kwin / vwin) of ring slot r of sequence b, kv head g.
+__host__ __device__ inline int64_t ring_row(const CacheLayer& c, int b, int g, int64_t r) {
+    if (c.pages) {
+        const int64_t page =
+            c.pages[(int64_t)b * c.pages_per_seq + (c.pcap >> c.page_shift) + (r >> c.page_shift)];
+        return ((page * c.hkv + g) << c.page_shift) + (r & ((1 << c.page_shift) - 1));
+    }
+    return ((int64_t)c.rows[b] * c.hkv + g) * c.window + r;
+}
 
 // Device-side checks of a call's per-sequence arguments (debug mode of a
 // cache).  One workgroup: every violation is OR-ed into *flags (bits of
@@ -76,6 +106,8 @@ struct CheckParams {
     int32_t max_seqs, prefix_blocks, pcap;
     int64_t* next_pos;     // [max_seqs] of the layer; -1 = nothing appended yet
     uint32_t* flags;
+    const int32_t* pages;  // paged layout: page table [n][pages_per_seq], else null
+    int32_t pages_per_seq, n_pages;
 };
 hipError_t launch_check(const CheckParams& p, hipStream_t stream);
 
@@ -189,52 +221,92 @@ struct KeyRun {
     int64_t pos0;          // position of row 0
     int64_t n;             // rows in the run
     const int32_t* rows;   // if non-null: sequence b uses cache row rows[b] (seq_stride applies to it)
+    // Paged runs (pages non-null): k, v are the page pool; row r of the run
+    // is slot first_slot + r of a region whose page j is table entry
+    // page_col + j of the sequence's row in `pages`, and is found at row
+    // (page * hkv + g) * page + slot % page of the pool.  A paged run never
+    // crosses a page boundary inside a 128-row tile (the ring run is split at
+    // its first page boundary).
+    const int32_t* pages;
+    int32_t pages_per_seq, page_col, page_shift;
+    int64_t first_slot;
 };
 
-constexpr int kMaxRuns = 4;
+constexpr int kMaxRuns = 5;
 
 // One layer's cache pools as a chunk reads them.
 struct PrefillCache {
-    const char* kpre;      // prefix pool: [prefix_blocks][hkv][pcap][d]
+    const char* kpre;      // prefix pool: [prefix_blocks][hkv][pcap][d] (paged: the page pool)
     const char* vpre;
-    const char* kwin;      // window pool: [max_seqs][hkv][window][d]
+    const char* kwin;      // window pool: [max_seqs][hkv][window][d] (paged: the page pool)
     const char* vwin;
     int64_t pcap, window;
     int32_t hkv, head_dim, elem_bytes;
     const int32_t* rows;   // window block of each sequence
     const int32_t* prows;  // prefix block of each sequence
+    const int32_t* pages;  // paged layout: page table [B][pages_per_seq], else null
+    int32_t pages_per_seq, page_shift;
 };
 
 __host__ __device__ inline void set_cache_run(KeyRun& r, const char* kpool, const char* vpool, int64_t block_rows,
                                               const int32_t* blocks, const PrefillCache& c, int64_t first_slot,
-                                              int64_t pos0, int64_t n) {
+                                              int64_t pos0, int64_t n, int32_t page_col) {
     const int64_t d = c.head_dim;
+    r.pos0 = pos0;
+    r.n = n;
+    r.row_stride = d;
+    r.first_slot = first_slot;
+    if (c.pages) {
+        r.k = kpool;
+        r.v = vpool;
+        r.seq_stride = 0;
+        r.head_stride = d << c.page_shift;
+        r.rows = nullptr;
+        r.pages = c.pages;
+        r.pages_per_seq = c.pages_per_seq;
+        r.page_col = page_col;
+        r.page_shift = c.page_shift;
+        return;
+    }
     r.k = kpool + first_slot * d * c.elem_bytes;
     r.v = vpool + first_slot * d * c.elem_bytes;
     r.seq_stride = (int64_t)c.hkv * block_rows * d;
     r.head_stride = block_rows * d;
-    r.row_stride = d;
-    r.pos0 = pos0;
-    r.n = n;
     r.rows = blocks;
+    r.pages = nullptr;
+    r.pages_per_seq = r.page_col = r.page_shift = 0;
 }
 
 // Runs of the cached keys a chunk starting at position S (prefix length P)
 // reads: the prefix slots [0, min(S, P)), then the ring slots of positions
-// [max(P, S - W), S) as one or two runs (split where the ring wraps).
-// Returns the number of runs written (0 to 3).
+// [max(P, S - W), S) as one or two runs (split where the ring wraps); in the
+// paged layout the first ring run is also split at its first page boundary,
+// so that every run's 128-row tiles lie inside single pages.  Returns the
+// number of runs written (0 to 4).
 __host__ __device__ inline int cache_key_runs(const PrefillCache& c, int64_t S, int64_t P, KeyRun* runs) {
     int nr = 0;
     const int64_t W = c.window;
     const int64_t n_pre = S < P ? S : P;
-    if (n_pre > 0) set_cache_run(runs[nr++], c.kpre, c.vpre, c.pcap, c.prows, c, 0, 0, n_pre);
+    const int32_t ring_col = c.pages ? (int32_t)(c.pcap >> c.page_shift) : 0;
+    if (n_pre > 0) set_cache_run(runs[nr++], c.kpre, c.vpre, c.pcap, c.prows, c, 0, 0, n_pre, 0);
     if (S > P) {
         const int64_t first = S - W > P ? S - W : P;  // oldest position the ring still holds
         const int64_t cnt = S - first;
         const int64_t slot = (first - P) % W;
-        const int64_t n_a = slot + cnt <= W ? cnt : W - slot;
-        set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, slot, first, n_a);
-        if (n_a < cnt) set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, 0, first + n_a, cnt - n_a);
+        int64_t n_a = slot + cnt <= W ? cnt : W - slot;
+        int64_t head = 0;  // paged: slots of the first run before its first page boundary
+        if (c.pages) {
+            const int64_t pg = (int64_t)1 << c.page_shift;
+            const int64_t to_boundary = (pg - (slot & (pg - 1))) & (pg - 1);
+            head = to_boundary < n_a ? to_boundary : 0;
+        }
+        if (head > 0) {
+            set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, slot, first, head, ring_col);
+            set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, slot + head, first + head, n_a - head, ring_col);
+        } else {
+            set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, slot, first, n_a, ring_col);
+        }
+        if (n_a < cnt) set_cache_run(runs[nr++], c.kwin, c.vwin, W, c.rows, c, 0, first + n_a, cnt - n_a, ring_col);
     }
     return nr;
 }

@@ -68,7 +68,48 @@ struct RunView {
     int64_t pos0;
     int n;
     int row_bytes;
+    // paged runs: page_shift >= 0; row r is slot first_slot + r of the
+    // region whose pages are table entries page_col, page_col + 1, ...
+    int page_shift, page_col, first_slot, page_rows;
 };
+
+// Pages a sequence's page table may hold (the host enforces it); the bf16
+// and plain kernels keep the sequence's table row in LDS.
+constexpr int kMaxPagesPerSeq = 256;
+
+// Fill a run view for sequence b, kv head g (element size esz).
+__device__ inline void make_view(RunView& v, const KeyRun& run, int b, int g, int hkv, int esz) {
+    if (run.pages) {
+        const int64_t head_el = (int64_t)g * run.head_stride;
+        v.k = static_cast<const char*>(run.k) + head_el * esz;
+        v.v = static_cast<const char*>(run.v) + head_el * esz;
+        v.page_shift = run.page_shift;
+        v.page_col = run.page_col;
+        v.first_slot = (int)run.first_slot;
+        v.page_rows = hkv << run.page_shift;
+    } else {
+        const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
+        const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride;
+        v.k = static_cast<const char*>(run.k) + base_el * esz;
+        v.v = static_cast<const char*>(run.v) + base_el * esz;
+        v.page_shift = -1;
+        v.page_col = v.first_slot = v.page_rows = 0;
+    }
+    v.pos0 = run.pos0;
+    v.n = (int)run.n;
+    v.row_bytes = (int)(run.row_stride * esz);
+}
+
+// Byte offset from a view's base of rows [row0, row0 + n) of its run, which
+// lie inside one page when the run is paged (table: the sequence's page
+// table row in LDS).
+__device__ inline int64_t view_row_offset(int shift, int page_col, int first_slot, int page_rows, int rs,
+                                          const int32_t* table, int row0) {
+    if (shift < 0) return (int64_t)row0 * rs;
+    const int slot = first_slot + row0;
+    const int64_t page = table[page_col + (slot >> shift)];
+    return (page * page_rows + (slot & ((1 << shift) - 1))) * (int64_t)rs;
+}
 
 __device__ inline int64_t clamp64(int64_t x, int64_t lo, int64_t hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
@@ -178,6 +219,7 @@ struct Cursor {
     const char* v;
     int64_t pos0;
     int n, rs;
+    int shift, page_col, first_slot, page_rows;  // paged runs (shift >= 0)
 };
 
 __device__ inline void cursor_enter(Cursor& c, int r, const TileWalk& w, const RunView* views) {
@@ -190,6 +232,10 @@ __device__ inline void cursor_enter(Cursor& c, int r, const TileWalk& w, const R
     c.pos0 = uniform_i64(v.pos0);
     c.n = uniform_int(v.n);
     c.rs = uniform_int(v.row_bytes);
+    c.shift = uniform_int(v.page_shift);
+    c.page_col = uniform_int(v.page_col);
+    c.first_slot = uniform_int(v.first_slot);
+    c.page_rows = uniform_int(v.page_rows);
 }
 
 // Step to the next tile; returns true when the cursor entered a new range.
@@ -224,10 +270,13 @@ __device__ inline void lane_offsets(LaneOffsets& o, int rs, int lane, int wave) 
 // each lane loads the global chunk that belongs at its swizzled position).
 // The buffer resources cover only the run's rows of this tile, so rows past
 // the run's end read as zero (those keys are masked; zero V rows add nothing).
-__device__ inline void load_tile_bf16(const Cursor& c, const LaneOffsets& lo, int wave, char* stage) {
+__device__ inline void load_tile_bf16(const Cursor& c, const LaneOffsets& lo, int wave, char* stage,
+                                      const int32_t* table) {
     const int row0 = c.t * kBNB;
     const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
-    const int64_t off = (int64_t)row0 * c.rs;
+    const int64_t off =
+        c.shift < 0 ? (int64_t)row0 * c.rs
+                    : uniform_i64(view_row_offset(c.shift, c.page_col, c.first_slot, c.page_rows, c.rs, table, row0));
     const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
     const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
     if (wave >= kLoadWaves) return;
@@ -369,19 +418,14 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     __shared__ TileWalk walk;
     __shared__ RunView views[kMaxRuns];
     __shared__ KeyRun s_runs[kMaxRuns];
+    __shared__ int32_t s_table[kMaxPagesPerSeq];  // paged layout: the sequence's page table row
+    if (p.cache_mode && p.cache.pages)
+        for (int j = tid; j < p.cache.pages_per_seq; j += kThreads)
+            s_table[j] = p.cache.pages[(int64_t)b * p.cache.pages_per_seq + j];
     if (tid == 0) {
         const int n_runs = seq_key_runs(p, b, S_abs, P_abs, fr, s_runs);
         plan_walk<kBNB>(s_runs, n_runs, Pb, fr.W, (int64_t)i0, (int64_t)i1, walk);
-        for (int r = 0; r < n_runs; ++r) {
-            const KeyRun& run = s_runs[r];
-            const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
-            const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride;
-            views[r].k = static_cast<const char*>(run.k) + base_el * 2;
-            views[r].v = static_cast<const char*>(run.v) + base_el * 2;
-            views[r].pos0 = run.pos0;
-            views[r].n = (int)run.n;
-            views[r].row_bytes = (int)(run.row_stride * 2);
-        }
+        for (int r = 0; r < n_runs; ++r) make_view(views[r], s_runs[r], b, g, p.hkv, 2);
     }
     __syncthreads();
     int total = 0;
@@ -422,7 +466,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         lane_offsets(lo, pc.rs, lane, wave);
     }
     auto stage_next = [&](char* stage) {
-        load_tile_bf16(pc, lo, wave, stage);
+        load_tile_bf16(pc, lo, wave, stage, s_table);
         if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets(lo, pc.rs, lane, wave);
     };
     static_assert(kStages == 2 && kLoadsPerTile == 16, "vmcnt immediates assume 2 stages of 16 loads");
@@ -636,11 +680,22 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
     for (int rr = 0; rr < walk.n_ranges; ++rr) {
         const KeyRun& run = s_runs[walk.run[rr]];
         const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
-        const T* kb = reinterpret_cast<const T*>(run.k) + seq * run.seq_stride + (int64_t)g * run.head_stride;
-        const T* vb = reinterpret_cast<const T*>(run.v) + seq * run.seq_stride + (int64_t)g * run.head_stride;
+        const int64_t base_el = run.pages ? (int64_t)g * run.head_stride : seq * run.seq_stride + (int64_t)g * run.head_stride;
+        const T* kb = reinterpret_cast<const T*>(run.k) + base_el;
+        const T* vb = reinterpret_cast<const T*>(run.v) + base_el;
         for (int tile = walk.begin[rr]; tile < walk.end[rr]; ++tile) {
             const int64_t row0 = (int64_t)tile * kBN;
             const int64_t nrows = run.n - row0 < kBN ? run.n - row0 : kBN;
+            // first row of the tile: a paged run's 64-row tile lies in one page
+            int64_t tile_el = row0 * run.row_stride;
+            if (run.pages) {
+                const int64_t slot = run.first_slot + row0;
+                const int64_t page = run.pages[(int64_t)b * run.pages_per_seq + run.page_col + (slot >> run.page_shift)];
+                tile_el = ((page * p.hkv) << run.page_shift) * run.row_stride +
+                          (slot & (((int64_t)1 << run.page_shift) - 1)) * run.row_stride;
+            }
+            const T* kt = kb + tile_el;
+            const T* vt = vb + tile_el;
             const int64_t j0 = run.pos0 + row0;
             const int cls = nrows < kBN ? kMasked : tile_class(i0, i1, j0, j0 + nrows - 1, Pb, Wb);
             if (cls == kSkip) continue;
@@ -652,8 +707,8 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
                         const int r = idx / D, e = idx % D;
                         const int64_t row = half * BR + r;
                         const bool ok = row < nrows;
-                        ks[r][e] = ok ? to_f32(kb[(row0 + row) * run.row_stride + e]) : 0.f;
-                        vs[r][e] = ok ? to_f32(vb[(row0 + row) * run.row_stride + e]) : 0.f;
+                        ks[r][e] = ok ? to_f32(kt[row * run.row_stride + e]) : 0.f;
+                        vs[r][e] = ok ? to_f32(vt[row * run.row_stride + e]) : 0.f;
                     }
                     __syncthreads();
                     for (int r = 0; r < BR; ++r) {
@@ -870,16 +925,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
     __shared__ RunView views[kMaxRuns];
     if (tid == 0) {
         plan_walk<kBNB>(p.runs, p.n_runs, p.P, p.W, (int64_t)i0, (int64_t)i1, walk);
-        for (int r = 0; r < p.n_runs; ++r) {
-            const KeyRun& run = p.runs[r];
-            const int64_t seq = run.rows ? (int64_t)run.rows[b] : (int64_t)b;
-            const int64_t base_el = seq * run.seq_stride + (int64_t)g * run.head_stride;
-            views[r].k = static_cast<const char*>(run.k) + base_el * 2;
-            views[r].v = static_cast<const char*>(run.v) + base_el * 2;
-            views[r].pos0 = run.pos0;
-            views[r].n = (int)run.n;
-            views[r].row_bytes = (int)(run.row_stride * 2);
-        }
+        for (int r = 0; r < p.n_runs; ++r) make_view(views[r], p.runs[r], b, g, p.hkv, 2);
     }
     __syncthreads();
     int total = 0;

@@ -276,3 +276,22 @@ def test_position_frame_keeps_every_visibility_decision(tmp_path):
 
 def test_decode_trace_rejects_bad_arguments():
     assert ps.lib.ps_cache_set_decode_trace(None, None, 0, 0) == ps.PS_ERR_INVALID
+
+
+def test_paged_cache_descriptor_validation_and_size():
+    """Paged layout: page size a power of two >= 128 dividing prefix_cap and
+    W, at most 256 pages per sequence, no prefix blocks; the pools take
+    n_pages * Hkv * page * d elements per layer for K and for V."""
+    D = lambda **kw: ps.CacheDesc(*[kw.get(k, v) for k, v in (
+        ("n_layers", 2), ("max_seqs", 4), ("n_q_heads", 16), ("n_kv_heads", 8), ("head_dim", 128),
+        ("prefix_cap", 256), ("window", 4096), ("dtype", ps.PS_BF16), ("prefix_blocks", 0), ("page_size", 128),
+        ("n_pages", 100))])
+    ok = ps.ps_cache_bytes(D())
+    blocks = ps.ps_cache_bytes(D(page_size=0, n_pages=0))
+    assert ok > 0 and blocks > 0
+    pool = 100 * 8 * 128 * 128 * 2
+    assert ok - pool * 2 * 2 == blocks - (4 * 8 * (256 + 4096) * 128 * 2) * 2 * 2
+    for bad in (dict(page_size=96), dict(page_size=64), dict(page_size=256, prefix_cap=128),
+                dict(window=4096 + 128, page_size=256), dict(n_pages=0), dict(prefix_blocks=2),
+                dict(page_size=128, window=128 * 300), dict(page_size=0, n_pages=5)):
+        assert ps.ps_cache_bytes(D(**bad)) == 0, bad
