@@ -207,7 +207,6 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     // group share blockIdx % 8 whenever the group count is a multiple of 8, so
     // the hardware's round-robin deal puts them on one XCD (one L2); measured
     // 3% faster at batch 1 than the (split, kv head, sequence) grid.
-    if (p.c.guard && *p.c.guard) return;  // checks on and a check failed
     if constexpr (TRACE) {
         if (threadIdx.x == 0) {
             trace_mark(p, 0);
@@ -217,7 +216,8 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     const int n_groups = p.n_seqs * p.c.hkv;
     const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
     const int g = group % p.c.hkv, b = group / p.c.hkv;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address arithmetic
     const int sub = lane % LPR, rg = lane / LPR;
 
     // Metadata and queries first: independent loads, issued together.
@@ -231,6 +231,12 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         PAGED ? (int64_t)p.c.pages[(int64_t)b * p.c.pages_per_seq +
                                    (wave_row0 < p.rows_per_head ? (wave_row0 >> p.c.page_shift) : 0)]
               : 0;
+    // The debug-check flag word is read beside the metadata rather than
+    // before it (when checks are off any readable word stands in and the
+    // value is ignored), so no round trip precedes the metadata; nothing
+    // below the test is addressed from the metadata before it.
+    const uint32_t* guard_p = p.c.guard ? p.c.guard : reinterpret_cast<const uint32_t*>(p.plen);
+    const uint32_t guard_v = *guard_p;
     Vec16 qraw[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -242,6 +248,7 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     const int64_t n = n_pre + n_ring;
     const int nsplit = PAGED ? (int)((p.rows_per_head + R - 1) / R) : (int)((n + R - 1) / R);
     if (split >= nsplit) return;
+    if (p.c.guard && guard_v) return;  // checks on and a check failed
     if constexpr (TRACE) {
         if (tid == 0) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -276,6 +283,9 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     auto paged_k = [&](int64_t page, int64_t r) -> const char* {
         return static_cast<const char*>(p.c.kpre) + (((page * p.c.hkv + g) << p.c.page_shift) + (r & page_mask)) * kRowBytes;
     };
+    // paged: this lane's rows r0 + (wave U + u) RPW + rg all lie in the wave's
+    // page, at a constant stride from the first
+    const char* lane_k = PAGED ? paged_k(wave_page, wave_row0 + rg) : nullptr;
     const T* knew_row = fused ? reinterpret_cast<const T*>(p.knew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
     const T* vnew_row = fused ? reinterpret_cast<const T*>(p.vnew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
 
@@ -289,17 +299,16 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     for (int u = 0; u < U; ++u) {
         int64_t r = r0 + (int64_t)(wave * U + u) * RPW + rg;
         if constexpr (PAGED) {
-            // unfilled slots are never read: their loads are masked off
+            // Every row is loaded (its page is a pool page, so the read is in
+            // bounds); an unfilled slot may hold anything, so its score is
+            // replaced by -inf and its V row by zeros below.
             valid[u] = r < p.c.pcap ? r < n_pre : (r - p.c.pcap < n_ring);
             const bool is_new = fused && r == new_r;
-            const T* kp = is_new ? knew_row : reinterpret_cast<const T*>(paged_k(wave_page, r));
-            const T* vp = is_new ? vnew_row : reinterpret_cast<const T*>(paged_k(wave_page, r) + v_off);
-            kr[u] = Vec16{{0, 0, 0, 0}};
-            vr[u] = Vec16{{0, 0, 0, 0}};
-            if (valid[u]) {
-                kr[u] = load16_stream<NTL>(kp + sub * VEC);
-                vr[u] = load16_stream<NTL>(vp + sub * VEC);
-            }
+            const char* ka = lane_k + (int64_t)u * RPW * kRowBytes;
+            const T* kp = is_new ? knew_row : reinterpret_cast<const T*>(ka);
+            const T* vp = is_new ? vnew_row : reinterpret_cast<const T*>(ka + v_off);
+            kr[u] = load16_stream<NTL>(kp + sub * VEC);
+            vr[u] = load16_stream<NTL>(vp + sub * VEC);
             continue;
         }
         valid[u] = r < n;
@@ -363,6 +372,10 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float vf[VEC];
+        if constexpr (PAGED) {
+#pragma unroll
+            for (int w4 = 0; w4 < 4; ++w4) vr[u].w[w4] = valid[u] ? vr[u].w[w4] : 0u;
+        }
         Elem<T>::unpack(vr[u], vf);
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
