@@ -169,19 +169,51 @@ constexpr int kRowBytes = 128 * 2;       // one K or V row (head_dim 128, bf16)
 constexpr int kTileBytes = kBNB * kRowBytes;
 constexpr int kStageBytes = 2 * kTileBytes;  // K tile then V tile
 
-// Both tiles are row-major (row = key, 256 bytes) with 16-byte chunks
-// xor-swizzled by row so that the operand reads hit every LDS bank once:
-//  K: chunk c of row r at c ^ (r & 15)   (8 consecutive rows, same chunk, per
-//     16-byte read group);
-//  V: chunk c of row r at c ^ 2(r & 3)   (4 consecutive rows, two chunks, per
-//     16-lane transposing read).
+// Both tiles are row-major (row = key, 256 bytes = all 64 LDS banks once)
+// with 16-byte chunks xor-swizzled by row so that the operand reads hit every
+// bank once per cycle:
+//  K: chunk c of row r at c ^ (r & 15): a 16-byte read serves 16 lanes per
+//     cycle, 16 consecutive rows at the same logical chunk;
+//  V: chunk c of row r at c ^ 4(r & 3): an 8-byte transposing read serves 32
+//     lanes per cycle, rows 4h .. 4h + 3 at logical chunks 4m .. 4m + 3, and
+//     4(r & 3) spreads those 16 chunks over 16 distinct bank quads.  (With
+//     c ^ 2(r & 3) the two 16-lane halves land on the same 32 banks: a 2-way
+//     conflict on every V^T read.)
 __device__ inline int k_chunk_swz(int row) { return row & 15; }
-__device__ inline int v_chunk_swz(int row) { return 2 * (row & 3); }
+__device__ inline int v_chunk_swz(int row) { return 4 * (row & 3); }
 
-// Buffer resource (V#) over [base, base + bytes): loads at offsets past the
-// end return zero, so partial tiles need no per-lane checks.
-__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+// 32-bit LDS address of a pointer into shared memory.
+__device__ inline uint32_t lds_addr(const char* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Buffer resource (V#) over [base, base + bytes), as four uniform words:
+// loads at offsets past the end return zero, so partial tiles need no
+// per-lane checks.
+__device__ inline i32x4 rsrc_words(const void* base, int bytes) {
+    i32x4 r;
+    r[0] = (int)(uint32_t)(uintptr_t)base;
+    r[1] = (int)(((uintptr_t)base >> 32) & 0xFFFF);
+    r[2] = bytes;
+    r[3] = 0x00020000;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
+    return r;
+}
+
+// Direct-to-LDS loads written as asm: 16 (or 4) bytes per lane from
+// rsrc + voff land at LDS address m0 + 16 (4) * lane.  The compiler does not
+// see them, so it does not make every later LDS read wait for them (with the
+// builtin it waits for all loads in flight before the first read of any
+// buffer); the kernels order them against the reads of their buffer
+// themselves (vmcnt before the barrier that hands the buffer over).  The
+// hardware counter is in order, so the compiler's own vmcnt waits only wait
+// longer for the loads it does not see.
+__device__ inline void dma16_asm(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
+}
+__device__ inline void dma4_asm(i32x4 rsrc, int voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
 }
 
 // Bits [lo, hi) of a 32-bit word, with lo and hi clamped to [0, 32].
@@ -277,16 +309,15 @@ __device__ inline void load_tile_bf16(const Cursor& c, const LaneOffsets& lo, in
     const int64_t off =
         c.shift < 0 ? (int64_t)row0 * c.rs
                     : uniform_i64(view_row_offset(c.shift, c.page_col, c.first_slot, c.page_rows, c.rs, table, row0));
-    const __amdgpu_buffer_rsrc_t kr = make_rsrc(c.k + off, nrows * c.rs);
-    const __amdgpu_buffer_rsrc_t vr = make_rsrc(c.v + off, nrows * c.rs);
     if (wave >= kLoadWaves) return;
+    const i32x4 kr = rsrc_words(c.k + off, nrows * c.rs);
+    const i32x4 vr = rsrc_words(c.v + off, nrows * c.rs);
+    const uint32_t sb = lds_addr(stage);
 #pragma unroll
     for (int i = 0; i < kLoadsPerWave; ++i) {
         const int r4 = (kBNB / kLoadWaves) * wave + 4 * i;  // first of the 4 rows this instruction fills
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            kr, (__attribute__((address_space(3))) void*)(stage + r4 * kRowBytes), 16, lo.k[i], 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            vr, (__attribute__((address_space(3))) void*)(stage + kTileBytes + r4 * kRowBytes), 16, lo.v[i], 0, 0, 0);
+        dma16_asm(kr, lo.k[i], sb + r4 * kRowBytes);
+        dma16_asm(vr, lo.v[i], sb + kTileBytes + r4 * kRowBytes);
     }
 }
 constexpr int kLoadsPerTile = 2 * kLoadsPerWave;  // vector memory instructions per thread per staged tile
@@ -321,10 +352,6 @@ __device__ inline float sum_bf16x8(const Vec16& v) {
     return acc;
 }
 
-__device__ inline uint32_t lds_addr(const char* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
-}
-
 // V^T operands of k-step ST (keys 16 ST .. 16 ST + 15) for the four dim
 // blocks, from the row-major V tile.  ds_read_b64_tr_b16 works on 16-lane
 // groups: group lane k reads 4 bf16 at its own address and lane i of the
@@ -334,9 +361,7 @@ __device__ inline uint32_t lds_addr(const char* p) {
 // head dim (32m + lane % 32) of four consecutive keys; the reads at rows
 // +0 and +8 fill the two halves of the 8-key operand.  vaddr[m] already holds
 // the swizzled LDS address of row 4h + k / 4 (h = lane / 32) for dim block m;
-// the k-step and half become immediate offsets.  (The compiler cannot tell
-// these reads from the direct-to-LDS loads in flight and waits for those
-// first; the ring's depth still hides most of their latency.)
+// the k-step and half become immediate offsets.
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 __device__ inline void read_vt(int st, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3, Vec16 (&va)[4]) {
     const uint32_t ad[4] = {a0, a1, a2, a3};
@@ -753,29 +778,6 @@ __global__ void __launch_bounds__(64) prefill_plain_kernel(PrefillParams p) {
 // query tiles that see it).  P is rebuilt from the forward's log-sum-exp, so
 // no running maximum is needed.  Tile classification is the forward's: SKIP
 // pairs cost nothing, FULL pairs run unmasked, MASKED pairs mask per element.
-
-// Direct-to-LDS loads written as asm: 16 (or 4) bytes per lane from
-// rsrc + voff land at LDS address m0 + 16 (4) * lane.  The compiler does not
-// see them, so it does not make every later LDS read wait for them; the
-// kernels order them against the reads of their buffer themselves (vmcnt
-// before the barrier that hands the buffer over).  Compiler-visible global
-// loads issued before them are waited for explicitly before the loops.
-__device__ inline i32x4 rsrc_words(const void* base, int bytes) {
-    i32x4 r;
-    r[0] = (int)(uint32_t)(uintptr_t)base;
-    r[1] = (int)(((uintptr_t)base >> 32) & 0xFFFF);
-    r[2] = bytes;
-    r[3] = 0x00020000;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r[i] = __builtin_amdgcn_readfirstlane(r[i]);
-    return r;
-}
-__device__ inline void dma16_asm(i32x4 rsrc, int voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
-__device__ inline void dma4_asm(i32x4 rsrc, int voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds" ::"v"(voff), "s"(rsrc), "{m0}"(lds) : "memory");
-}
 
 // Delta[row] = sum_d dO[row][d] * O[row][d] over rows of 128 bf16; 16 lanes
 // per row, 8 elements per lane.
