@@ -47,7 +47,7 @@ def build() -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_SO):
+        if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(os.path.join(_HERE, "oracle.c")):
             build()
         lib = ctypes.CDLL(_SO)
         i64, vp = ctypes.c_int64, ctypes.c_void_p
@@ -65,6 +65,10 @@ def _load():
         lib.oracle_attention_bwd.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
                                              i64, vp, vp, vp, vp, i64, i64, ctypes.c_double,
                                              vp, vp, vp, ctypes.c_int]
+        lib.oracle_attention_bwd_delta.restype = None
+        lib.oracle_attention_bwd_delta.argtypes = [i64, ctypes.c_int, ctypes.c_int, ctypes.c_int, vp, vp,
+                                                   i64, vp, vp, vp, vp, i64, i64, ctypes.c_double, vp,
+                                                   vp, vp, vp, ctypes.c_int]
         lib.oracle_rope_turn.restype = None
         lib.oracle_rope_turn.argtypes = [i64, ctypes.c_int, vp, vp, ctypes.c_double, vp]
         _lib = lib
@@ -149,6 +153,37 @@ def attention_bwd(q, qpos, k, v, kpos, dout, P: int, W: int, scale: float | None
     _load().oracle_attention_bwd(nq, hq, hkv, d, q.ctypes.data, qpos.ctypes.data, nk, k.ctypes.data,
                                  v.ctypes.data, kpos.ctypes.data, dout.ctypes.data, P, W, float(scale),
                                  dq.ctypes.data, dk.ctypes.data, dv.ctypes.data, int(threads))
+    return dq, dk, dv
+
+
+def attention_bwd_delta(q, qpos, k, v, kpos, dout, delta, P: int, W: int, scale: float | None = None,
+                        threads: int = 1):
+    """``attention_bwd`` with the row term D = <dout, out> of every query
+    supplied as ``delta`` [nq][hq] instead of computed (see oracle.c).
+    Returns (dq, dk, dv), float64."""
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    dout = np.ascontiguousarray(dout, dtype=np.float32)
+    qpos = np.ascontiguousarray(np.asarray(qpos, dtype=np.int64).reshape(-1))
+    kpos = np.ascontiguousarray(np.asarray(kpos, dtype=np.int64).reshape(-1))
+    nq, hq, d = q.shape
+    nk, hkv, dk_ = k.shape
+    delta = np.ascontiguousarray(delta, dtype=np.float64)
+    if (dk_ != d or v.shape != k.shape or dout.shape != q.shape or qpos.size != nq or kpos.size != nk
+            or delta.shape != (nq, hq)):
+        raise ValueError("oracle.attention_bwd_delta: inconsistent shapes")
+    if hq % hkv != 0:
+        raise ValueError("oracle.attention_bwd_delta: Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq = np.empty((nq, hq, d), dtype=np.float64)
+    dk = np.empty((nk, hkv, d), dtype=np.float64)
+    dv = np.empty((nk, hkv, d), dtype=np.float64)
+    _load().oracle_attention_bwd_delta(nq, hq, hkv, d, q.ctypes.data, qpos.ctypes.data, nk, k.ctypes.data,
+                                       v.ctypes.data, kpos.ctypes.data, dout.ctypes.data, P, W, float(scale),
+                                       delta.ctypes.data, dq.ctypes.data, dk.ctypes.data, dv.ctypes.data,
+                                       int(threads))
     return dq, dk, dv
 
 

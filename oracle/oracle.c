@@ -147,12 +147,14 @@ int oracle_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P,
  *   dv[j][g]  += p_j dO
  * Hidden keys get nothing (they are skipped).  Outputs are overwritten.
  * Parallel over kv heads: every write of one thread stays in its kv head.
+ * With delta_in non-null, D of query (t, h) is taken from delta_in[t*hq + h]
+ * instead (the same formulas with the row term given).
  */
-void oracle_attention_bwd(int64_t nq, int hq, int hkv, int d,
-                          const float* q, const int64_t* qpos,
-                          int64_t nk, const float* k, const float* v, const int64_t* kpos,
-                          const float* dout, int64_t P, int64_t W, double scale,
-                          double* dq, double* dk, double* dv, int n_threads) {
+static void attention_bwd_impl(int64_t nq, int hq, int hkv, int d,
+                               const float* q, const int64_t* qpos,
+                               int64_t nk, const float* k, const float* v, const int64_t* kpos,
+                               const float* dout, int64_t P, int64_t W, double scale, const double* delta_in,
+                               double* dq, double* dk, double* dv, int n_threads) {
     for (int64_t x = 0; x < nq * hq * (int64_t)d; ++x) dq[x] = 0.0;
     for (int64_t x = 0; x < nk * hkv * (int64_t)d; ++x) { dk[x] = 0.0; dv[x] = 0.0; }
 #pragma omp parallel for schedule(dynamic, 1) num_threads(n_threads > 0 ? n_threads : 1)
@@ -195,6 +197,7 @@ void oracle_attention_bwd(int64_t nq, int hq, int hkv, int d,
                     for (int e = 0; e < d; ++e) dpj += (double)dor[e] * (double)vr[e];
                     D += exp(s * scale - m) / l * dpj;
                 }
+                if (delta_in) D = delta_in[t * hq + h];
                 for (int64_t j = 0; j < nk; ++j) {
                     if (!oracle_visible(i, kpos[j], P, W)) continue;
                     const float* kr = k + (j * hkv + g) * (int64_t)d;
@@ -214,6 +217,30 @@ void oracle_attention_bwd(int64_t nq, int hq, int hkv, int d,
                 }
             }
     }
+}
+
+void oracle_attention_bwd(int64_t nq, int hq, int hkv, int d,
+                          const float* q, const int64_t* qpos,
+                          int64_t nk, const float* k, const float* v, const int64_t* kpos,
+                          const float* dout, int64_t P, int64_t W, double scale,
+                          double* dq, double* dk, double* dv, int n_threads) {
+    attention_bwd_impl(nq, hq, hkv, d, q, qpos, nk, k, v, kpos, dout, P, W, scale, (const double*)0, dq, dk, dv,
+                       n_threads);
+}
+
+/*
+ * The gradient above with the row term D of every query supplied by the
+ * caller (delta [nq][hq]).  A trainer that stores its forward output in a
+ * narrow type forms D = <dO, out> from the stored output; evaluating the
+ * exact formulas with that D separates the error the stored output carries
+ * into D from the error of the rest of a backward computation.
+ */
+void oracle_attention_bwd_delta(int64_t nq, int hq, int hkv, int d,
+                                const float* q, const int64_t* qpos,
+                                int64_t nk, const float* k, const float* v, const int64_t* kpos,
+                                const float* dout, int64_t P, int64_t W, double scale, const double* delta,
+                                double* dq, double* dk, double* dv, int n_threads) {
+    attention_bwd_impl(nq, hq, hkv, d, q, qpos, nk, k, v, kpos, dout, P, W, scale, delta, dq, dk, dv, n_threads);
 }
 
 /*

@@ -427,6 +427,33 @@ def test_attention_bwd_sum_invariants():
     assert np.all(dk2[-1] == 0.0) and np.all(dv2[-1] == 0.0)
 
 
+def test_attention_bwd_delta_row_term():
+    """The backward with its row term supplied: with D = <dout, out> from the
+    forward oracle it is the plain gradient; moving D by c changes ds_j by
+    -c p_j, so dq moves by -c * scale * sum_j p_j k_j (the forward oracle with
+    the keys as values), the key gradients of a kv head move in sum by
+    -c * scale * (sum of its queries), and dv does not move."""
+    P, W, L, hq, hkv, d = 3, 7, 29, 4, 2, 8
+    pos, q, k, v = rand_qkv(17, L, hq, hkv, d)
+    dout = synth.rows(18, synth.V, 0, 0, pos, hq, d, 0.0, synth.F32)
+    scale = 0.3
+    out, _ = oracle.attention(q, pos, k, v, pos, P, W, scale)
+    D = (np.asarray(dout, np.float64) * out).sum(axis=-1)
+    base = oracle.attention_bwd(q, pos, k, v, pos, dout, P, W, scale)
+    got = oracle.attention_bwd_delta(q, pos, k, v, pos, dout, D, P, W, scale)
+    for a, b in zip(base, got):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-12)
+    c = 0.37
+    dq2, dk2, dv2 = oracle.attention_bwd_delta(q, pos, k, v, pos, dout, D + c, P, W, scale)
+    pk, _ = oracle.attention(q, pos, k, k, pos, P, W, scale)
+    np.testing.assert_allclose(dq2 - got[0], -c * scale * pk, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(dv2, got[2])
+    rep = hq // hkv
+    for g in range(hkv):
+        want = -c * scale * np.asarray(q, np.float64)[:, g * rep:(g + 1) * rep, :].sum(axis=(0, 1))
+        np.testing.assert_allclose((dk2 - got[1])[:, g, :].sum(axis=0), want, rtol=0, atol=1e-11)
+
+
 # ------------------------------------------------------------------ Reset PE
 @pytest.mark.parametrize("d,base", [(128, 1e6), (128, 1e4), (64, 1e4)])
 def test_rope_turn_matches_generator_rotation(d, base):
