@@ -1221,9 +1221,15 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                 const int my_j = jw0 + col;
                 float pf[16];
                 Vec16 pb[2], sb[2];
+                // lse and Delta of the lane's rows come four at a time: rows
+                // 8a + 4h .. 8a + 4h + 3 of the half (registers 4a .. 4a + 3) are
+                // one 16-byte read, the same address for the 32 lanes of a half
+                float4 l4;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int qr_ = 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
+                    if ((r & 3) == 0) l4 = *reinterpret_cast<const float4*>(lse_s + qr_);
+                    const float lse_v = (r & 3) == 0 ? l4.x : (r & 3) == 1 ? l4.y : (r & 3) == 2 ? l4.z : l4.w;
                     float sv = s[r];
                     if (cls == kMasked || padded) {
                         const int i = S0 + ts + qr_ % QS;
@@ -1231,7 +1237,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                                          qr_ / QS < greal;
                         sv = vis ? sv : -INFINITY;
                     }
-                    pf[r] = fast_exp2(fmaf(sv, c, -lse_s[qr_] * kLog2eF));
+                    pf[r] = fast_exp2(fmaf(sv, c, -lse_v * kLog2eF));
                 }
 #pragma unroll
                 for (int st2 = 0; st2 < 2; ++st2)
@@ -1247,6 +1253,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                         vblk + vrow * kRowBytes + (((2 * kk + h) ^ b_chunk_swz(vrow)) << 4));
                     dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(da), as_bf16x8(vb), dp, 0, 0, 0);
                 }
+                float4 d4;
 #pragma unroll
                 for (int st2 = 0; st2 < 2; ++st2)
 #pragma unroll
@@ -1255,8 +1262,9 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
                         for (int e = 0; e < 2; ++e) {
                             const int r = 8 * st2 + 2 * w + e;
-                            const int qr_ = 32 * half + 8 * (r >> 2) + 4 * h + (r & 3);
-                            dv2[e] = pf[r] * (dp[r] - dlt_s[qr_]);
+                            if ((r & 3) == 0) d4 = *reinterpret_cast<const float4*>(dlt_s + 32 * half + 8 * (r >> 2) + 4 * h);
+                            const float dl = (r & 3) == 0 ? d4.x : (r & 3) == 1 ? d4.y : (r & 3) == 2 ? d4.z : d4.w;
+                            dv2[e] = pf[r] * (dp[r] - dl);
                         }
                         sb[st2].w[w] = pack_bf16x2(dv2[0], dv2[1]);
                     }
