@@ -19,6 +19,8 @@ generator.  Two comparisons per gradient:
   key dominates a row dP - Delta cancels, so that output's rounding reaches
   dq and dk almost undamped (the same sweep measured up to 6.3e-3 for it, and
   short peaky rows, T = 2 to 50, up to 1.44%); dv does not depend on Delta.
+  Without peaky rows (score scale 1) the total stays below 1e-2, which the
+  hand-picked cases assert.
 A dropped or leaked key, a wrong head or a missing scale moves some element
 by far more than either bar (the "peaky" cases spread scores over tens of
 units)."""
@@ -106,6 +108,12 @@ def test_trainer_backward_small(hq, hkv, B, T, P, W, start, scale):
         check("dk", dk[b], rk)
         check("dv", dv[b], rv)
         check_kernel_part(q[b], k[b], v[b], do[b], delta[b], pos, P, W, (dq[b], dk[b], dv[b]))
+        if scale == 1.0:
+            # non-peaky rows: no cancellation in dP - Delta, so the total
+            # error stays near the kernel's own (measured <= 2.9e-3)
+            for name, g_, r_ in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
+                fro = float(np.linalg.norm(g_ - r_) / max(np.linalg.norm(r_), 1.0))
+                assert fro <= 1e-2, ("non-peaky total", name, fro)
         # Delta is rowsum(dout * out) of the bf16 forward output
         np.testing.assert_allclose(delta[b], np.sum(as_f32(do[b]) * out[b], axis=-1), rtol=0, atol=1e-3)
 
