@@ -1290,8 +1290,14 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
         if (n + 2 < n_sub) stage_sub(n + 2, stage0 + (n & 1) * kSubStage);
     }
 
-    if (col >= wk_n) return;
-    const int64_t kel = (((int64_t)b * T + wk0 + col) * hkv + g) * D;
+    // The lane index is taken afresh here (mbcnt in asm, which the compiler
+    // cannot equate with the one above): otherwise it keeps the lane-derived
+    // values live across the loop and spills them at 256 VGPRs.
+    int lane_e;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane_e));
+    const int col_e = lane_e & 31, h_e = lane_e >> 5;
+    if (col_e >= wk_n) return;
+    const int64_t kel = (((int64_t)b * T + wk0 + col_e) * hkv + g) * D;
     uint16_t* dkp = reinterpret_cast<uint16_t*>(bp.dk) + kel;
     uint16_t* dvp = reinterpret_cast<uint16_t*>(bp.dv) + kel;
 #pragma unroll
@@ -1303,8 +1309,8 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
             wk.w[1] = pack_bf16x2(dkacc[m][4 * cc4 + 2] * bp.scale, dkacc[m][4 * cc4 + 3] * bp.scale);
             wv.w[0] = pack_bf16x2(dvacc[m][4 * cc4], dvacc[m][4 * cc4 + 1]);
             wv.w[1] = pack_bf16x2(dvacc[m][4 * cc4 + 2], dvacc[m][4 * cc4 + 3]);
-            *reinterpret_cast<Vec8*>(dkp + 32 * m + 8 * cc4 + 4 * h) = wk;
-            *reinterpret_cast<Vec8*>(dvp + 32 * m + 8 * cc4 + 4 * h) = wv;
+            *reinterpret_cast<Vec8*>(dkp + 32 * m + 8 * cc4 + 4 * h_e) = wk;
+            *reinterpret_cast<Vec8*>(dvp + 32 * m + 8 * cc4 + 4 * h_e) = wv;
         }
 }
 
