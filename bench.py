@@ -15,7 +15,9 @@ Printed as one JSON line (rank 0, N=1):
   cpu_baseline the CPU oracle on a bounded sample of the same workload
   prefill      chunked prefill (28 layers, P=1024, W=8192, 4096 queries at
                98304..102399) and trainer forward (B=8, T=8192, P=256,
-               W=2048): TFLOP/s on exact visible pairs and on unskipped tiles
+               W=2048): TFLOP/s on exact visible pairs and on unskipped tiles;
+               trainer_phases: cycles per wave and tile in each phase of the
+               forward's tile loop (the kernel's traced copy, one launch)
   baselines    full attention (W >= L) and a vanilla sliding window (P = 0)
                through the same decode kernel from 2K to 128K, beside
                Prefix Sliding (attention-only tok/s)
@@ -780,6 +782,7 @@ def prefill_bench(torch, ps, synth, np):
                       "tflops_tiles": round(ft / ms / 1e9, 1),
                       "frac_mfma_tiles": round(ft / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"trainer forward: {res['trainer']}")
+    res["trainer_phases"] = prefill_phases(torch, ps, q, k, v, out, Pt, Wt, scale, stream)
 
     # trainer backward of the same forward: Delta, dQ, dK/dV
     lse = torch.empty(B, T, HQ, device="cuda")
@@ -806,6 +809,27 @@ def prefill_bench(torch, ps, synth, np):
                                "ms": round(ms, 3), "tflops_exact": round(fb / ms / 1e9, 1),
                                "frac_mfma_exact": round(fb / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"trainer backward: {res['trainer_backward']}")
+    return res
+
+
+def prefill_phases(torch, ps, q, k, v, out, P_, W_, scale, stream):
+    """Shader-clock cycles per wave and key tile in each phase of the forward's
+    tile loop (the traced copy of the kernel, ps.h "prefill phase trace"), for
+    the stager waves 0-3 and for waves 4-7, after a few untraced launches."""
+    tr = torch.zeros(2, 8, dtype=torch.int64, device="cuda")
+    for _ in range(3):
+        ps.ps_prefill_attn(q, k, v, out, start_pos=0, prefix_len=P_, window=W_, scale=scale, stream=stream)
+    ps.ps_prefill_attn(q, k, v, out, start_pos=0, prefix_len=P_, window=W_, scale=scale, stream=stream, trace=tr)
+    torch.cuda.synchronize()
+    t = tr.cpu().tolist()
+    names = ["scores", "mask_and_max", "exp_and_pv", "load_wait", "barrier", "load_issue"]
+    res = {"note": "s_memtime cycles per wave and 128-key tile, one traced trainer forward; "
+                   "waves 0-3 stage the tiles"}
+    for grp, label in ((0, "waves_0_3"), (1, "waves_4_7")):
+        wave_tiles = max(t[grp][6], 1)
+        res[label] = {n: round(t[grp][i] / wave_tiles, 1) for i, n in enumerate(names)}
+        res[label]["loop_total"] = round(t[grp][7] / wave_tiles, 1)
+    log(f"trainer forward phases: {res}")
     return res
 
 

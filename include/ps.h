@@ -346,7 +346,22 @@ typedef struct {
                                    NULL: prefix_len; only together with starts */
     const int32_t* page_table;  /* paged cache: device [B][pages per sequence] page
                                    table (see ps_seq_batch), else NULL */
+    uint64_t* trace;            /* NULL, or a phase trace (a profiling aid): a
+                                   device array [2][8] of uint64 the caller owns
+                                   and clears; see below */
 } ps_prefill_args;
+
+/* Prefill phase trace.  With args->trace non-NULL a call that runs on the
+ * MFMA kernel (bf16, head_dim 128) runs a copy of it that reads the shader
+ * clock (s_memtime) around each phase of its tile loop and adds, per wave,
+ * the cycles spent into trace[grp][k], grp 0 for waves 0-3 (they stage the
+ * key tiles), 1 for waves 4-7:
+ *   k = 0 scores (S^T = K Q^T), 1 mask and row maximum, 2 exponentials and
+ *   P.V, 3 wait for the next tile's loads, 4 barrier, 5 issuing the next
+ *   tile's loads, 6 tiles processed, 7 cycles from kernel entry to the end
+ *   of the tile loop.
+ * The traced copy computes the same results (bit for bit); the clock reads
+ * and their waits cost a little time.  Other shapes ignore the field. */
 
 /* bf16 with head_dim 128 and a GQA group of 1 to 8 runs on the MFMA kernel
  * (groups 3 and 5-7 on the layout of the next power of two, the missing

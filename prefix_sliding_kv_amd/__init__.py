@@ -57,7 +57,7 @@ class _PrefillArgs(ctypes.Structure):
                 ("rows", ctypes.c_void_p), ("q", ctypes.c_void_p), ("k", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p),
                 ("scale", ctypes.c_float), ("prefix_rows", ctypes.c_void_p), ("starts", ctypes.c_void_p),
-                ("prefix_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p)]
+                ("prefix_lens", ctypes.c_void_p), ("page_table", ctypes.c_void_p), ("trace", ctypes.c_void_p)]
 
 
 class _PrefillBwdArgs(ctypes.Structure):
@@ -301,12 +301,13 @@ def ps_decode_step(handle: int, layer: int, batch: SeqBatch, q, k_new, v_new, ou
 def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: int, scale: float,
                     lse=None, cache: int | None = None, layer: int = 0, rows=None,
                     prefix_rows=None, starts=None, prefix_lens=None, dtype: int | None = None,
-                    stream=None, page_table=None) -> None:
+                    stream=None, page_table=None, trace=None) -> None:
     """q/out [B][T][Hq][d], k/v [B][T][Hkv][d] CUDA tensors; ``cache`` None means
     trainer mode (self-attention over the given tokens only).  ``starts``
     (int64 [B]) and ``prefix_lens`` (int32 [B]) give ragged chunks: per-sequence
     start positions and prefix lengths (then ``start_pos``/``prefix_len`` are
-    not used for the sequences)."""
+    not used for the sequences).  ``trace`` (uint64 [2][8], zeroed by the
+    caller) turns on the phase trace of the MFMA kernel (see ps.h)."""
     B, T, hq, d = q.shape
     hkv = k.shape[2]
     if dtype is None:
@@ -317,7 +318,10 @@ def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: in
                      prefix_rows.data_ptr() if prefix_rows is not None else 0,
                      starts.data_ptr() if starts is not None else 0,
                      prefix_lens.data_ptr() if prefix_lens is not None else 0,
-                     page_table.data_ptr() if page_table is not None else 0)
+                     page_table.data_ptr() if page_table is not None else 0,
+                     trace.data_ptr() if trace is not None else 0)
+    if trace is not None:
+        assert trace.dtype == torch.int64 and trace.numel() >= 16 and trace.is_cuda
     if starts is not None:
         assert starts.dtype == torch.int64 and starts.numel() == B
     if prefix_lens is not None:

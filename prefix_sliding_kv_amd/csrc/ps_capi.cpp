@@ -585,6 +585,7 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
     p.scale_log2 = a->scale * kLog2e;
     p.starts = a->starts;
     p.plens = ragged ? a->prefix_lens : nullptr;
+    p.trace = reinterpret_cast<unsigned long long*>(a->trace);
     return hip_status(ps::launch_prefill(dtype, d, group, p, (hipStream_t)stream));
 }
 

@@ -329,6 +329,7 @@ struct PrefillParams {
     int32_t cache_mode;
     PrefillCache cache;
     const uint32_t* guard;  // checks on: the cache's flag word; the kernel does nothing while it is set
+    unsigned long long* trace;  // phase trace [2][8] (bf16 MFMA kernel only), or null
 };
 
 // Positions enter the visibility rule only through j < P and i - W < j <= i,

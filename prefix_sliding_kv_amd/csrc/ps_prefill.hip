@@ -386,12 +386,29 @@ __device__ inline int tile_class32(int i0, int i1, int j0, int j1, int P, int W)
 // One workgroup of 8 waves per CU owns 256 query rows: the G heads of a GQA
 // group stacked over 256/G positions; wave w owns rows 32w .. 32w + 31, so
 // every key tile staged in LDS serves all heads of the group.
-template <int G>
+// TRACE: the same kernel reading the shader clock around each phase of the
+// tile loop (the prefill phase trace of ps.h); the results are identical.
+template <int G, bool TRACE = false>
 __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams p) {
     constexpr int D = 128;
     constexpr int QP = 32 * kWaves / G;  // positions per query tile
     extern __shared__ __attribute__((aligned(16))) char smem[];
     if (p.guard && *p.guard) return;  // checks on and a check failed
+    // phase cycle sums of this wave (TRACE only): scores, mask + maximum,
+    // P.V, load wait, barrier, load issue
+    uint32_t tr_acc[6] = {0, 0, 0, 0, 0, 0};
+    uint64_t tr_last = 0, tr_entry = 0;
+    auto tr_mark = [&](int k) __attribute__((always_inline)) {
+        if constexpr (TRACE) {
+            const uint64_t t = __builtin_amdgcn_s_memtime();
+            if (k >= 0) tr_acc[k] += (uint32_t)(t - tr_last);
+            tr_last = t;
+        }
+    };
+    if constexpr (TRACE) {
+        tr_mark(-1);
+        tr_entry = tr_last;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -508,6 +525,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
 
     constexpr int kMB = kBNB / 32;  // 32-key score blocks per tile
     constexpr int kST = kBNB / 16;  // 16-key k-steps of P.V per tile
+    tr_mark(-1);
     for (int f = 0; f < total; ++f) {
         const int row0 = cc.t * kBNB;
         const int nrows = cc.n - row0 < kBNB ? cc.n - row0 : kBNB;
@@ -532,6 +550,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
                 }
         }
         __builtin_amdgcn_sched_barrier(0);
+        tr_mark(0);
 
         // Elementwise mask, straddling tiles only.  For this lane's query the
         // visible keys of the tile (tile-relative index kr) form at most two
@@ -582,6 +601,7 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         }
         const float mc = m_run == -INFINITY ? 0.f : m_run * c;
         __builtin_amdgcn_sched_barrier(0);
+        tr_mark(1);
 
         // O^T += V^T P^T, k-step by k-step.  P^T of k-step st (keys 16 st ..
         // 16 st + 15, exp2((s - m) * c) packed to bf16) is made right before
@@ -608,13 +628,26 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
             }
         }
         __builtin_amdgcn_sched_barrier(0);
+        tr_mark(2);
 
         // tile f + 1 must have landed before anyone reads it; then the stage
         // of tile f takes tile f + 2
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        tr_mark(3);
         tile_barrier();
+        tr_mark(4);
         if (f + kStages < total) stage_next(smem + (f & 1) * kStageBytes);
         cursor_next(cc, walk.n_ranges, walk, views);
+        tr_mark(5);
+    }
+    if constexpr (TRACE) {
+        if (lane == 0 && p.trace) {
+            unsigned long long* tr = p.trace + 8 * (wave >= kLoadWaves ? 1 : 0);
+#pragma unroll
+            for (int k = 0; k < 6; ++k) atomicAdd(tr + k, (unsigned long long)tr_acc[k]);
+            atomicAdd(tr + 6, (unsigned long long)total);
+            atomicAdd(tr + 7, (unsigned long long)(__builtin_amdgcn_s_memtime() - tr_entry));
+        }
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
@@ -642,7 +675,7 @@ inline int layout_group(int group) { return group <= 2 ? group : (group <= 4 ? 4
 // current device (a host call made once per kernel and device).
 constexpr int kMaxDevices = 64;
 inline bool* lds_flag(int slot) {
-    static bool flags[kMaxDevices][8] = {};
+    static bool flags[kMaxDevices][12] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     return &flags[dev][slot];
@@ -1323,27 +1356,39 @@ hipError_t launch_prefill(int dtype, int head_dim, int group, const PrefillParam
         const int qp = 32 * kWaves / group;
         dim3 grid((unsigned)(((p.seq_len + qp - 1) / qp) * p.hkv * p.batch));
         const size_t lds = (size_t)kStages * kStageBytes;
+        // the traced copy (phase trace) is a kernel of its own, with its own
+        // LDS-limit flag
+        const bool traced = p.trace != nullptr;
         const void* fn = nullptr;
         switch (group) {
-            case 1: fn = (const void*)prefill_bf16_kernel<1>; break;
-            case 2: fn = (const void*)prefill_bf16_kernel<2>; break;
-            case 4: fn = (const void*)prefill_bf16_kernel<4>; break;
-            case 8: fn = (const void*)prefill_bf16_kernel<8>; break;
+            case 1: fn = traced ? (const void*)prefill_bf16_kernel<1, true> : (const void*)prefill_bf16_kernel<1>; break;
+            case 2: fn = traced ? (const void*)prefill_bf16_kernel<2, true> : (const void*)prefill_bf16_kernel<2>; break;
+            case 4: fn = traced ? (const void*)prefill_bf16_kernel<4, true> : (const void*)prefill_bf16_kernel<4>; break;
+            case 8: fn = traced ? (const void*)prefill_bf16_kernel<8, true> : (const void*)prefill_bf16_kernel<8>; break;
             default: return hipErrorInvalidValue;
         }
         // raise the dynamic LDS limit once per kernel and device (a host call, not per launch)
         const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
-        bool* set = lds_flag(gi);
+        bool* set = lds_flag(traced ? 8 + gi : gi);
         if (!set || !*set) {
             const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
             if (set) *set = true;
         }
-        switch (group) {
-            case 1: hipLaunchKernelGGL(prefill_bf16_kernel<1>, grid, dim3(kThreads), lds, stream, p); break;
-            case 2: hipLaunchKernelGGL(prefill_bf16_kernel<2>, grid, dim3(kThreads), lds, stream, p); break;
-            case 4: hipLaunchKernelGGL(prefill_bf16_kernel<4>, grid, dim3(kThreads), lds, stream, p); break;
-            case 8: hipLaunchKernelGGL(prefill_bf16_kernel<8>, grid, dim3(kThreads), lds, stream, p); break;
+        if (traced) {
+            switch (group) {
+                case 1: hipLaunchKernelGGL((prefill_bf16_kernel<1, true>), grid, dim3(kThreads), lds, stream, p); break;
+                case 2: hipLaunchKernelGGL((prefill_bf16_kernel<2, true>), grid, dim3(kThreads), lds, stream, p); break;
+                case 4: hipLaunchKernelGGL((prefill_bf16_kernel<4, true>), grid, dim3(kThreads), lds, stream, p); break;
+                case 8: hipLaunchKernelGGL((prefill_bf16_kernel<8, true>), grid, dim3(kThreads), lds, stream, p); break;
+            }
+        } else {
+            switch (group) {
+                case 1: hipLaunchKernelGGL(prefill_bf16_kernel<1>, grid, dim3(kThreads), lds, stream, p); break;
+                case 2: hipLaunchKernelGGL(prefill_bf16_kernel<2>, grid, dim3(kThreads), lds, stream, p); break;
+                case 4: hipLaunchKernelGGL(prefill_bf16_kernel<4>, grid, dim3(kThreads), lds, stream, p); break;
+                case 8: hipLaunchKernelGGL(prefill_bf16_kernel<8>, grid, dim3(kThreads), lds, stream, p); break;
+            }
         }
         return hipGetLastError();
     }

@@ -240,3 +240,33 @@ def test_fp32_chunk_over_9216_cached_keys():
     ref, ref_lse = oracle.attention(q[0], pos, kall, vall, kpos, P, W, 1.0 / math.sqrt(d), threads=16)
     np.testing.assert_allclose(dev_to_f32(out)[0], ref, rtol=0, atol=tol(DT_F32))
     np.testing.assert_allclose(dev_to_f32(lse)[0], ref_lse, rtol=0, atol=lse_tol(DT_F32))
+
+
+@pytest.mark.parametrize("hq,hkv,B,T,P,W", [(4, 2, 2, 700, 40, 300), (8, 1, 1, 513, 0, 1000)])
+def test_phase_trace_is_observation_only(hq, hkv, B, T, P, W):
+    """The traced copy of the MFMA kernel (args->trace) writes the same bytes
+    as the plain kernel, and its counters add up: every wave group reports
+    the tiles the walk visits, and the phase sums stay within the loop's
+    total."""
+    note(f"phase trace hq={hq} hkv={hkv} B={B} T={T} P={P} W={W}")
+    d = 128
+    pos, q, k, v = chunk_inputs(31, 0, B, 0, T, hq, hkv, d, 1e4, DT_BF16, 3.0)
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    outs = []
+    tr = torch.zeros(2, 8, dtype=torch.int64, device="cuda")
+    for trace in (None, tr):
+        out = torch.empty(qd.shape, device="cuda", dtype=qd.dtype)
+        lse = torch.empty(B, T, hq, device="cuda")
+        ps.ps_prefill_attn(qd, kd, vd, out, start_pos=0, prefix_len=P, window=W, scale=1.0 / math.sqrt(d),
+                           lse=lse, trace=trace)
+        torch.cuda.synchronize()
+        outs.append((out.view(torch.int16).cpu(), lse.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    t = tr.cpu().numpy().astype(np.int64)
+    G = hq // hkv
+    layout = G if G in (1, 2, 4, 8) else (4 if G <= 4 else 8)
+    n_wg = -(-T // (256 // layout)) * hkv * B
+    assert t[0, 6] == t[1, 6] > 0 and t[0, 6] % (4 * 1) == 0  # each of the 4 waves of a group adds the same count
+    assert t[0, 6] // 4 >= n_wg  # at least one tile per workgroup
+    for grp in range(2):
+        assert np.all(t[grp, :6] > 0) and t[grp, :6].sum() <= t[grp, 7]
