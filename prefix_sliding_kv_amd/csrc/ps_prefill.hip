@@ -225,6 +225,12 @@ __device__ inline uint32_t range_bits(int lo, int hi) {
 }
 
 __device__ inline int uniform_int(int x) { return __builtin_amdgcn_readfirstlane(x); }
+// A uniform read of device memory the kernel does not write, through the
+// scalar data cache (s_load).
+template <typename V>
+__device__ inline V scalar_load(const V* ptr) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) V*>(reinterpret_cast<uintptr_t>(ptr));
+}
 __device__ inline const char* uniform_ptr(const char* p) {
     const uint64_t u = (uint64_t)p;
     return (const char*)(((uint64_t)(uint32_t)uniform_int((int)(u >> 32)) << 32) | (uint32_t)uniform_int((int)(uint32_t)u));
@@ -240,6 +246,11 @@ __device__ inline int64_t uniform_i64(int64_t x) {
 // everything that matters; __syncthreads would add a release fence that
 // waits for every direct-to-LDS load still in flight, prefetches included.
 __device__ inline void tile_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Workgroup barrier for data in LDS: every wave's LDS operations (and scalar
+// loads) have completed; vector memory loads still in flight stay in flight
+// (__syncthreads would wait for those as well).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // A position in the tile walk: range r, tile t of its run, end of the range,
 // and the run's geometry.  Everything is uniform across a wave and lives in
@@ -425,8 +436,11 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     // chunk (pos_frame; the host moved uniform chunks already): there every
     // position is below 2^31 (the host checks the bound), so positions are
     // handled in 32 bits.
-    const int64_t S_abs = p.starts ? p.starts[b] : p.start_pos;
-    const int64_t P_abs = p.plens ? (int64_t)p.plens[b] : p.P;
+    // (scalar loads: a pending vector load read under a condition would make
+    // the compiler wait for every vector load, the query loads included, at
+    // its first use past the planning barriers)
+    const int64_t S_abs = p.starts ? scalar_load(p.starts + b) : p.start_pos;
+    const int64_t P_abs = p.plens ? (int64_t)scalar_load(p.plens + b) : p.P;
     const PosFrame fr = p.starts ? pos_frame(S_abs, p.seq_len, P_abs, p.W, !p.cache_mode)
                                  : PosFrame{P_abs, p.W, 0, 0};
     const int64_t S = S_abs - fr.shift, Pb = fr.P;
@@ -448,6 +462,34 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     const int my_t = t0 + qrow % QP;
     const bool q_ok = my_t < p.seq_len && hh < greal;
     const int my_i = (int)S + my_t;
+
+    // The walk over the key tiles is planned by thread 0 from the key runs in
+    // LDS.  Uniform chunks copy the runs from the kernel arguments, each wave
+    // 16 words with scalar loads (thread 0 copying them field by field takes
+    // several microseconds of dependent loads); ragged chunks build each
+    // sequence's runs on thread 0.  Scalar loads and LDS count in lgkmcnt,
+    // and the barriers around the planning wait for that counter only, so
+    // the query loads below stay in flight through the planning.
+    __shared__ TileWalk walk;
+    __shared__ RunView views[kMaxRuns];
+    __shared__ KeyRun s_runs[kMaxRuns];
+    __shared__ int32_t s_table[kMaxPagesPerSeq];  // paged layout: the sequence's page table row
+    static_assert(sizeof(KeyRun) % 4 == 0 && kMaxRuns * sizeof(KeyRun) / 4 <= 16 * kWaves, "16 words per wave");
+    const int run_words = p.starts ? 0 : p.n_runs * (int)(sizeof(KeyRun) / 4);
+    uint32_t run_word = 0;  // word 16 * wave + lane of the run table (lanes 0-15)
+    {
+        // uniform indexes: the words stay inside the kernel argument block
+        // (the run table is followed by more arguments)
+        static_assert(16 * kWaves * 4 <= sizeof(PrefillParams) - offsetof(PrefillParams, runs),
+                      "every wave's 16 words lie inside the parameter block");
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(p.runs) + 16 * wave;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const uint32_t wd = src[j];
+            run_word = lane == j ? wd : run_word;
+        }
+    }
+
     Vec16 qreg[8];
     {
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(p.q) +
@@ -457,19 +499,17 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
             qreg[ks] = q_ok ? *reinterpret_cast<const Vec16*>(qp + 8 * h + 16 * ks) : Vec16{{0, 0, 0, 0}};
     }
 
-    __shared__ TileWalk walk;
-    __shared__ RunView views[kMaxRuns];
-    __shared__ KeyRun s_runs[kMaxRuns];
-    __shared__ int32_t s_table[kMaxPagesPerSeq];  // paged layout: the sequence's page table row
+    if (lane < 16 && 16 * wave + lane < run_words) reinterpret_cast<uint32_t*>(s_runs)[16 * wave + lane] = run_word;
     if (p.cache_mode && p.cache.pages)
         for (int j = tid; j < p.cache.pages_per_seq; j += kThreads)
             s_table[j] = p.cache.pages[(int64_t)b * p.cache.pages_per_seq + j];
+    lds_barrier();
     if (tid == 0) {
-        const int n_runs = seq_key_runs(p, b, S_abs, P_abs, fr, s_runs);
+        const int n_runs = p.starts ? seq_key_runs(p, b, S_abs, P_abs, fr, s_runs) : p.n_runs;
         plan_walk<kBNB>(s_runs, n_runs, Pb, fr.W, (int64_t)i0, (int64_t)i1, walk);
         for (int r = 0; r < n_runs; ++r) make_view(views[r], s_runs[r], b, g, p.hkv, 2);
     }
-    __syncthreads();
+    lds_barrier();
     int total = 0;
     for (int r = 0; r < walk.n_ranges; ++r) total += walk.end[r] - walk.begin[r];
 
@@ -513,14 +553,15 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
     };
     static_assert(kStages == 2 && kLoadsPerTile == 16, "vmcnt immediates assume 2 stages of 16 loads");
 
-    // prologue: tiles 0 and 1 in flight, wait for tile 0
+    // prologue: tile 0 in flight beside the query loads; both have landed
+    // before tile 1 is issued.  (The query registers are waited for here, once:
+    // left to the compiler, that wait would sit at their first use inside the
+    // tile loop and drain the tile prefetch on every iteration.)
     if (total > 0) stage_next(smem);
-    if (total > 1) {
-        stage_next(smem + kStageBytes);
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(qreg[ks].w[0]), "v"(qreg[ks].w[3]));
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (total > 1) stage_next(smem + kStageBytes);
     tile_barrier();
 
     constexpr int kMB = kBNB / 32;  // 32-key score blocks per tile
