@@ -683,8 +683,10 @@ def r1_distill_bench(torch, ps, np):
     do = torch.randn_like(q)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(B, T, hq, device="cuda")
+    ds_work = torch.empty(ps.ps_prefill_bwd_ds_bytes(B, T, hq, hkv, start_pos=0, prefix_len=Pt, window=Wt),
+                          dtype=torch.uint8, device="cuda")
     bwd = lambda: ps.ps_prefill_attn_bwd(q, k, v, o, lse, do, dq, dk, dv, delta, start_pos=0, prefix_len=Pt,
-                                         window=Wt, scale=scale, stream=stream)
+                                         window=Wt, scale=scale, stream=stream, ds_work=ds_work)
     fx = exact_flops(0, T, Pt, Wt, hq, D) * B
     for name, fn, flops in (("trainer_forward", fwd, fx), ("trainer_backward", bwd, 2.5 * fx)):
         for _ in range(10):
@@ -696,7 +698,8 @@ def r1_distill_bench(torch, ps, np):
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 5
-        res[name] = {"config": "B=8, T=8192, P=256, W=2048", "ms": round(t, 3),
+        res[name] = {"config": "B=8, T=8192, P=256, W=2048" + (", stored dS" if name == "trainer_backward" else ""),
+                     "ms": round(t, 3),
                      "tflops_exact": round(flops / t / 1e9, 1),
                      "frac_mfma_exact": round(flops / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
     log(f"R1-Distill-Qwen-7B shape: {res}")
@@ -790,24 +793,39 @@ def prefill_bench(torch, ps, synth, np):
     do = torch.stack([bf16_dev(torch, synth.rows(1, synth.V, 1, b, pos, HQ, D)) for b in range(B)])
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     delta = torch.empty(B, T, HQ, device="cuda")
-    run3 = lambda: ps.ps_prefill_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, start_pos=0, prefix_len=Pt,
-                                          window=Wt, scale=scale, stream=stream)
-    for _ in range(5):
-        run3()
-    torch.cuda.synchronize()
-    reps = 5
-    e0.record(stream)
-    for _ in range(reps):
-        run3()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
+    # stored dS (the dK/dV pass writes dS, dQ reads it) and, for comparison,
+    # dS rebuilt by the dQ pass; alternated in one process, median of rounds
+    ds_bytes = ps.ps_prefill_bwd_ds_bytes(B, T, HQ, HKV, start_pos=0, prefix_len=Pt, window=Wt)
+    ds_work = torch.empty(ds_bytes, dtype=torch.uint8, device="cuda")
+    runs = {
+        "stored": lambda: ps.ps_prefill_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, start_pos=0,
+                                                 prefix_len=Pt, window=Wt, scale=scale, stream=stream,
+                                                 ds_work=ds_work),
+        "rebuilt": lambda: ps.ps_prefill_attn_bwd(q, k, v, out, lse, do, dq, dk, dv, delta, start_pos=0,
+                                                  prefix_len=Pt, window=Wt, scale=scale, stream=stream),
+    }
+    times = {name: [] for name in runs}
+    for _ in range(3):
+        for name, fn in runs.items():
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(5):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times[name].append(e0.elapsed_time(e1) / 5)
     # five products of the size of one forward product per visible pair:
     # S (recomputed), dP, dV, dK, dQ
     fb = exact_flops(0, T, Pt, Wt, HQ, D) * B * 2.5
-    res["trainer_backward"] = {"workload": "backward of the trainer forward above (dq, dk, dv)",
+    ms = sorted(times["stored"])[1]
+    ms_r = sorted(times["rebuilt"])[1]
+    res["trainer_backward"] = {"workload": "backward of the trainer forward above (dq, dk, dv), stored dS",
                                "ms": round(ms, 3), "tflops_exact": round(fb / ms / 1e9, 1),
-                               "frac_mfma_exact": round(fb / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}
+                               "frac_mfma_exact": round(fb / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4),
+                               "ds_workspace_bytes": ds_bytes,
+                               "rebuilt_dS": {"ms": round(ms_r, 3), "tflops_exact": round(fb / ms_r / 1e9, 1)}}
     log(f"trainer backward: {res['trainer_backward']}")
     return res
 

@@ -398,11 +398,26 @@ int ps_prefill_attn(const ps_prefill_args* args, void* stream);
  * bf16 only, head_dim 128, GQA group 1 to 8.  Stream-ordered: Delta, then
  * dk/dv, then dq, on the given stream.
  *
+ * Stored dS (optional): with ds_work non-NULL the dk/dv pass also writes dS
+ * (bf16, per query head) into that caller-owned device workspace, and dq is
+ * taken from it (dq = scale dS K) instead of rebuilding S and dP a second
+ * time: two of the seven products of the backward go away for HBM traffic of
+ * twice the workspace.  The workspace holds, for each (sequence, query head,
+ * block of 32 positions), the 32 x 32 tiles of the key blocks those rows can
+ * see: ps_prefill_bwd_ds_bytes gives its size, about
+ * batch * n_q_heads * seq_len * (min(window, seq_len) + min(P', seq_len) + 64) * 2
+ * bytes with P' the prefix keys inside the chunk.  Its contents on return are
+ * unspecified; nothing needs clearing before a call.  With ds_work NULL
+ * (ds_work_bytes ignored), or when ps_prefill_bwd_ds_bytes gives 0 (one kv
+ * head's share of the workspace would reach 2^31 bytes), S and dP are
+ * rebuilt and ds_work is not touched.
+ *
  * Errors: PS_ERR_INVALID (NULL pointer, batch < 1, seq_len < 0, start_pos < 0,
  * prefix_len < 0, window < 1, n_q_heads not a multiple of n_kv_heads, scale
  * <= 0 or not finite), PS_ERR_UNSUPPORTED (dtype other than bf16, head_dim
  * other than 128, another GQA group, start_pos + seq_len above 2^62),
- * PS_ERR_HIP. */
+ * PS_ERR_CAPACITY (ds_work non-NULL with ds_work_bytes below
+ * ps_prefill_bwd_ds_bytes), PS_ERR_HIP. */
 typedef struct {
     int32_t batch;          /* B >= 1 */
     int32_t seq_len;        /* T >= 0 (0: nothing to do) */
@@ -424,9 +439,21 @@ typedef struct {
     void* dv;
     float* delta;           /* workspace [B][T][n_q_heads] fp32 */
     float scale;            /* the forward's multiplier of q.k, > 0 */
+    void* ds_work;          /* optional stored-dS workspace (device), or NULL */
+    int64_t ds_work_bytes;  /* its size in bytes */
 } ps_prefill_bwd_args;
 
 int ps_prefill_attn_bwd(const ps_prefill_bwd_args* args, void* stream);
+
+/* Bytes of the stored-dS workspace ps_prefill_attn_bwd takes for these
+ * arguments (only batch, seq_len, n_q_heads, n_kv_heads, start_pos,
+ * prefix_len and window are read; no device call), written to *bytes: 0 when
+ * seq_len is 0 or the stored-dS path does not apply (then ds_work is unused).
+ * Errors: PS_ERR_INVALID (args or bytes NULL, batch < 1, seq_len < 0,
+ * start_pos < 0, prefix_len < 0, window < 1, n_q_heads or n_kv_heads < 1,
+ * n_q_heads not a multiple of n_kv_heads), PS_ERR_UNSUPPORTED
+ * (start_pos + seq_len above 2^62). */
+int ps_prefill_bwd_ds_bytes(const ps_prefill_bwd_args* args, int64_t* bytes);
 
 /* The same trainer backward for callers that cannot allocate device memory
  * (code under graph capture, tight serving loops, harnesses that forbid

@@ -67,7 +67,8 @@ class _PrefillBwdArgs(ctypes.Structure):
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("out", ctypes.c_void_p), ("lse", ctypes.c_void_p), ("dout", ctypes.c_void_p),
                 ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
-                ("delta", ctypes.c_void_p), ("scale", ctypes.c_float)]
+                ("delta", ctypes.c_void_p), ("scale", ctypes.c_float), ("ds_work", ctypes.c_void_p),
+                ("ds_work_bytes", ctypes.c_int64)]
 
 
 _vp, _i32, _i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
@@ -94,6 +95,7 @@ _SIGS = {
     "ps_prefill_attn": (ctypes.c_int, [ctypes.POINTER(_PrefillArgs), _vp]),
     "ps_prefill_attn_bwd": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), _vp]),
     "ps_prefill_attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), _vp]),
+    "ps_prefill_bwd_ds_bytes": (ctypes.c_int, [ctypes.POINTER(_PrefillBwdArgs), ctypes.POINTER(_i64)]),
     "ps_block_pool_create": (ctypes.c_int, [_i32, ctypes.POINTER(_vp)]),
     "ps_block_pool_destroy": (ctypes.c_int, [_vp]),
     "ps_block_alloc": (ctypes.c_int, [_vp, ctypes.POINTER(_i32)]),
@@ -330,17 +332,30 @@ def ps_prefill_attn(q, k, v, out, *, start_pos: int, prefix_len: int, window: in
 
 
 def ps_prefill_attn_bwd(q, k, v, out, lse, dout, dq, dk, dv, delta, *, start_pos: int,
-                        prefix_len: int, window: int, scale: float, stream=None) -> None:
+                        prefix_len: int, window: int, scale: float, stream=None, ds_work=None) -> None:
     """Trainer-mode backward: q/out/dout/dq [B][T][Hq][d], k/v/dk/dv [B][T][Hkv][d]
     bf16 CUDA tensors, lse/delta [B][T][Hq] float32 (lse from the forward,
-    delta a workspace)."""
+    delta a workspace).  ``ds_work``: optional CUDA tensor of at least
+    ps_prefill_bwd_ds_bytes(...) bytes; dq then comes from the stored dS."""
     B, T, hq, d = q.shape
     hkv = k.shape[2]
     dtype = PS_BF16 if q.dtype == torch.bfloat16 else PS_F32
+    ds_ptr, ds_bytes = (None, 0) if ds_work is None else (ds_work.data_ptr(),
+                                                          ds_work.numel() * ds_work.element_size())
     a = _PrefillBwdArgs(B, T, hq, hkv, d, dtype, start_pos, prefix_len, window, q.data_ptr(),
                         k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), dout.data_ptr(),
-                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), scale)
+                        dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(), scale, ds_ptr, ds_bytes)
     _check(lib.ps_prefill_attn_bwd(ctypes.byref(a), _stream(stream)), "ps_prefill_attn_bwd")
+
+
+def ps_prefill_bwd_ds_bytes(batch: int, seq_len: int, n_q_heads: int, n_kv_heads: int, *, start_pos: int,
+                            prefix_len: int, window: int) -> int:
+    """Bytes of the stored-dS workspace of ps_prefill_attn_bwd for these sizes
+    (0: the backward rebuilds S and dP and takes no workspace)."""
+    a = _PrefillBwdArgs(batch, seq_len, n_q_heads, n_kv_heads, 128, PS_BF16, start_pos, prefix_len, window)
+    out = _i64(0)
+    _check(lib.ps_prefill_bwd_ds_bytes(ctypes.byref(a), ctypes.byref(out)), "ps_prefill_bwd_ds_bytes")
+    return out.value
 
 
 PS_BWD_NOALLOC_MAX_ROWS = 4194304

@@ -278,6 +278,15 @@ int bwd_common(const ps_prefill_bwd_args* a, bool own_delta, void* stream) {
     p.k = a->k;
     p.v = a->v;
     p.scale = a->scale;
+    const ps::DsBand band = ps::ds_band(a->batch, T, hq, group, fr.P, fr.W);
+    if (a->ds_work && band.bytes > 0) {
+        if (a->ds_work_bytes < band.bytes) return PS_ERR_CAPACITY;
+        p.ds = static_cast<char*>(a->ds_work);
+        p.ds_nrb = (int32_t)band.nrb;
+        p.ds_npre = (int32_t)band.npre;
+        p.ds_nwin = (int32_t)band.nwin;
+        p.ds_nband = (int32_t)band.nband;
+    }
     return hip_status(ps::launch_prefill_bwd(group, p, (hipStream_t)stream));
 }
 
@@ -592,6 +601,18 @@ int ps_prefill_attn(const ps_prefill_args* a, void* stream) {
 int ps_prefill_attn_bwd(const ps_prefill_bwd_args* a, void* stream) { return bwd_common(a, false, stream); }
 
 int ps_prefill_attn_bwd_noalloc(const ps_prefill_bwd_args* a, void* stream) { return bwd_common(a, true, stream); }
+
+int ps_prefill_bwd_ds_bytes(const ps_prefill_bwd_args* a, int64_t* bytes) {
+    if (!a || !bytes) return PS_ERR_INVALID;
+    if (a->batch < 1 || a->seq_len < 0 || a->start_pos < 0 || a->prefix_len < 0 || a->window < 1 ||
+        a->n_q_heads < 1 || a->n_kv_heads < 1 || a->n_q_heads % a->n_kv_heads != 0)
+        return PS_ERR_INVALID;
+    if (a->start_pos > kMaxPos - a->seq_len) return PS_ERR_UNSUPPORTED;
+    const ps::PosFrame fr = ps::pos_frame(a->start_pos, a->seq_len, a->prefix_len, a->window, true);
+    const int group = a->n_q_heads / a->n_kv_heads;
+    *bytes = a->seq_len == 0 ? 0 : ps::ds_band(a->batch, a->seq_len, a->n_q_heads, group, fr.P, fr.W).bytes;
+    return PS_OK;
+}
 
 int ps_tile_class(int64_t i0, int64_t i1, int64_t j0, int64_t j1, int64_t P, int64_t W) {
     if (i1 < i0 || j1 < j0 || P < 0 || W < 1) return -1;

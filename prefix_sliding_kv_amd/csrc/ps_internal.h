@@ -408,7 +408,38 @@ struct BwdParams {
     const void* k;         // [B][T][Hkv][d]
     const void* v;
     float scale;
+    // Stored dS (DsBand): null, or the band the dK/dV kernel writes and the
+    // dQ kernel reads instead of recomputing S and dP
+    char* ds;
+    int32_t ds_nrb, ds_npre, ds_nwin, ds_nband;
 };
+
+// The band of stored dS tiles.  For every (sequence, query head, block rb of
+// 32 chunk positions) the blocks of 32 keys its rows can see are the prefix
+// blocks 0 .. npre-1 and the window blocks rb-nwin+1 .. rb; a key block kb
+// sits in slot kb when kb < npre, else in slot npre + kb - rb + nwin - 1.
+// Each slot holds a 32 x 32 tile of bf16 dS (query row x key) as the dK/dV
+// kernel holds it: two 1 KB halves of 16 rows, each 64 lanes x 16 bytes,
+// lane 32h + key holding rows 16 st + 4h + 0..3 and 16 st + 8 + 4h + 0..3
+// of half st.  P and W are in the chunk's frame (positions counted from the
+// chunk start, P <= T, W <= T).
+// The dK/dV kernel addresses one kv head's part (its `group` query heads)
+// with 32-bit offsets, so the band is used only while that part stays below
+// 2^31 bytes (bytes = 0 otherwise).
+struct DsBand {
+    int64_t nrb, npre, nwin, nband, bytes;
+};
+inline DsBand ds_band(int64_t batch, int64_t T, int64_t hq, int64_t group, int64_t P, int64_t W) {
+    DsBand d{};
+    d.nrb = (T + 31) / 32;
+    d.npre = (P + 31) / 32;
+    const int64_t nw0 = (W - 1 + 31) / 32;  // window blocks below the row block
+    d.nwin = nw0 + 1 < d.nrb ? nw0 + 1 : d.nrb;
+    d.nband = d.npre + d.nwin;
+    const bool fits = group * d.nrb * d.nband * 2048 < ((int64_t)1 << 31);
+    d.bytes = fits ? batch * hq * d.nrb * d.nband * 2048 : 0;
+    return d;
+}
 hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream);
 // The allocation-free backward's Delta rows: a device array of
 // PS_BWD_NOALLOC_MAX_ROWS floats the library owns (one copy per GPU, kept

@@ -716,7 +716,7 @@ inline int layout_group(int group) { return group <= 2 ? group : (group <= 4 ? 4
 // current device (a host call made once per kernel and device).
 constexpr int kMaxDevices = 64;
 inline bool* lds_flag(int slot) {
-    static bool flags[kMaxDevices][12] = {};
+    static bool flags[kMaxDevices][16] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
     return &flags[dev][slot];
@@ -1120,6 +1120,247 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dq_kernel(BwdParams bp) {
         }
 }
 
+// The lane index taken afresh (mbcnt in asm): the compiler cannot equate it
+// with an earlier one, so values derived from it are not kept live across
+// the caller's loop.
+__device__ inline int lane_now() {
+    int lane;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+    return lane;
+}
+
+// One 32 x 32 tile of bf16 dS from the key-on-the-lane layout the dK/dV
+// kernel stores (v[st]: rows 16 st + 4h + 0..3 in words 0-1 and
+// 16 st + 8 + 4h + 0..3 in words 2-3, the lane's key) to the query row on the
+// lane, through 2 KB of the wave's own LDS at tb: key rows of 32 query rows,
+// 8-byte units placed at u ^ ((key >> 2) & 7).  The transposing reads give
+// lane (row j, half h) keys 16 st + 4h + 0..3 and 16 st + 8 + 4h + 0..3, the
+// order of the K^T operands read_t_kswz gives.
+__device__ inline void ds_transpose(uint32_t tba, const Vec16 (&v)[2], Vec16 (&out)[2]) {
+    const int lane = lane_now();
+    const int h = lane >> 5, col = lane & 31, q = lane >> 4, gp = lane & 15;
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int part = 0; part < 2; ++part) {
+            const int u = 4 * st + 2 * part + h;
+            u32x2 w;
+            w.x = v[st].w[2 * part];
+            w.y = v[st].w[2 * part + 1];
+            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+                (uintptr_t)(tba + col * 64 + ((u ^ ((col >> 2) & 7)) << 3))) = w;
+        }
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            const int key = 16 * st + 8 * hf + 4 * h + (gp >> 2);
+            const int u = 4 * (q & 1) + (gp & 3);
+            const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4*)(uintptr_t)(tba + key * 64 + ((u ^ ((key >> 2) & 7)) << 3)));
+            __builtin_memcpy(&out[st].w[2 * hf], &r, 8);
+        }
+}
+constexpr int kDsXpose = 2048;  // LDS bytes of one tile transpose
+
+// Stage the cursor's K tile alone (b_chunk_swz, read transposed by the dQ
+// kernel that takes dS from the band).
+__device__ inline void load_tile_k(const Cursor& c, const LaneOffsets& lo, int wave, char* stage) {
+    const int row0 = c.t * kBNB;
+    const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
+    if (wave >= kLoadWaves) return;
+    const i32x4 kr = rsrc_words(c.k + (int64_t)row0 * c.rs, nrows * c.rs);
+    const uint32_t sb = lds_addr(stage);
+#pragma unroll
+    for (int i = 0; i < kLoadsPerWave; ++i)
+        dma16_asm(kr, lo.k[i], sb + ((kBNB / kLoadWaves) * wave + 4 * i) * kRowBytes);
+}
+
+// dQ from the stored dS band: dQ^T += K^T dS^T over the key tiles of the
+// walk, the forward's workgroup layout (8 waves, 256 stacked query rows;
+// wave w's 32 rows are one head's 32 positions, one row block of the band).
+// K tiles go through a 2-stage LDS ring (read transposed); each wave loads
+// its dS tiles from the band straight into registers, two tiles in flight,
+// and turns them to the query row on the lane through its own LDS
+// (ds_transpose, one 2 KB buffer per key block of the tile, after the K ring).  Blocks of 32 keys the wave's rows cannot see are skipped; on
+// blocks that straddle the rule the invisible pairs are zeroed (the band
+// holds only what the dK/dV kernel stored: its skipped halves are never
+// written).
+template <int G>
+__global__ void __launch_bounds__(kThreads, 1) bwd_dq_ds_kernel(BwdParams bp) {
+    constexpr int D = 128;
+    constexpr int QP = 32 * kWaves / G;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const PrefillParams& p = bp.f;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int h = lane >> 5, col = lane & 31;
+    const int n_qt = (p.seq_len + QP - 1) / QP;
+    const int work = xcd_remap((int)blockIdx.x, n_qt * p.hkv * p.batch);
+    const int qt = work % n_qt, g = (work / n_qt) % p.hkv, b = work / (n_qt * p.hkv);
+
+    const int S0 = (int)p.start_pos;
+    const int t0 = qt * QP;
+    const int t_last = (t0 + QP < p.seq_len ? t0 + QP : p.seq_len) - 1;
+    const int i0 = S0 + t0, i1 = S0 + t_last;
+    const int P32 = p.P > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.P;
+    const int w32 = p.W > 0x7FFFFFFF ? 0x7FFFFFFF : (int)p.W;
+
+    const int greal = p.hq / p.hkv;
+    const int hh = 32 * wave / QP;             // the wave's head of the group
+    const int tw = t0 + (32 * wave) % QP;      // its first position (chunk row)
+    const bool w_ok = hh < greal && tw < p.seq_len;
+    const int head = g * greal + (hh < greal ? hh : 0);
+    const int wi0 = S0 + tw, wi1 = wi0 + 31;   // its positions (rows past the chunk included)
+    const int rb = tw >> 5;
+    const int my_i = wi0 + col;
+    // the wave's row block of the band (waves without rows read slot 0 of the
+    // band's first block: every tile loads all its operands, so that no load
+    // is conditional and the compiler never waits for one before its use)
+    const char* dsb = bp.ds + (w_ok ? (((int64_t)b * p.hq + head) * bp.ds_nrb + rb) * bp.ds_nband * 2048 : 0) +
+                      lane * 16;
+
+    __shared__ TileWalk walk;
+    __shared__ RunView views[kMaxRuns];
+    if (tid == 0) {
+        plan_walk<kBNB>(p.runs, p.n_runs, p.P, p.W, (int64_t)i0, (int64_t)i1, walk);
+        for (int r = 0; r < p.n_runs; ++r) make_view(views[r], p.runs[r], b, g, p.hkv, 2);
+    }
+    __syncthreads();
+    int total = 0;
+    for (int r = 0; r < walk.n_ranges; ++r) total += walk.end[r] - walk.begin[r];
+
+    uint32_t kt_off[2][4];
+    kswz_tr_offsets(lane, kt_off);
+    f32x16 dq[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[m][r] = 0.f;
+
+    // class of the wave's rows against key block mb of the cursor's tile
+    auto block_class = [&](const Cursor& c, int mb, int& jb0, int& nb) __attribute__((always_inline)) {
+        const int row0 = c.t * kBNB;
+        const int nrows = c.n - row0 < kBNB ? c.n - row0 : kBNB;
+        jb0 = (int)c.pos0 + row0 + 32 * mb;
+        nb = nrows - 32 * mb < 32 ? nrows - 32 * mb : 32;
+        if (!w_ok || nb <= 0) return (int)kSkip;
+        return tile_class32(wi0, wi1, jb0, jb0 + nb - 1, P32, w32);
+    };
+    auto load_ds = [&](const Cursor& c, Vec16 (&buf)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            int jb0, nb;
+            const bool skip = block_class(c, mb, jb0, nb) == kSkip;  // then slot 0, never used
+            const int kb = (jb0 - S0) >> 5;
+            const int slot = skip ? 0 : kb < bp.ds_npre ? kb : bp.ds_npre + kb - rb + bp.ds_nwin - 1;
+            const char* src = dsb + (int64_t)slot * 2048;
+            buf[mb][0] = *reinterpret_cast<const Vec16*>(src);
+            buf[mb][1] = *reinterpret_cast<const Vec16*>(src + 1024);
+        }
+    };
+    const uint32_t xpose = lds_addr(smem + kStages * kTileBytes) + wave * 4 * kDsXpose;
+    auto compute = [&](const Cursor& c, const char* kstage, Vec16 (&raw)[4][2]) __attribute__((always_inline)) {
+        const uint32_t kb_lds = lds_addr(kstage);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+            int jb0, nb;
+            const int cls = block_class(c, mb, jb0, nb);
+            if (cls == kSkip) continue;
+            Vec16 ds[2];  // the block's dS, query row on the lane
+            ds_transpose(xpose + mb * kDsXpose, raw[mb], ds);
+            if (cls == kMasked) {
+                // visible keys of the lane's row among the block's nb keys
+                const int rel = my_i - jb0;
+                const int hic = rel < nb - 1 ? rel : nb - 1;
+                const int a_hi = P32 - jb0 < hic + 1 ? P32 - jb0 : hic + 1;
+                const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
+                const uint32_t bits = range_bits(0, a_hi) | range_bits(b_lo, hic + 1);
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int wd = 0; wd < 4; ++wd) {
+                        const int k0 = 16 * st + 8 * (wd >> 1) + 4 * h + 2 * (wd & 1);
+                        const uint32_t m2 = bits >> k0;
+                        const uint32_t keep = ((m2 & 1u) ? 0x0000FFFFu : 0u) | ((m2 & 2u) ? 0xFFFF0000u : 0u);
+                        ds[st].w[wd] &= keep;
+                    }
+            }
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                Vec16 ka[4];
+                read_t_kswz(2 * mb + st, kb_lds, kt_off, ka);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    dq[m] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[m]), as_bf16x8(ds[st]), dq[m], 0, 0, 0);
+            }
+        }
+    };
+    // the compiler cannot see the asm tile loads: after the explicit wait,
+    // a use of the next tile's dS registers settles its own wait for them
+    // there, not at their first use in the next tile
+    auto settle = [&](Vec16 (&buf)[4][2]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) asm volatile("" ::"v"(buf[mb][0].w[0]), "v"(buf[mb][1].w[0]));
+    };
+
+    Cursor cc, pc;
+    LaneOffsets lo;
+    if (total > 0) {
+        cursor_enter(cc, 0, walk, views);
+        cursor_enter(pc, 0, walk, views);
+        lane_offsets_bwd(lo, pc.rs, lane, wave);
+    }
+    Vec16 bufa[4][2], bufb[4][2];
+    auto stage_next = [&](char* stage, Vec16 (&buf)[4][2]) __attribute__((always_inline)) {
+        load_tile_k(pc, lo, wave, stage);
+        load_ds(pc, buf);
+        if (cursor_next(pc, walk.n_ranges, walk, views)) lane_offsets_bwd(lo, pc.rs, lane, wave);
+    };
+    if (total > 0) stage_next(smem, bufa);
+    if (total > 1) stage_next(smem + kTileBytes, bufb);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    settle(bufa);
+    settle(bufb);
+    tile_barrier();
+
+    // tile f: compute from stage f & 1, wait for tile f + 1, then stage tile
+    // f + 2 into the freed stage and registers
+    auto step = [&](int f, Vec16 (&cur)[4][2], Vec16 (&nxt)[4][2]) __attribute__((always_inline)) {
+        compute(cc, smem + (f & 1) * kTileBytes, cur);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        settle(nxt);
+        tile_barrier();
+        if (f + kStages < total) stage_next(smem + (f & 1) * kTileBytes, cur);
+        cursor_next(cc, walk.n_ranges, walk, views);
+    };
+    // (both steps unconditional inside the loop: on every path into an
+    // iteration the registers it computes from are settled)
+    int f = 0;
+    for (; f + 1 < total; f += 2) {
+        step(f, bufa, bufb);
+        step(f + 1, bufb, bufa);
+    }
+    if (f < total) step(f, bufa, bufb);
+
+    const int my_t = tw + col;
+    if (!w_ok || my_t >= p.seq_len) return;
+    const int64_t row_el = ((int64_t)b * p.seq_len + my_t) * p.hq + head;
+    uint16_t* op = reinterpret_cast<uint16_t*>(bp.dq) + row_el * D;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int cc4 = 0; cc4 < 4; ++cc4) {
+            Vec8 w;
+            w.w[0] = pack_bf16x2(dq[m][4 * cc4] * bp.scale, dq[m][4 * cc4 + 1] * bp.scale);
+            w.w[1] = pack_bf16x2(dq[m][4 * cc4 + 2] * bp.scale, dq[m][4 * cc4 + 3] * bp.scale);
+            *reinterpret_cast<Vec8*>(op + 32 * m + 8 * cc4 + 4 * h) = w;
+        }
+}
+
 // dK / dV: one workgroup of 8 waves per (sequence, kv head, block of 256
 // keys).  Wave w owns keys 32w .. 32w + 31 of the block: their K rows stay in
 // registers (B operand of S = Q K^T), their dK^T and dV^T accumulate in
@@ -1137,7 +1378,58 @@ constexpr int kSubStage = 2 * kSubRowBytes + 2 * kSubRows * 4;  // Q, dO, lse, D
 constexpr int kVBlock = kKB * kRowBytes;                  // 64 KB
 constexpr size_t kDkdvLds = (size_t)kVBlock + 2 * kSubStage;
 
+// dS of one 32-row half of a dK/dV sub-tile into the dS band (DsBand), as the
+// dK/dV kernel holds it: key on the lane, sb[st] = rows 16 st + 4h + 0..3
+// (words 0-1) and 16 st + 8 + 4h + 0..3 (words 2-3) of the half's stacked
+// rows.  Each 4-row piece goes to its head's tile of its 32-position block,
+// into the lane's own 16-byte slot of the 1 KB half that holds its 16
+// positions: up to four heads share a half, but a piece never straddles two
+// (G <= 4: one 16-byte store per st; G = 8: the two pieces of a slot belong
+// to different heads, one 8-byte store each).  Pieces of rows past the chunk
+// or of missing heads get an offset past the resource (dsr: this sequence
+// and kv head's part of the band), which the hardware drops, so every call
+// issues exactly kDsStoresPerHalf stores -- the caller's vmcnt accounting
+// relies on that.  Non-temporal: the band is read once, by the dQ kernel,
+// after this kernel has ended (measured 1.5% faster than plain stores).
 template <int G>
+constexpr int kDsStoresPerHalf = G == 8 ? 4 : 2;
+template <int G>
+__device__ inline void store_ds_native(const BwdParams& bp, const Vec16 (&sb)[2], i32x4 dsr, int greal, int ts,
+                                       int half, int kb) {
+    constexpr int QS = kSubRows / G;
+    const int lane = lane_now(), h = lane >> 5;
+    const int rb = uniform_int((ts + (G == 1 ? 32 * half : 0)) >> 5);
+    const int slot = kb < bp.ds_npre ? kb : bp.ds_npre + kb - rb + bp.ds_nwin - 1;
+    const int tile0 = rb * bp.ds_nband + slot;  // tile index within one head's band
+    // A piece starts at stacked row r = 32 half + 16 st + 8 part + 4h: its head
+    // r / QS does not depend on h (QS is a multiple of 8), its position is
+    // ts + (r - 4h) % QS + 4h.
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int part = 0; part < (G <= 4 ? 1 : 2); ++part) {
+            const int rr = 32 * half + 16 * st + 8 * part;  // the piece's row without the 4h
+            const int hh = rr / QS;
+            const int tu = uniform_int(ts + rr % QS);      // its position without the 4h
+            const int base = uniform_int((hh * bp.ds_nrb * bp.ds_nband + tile0) * 2048 + ((tu & 31) >> 4) * 1024 +
+                                         (G <= 4 ? 0 : ((tu >> 3) & 1) * 8));
+            const int voff = tu + 4 * h < bp.f.seq_len && hh < greal ? base + lane * 16 : (int)0x80000000u;
+            if constexpr (G <= 4) {
+                i32x4 d;
+                __builtin_memcpy(&d, &sb[st], 16);
+                asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt" ::"v"(d), "v"(voff), "s"(dsr) : "memory");
+            } else {
+                typedef int i32x2 __attribute__((ext_vector_type(2)));
+                i32x2 d;
+                d.x = (int)sb[st].w[2 * part];
+                d.y = (int)sb[st].w[2 * part + 1];
+                asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen nt" ::"v"(d), "v"(voff), "s"(dsr) : "memory");
+            }
+        }
+}
+
+// DS: also store each half's dS into the band the dQ kernel reads.
+template <int G, bool DS = false>
 __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
     constexpr int D = 128;
     constexpr int QS = kSubRows / G;  // positions per sub-tile
@@ -1265,7 +1557,14 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dkacc[m][r] = dvacc[m][r] = 0.f;
 
+    // DS: this (sequence, kv head)'s part of the dS band as a buffer resource
+    // (its size is below 2^31: the host uses the band only then)
+    i32x4 dsr = {0, 0, 0, 0};
+    if constexpr (DS)
+        dsr = rsrc_words(bp.ds + ((int64_t)b * hq + g * greal) * bp.ds_nrb * bp.ds_nband * 2048,
+                         greal * bp.ds_nrb * bp.ds_nband * 2048);
     for (int n = 0; n < n_sub; ++n) {
+        int stored = 0;  // DS: halves whose dS was stored in this sub-tile (uniform)
         const char* st = stage0 + (n & 1) * kSubStage;
         const char* qs = st;
         const char* ds_ = st + kSubRowBytes;
@@ -1342,6 +1641,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                         }
                         sb[st2].w[w] = pack_bf16x2(dv2[0], dv2[1]);
                     }
+                if constexpr (DS) {
+                    store_ds_native<G>(bp, sb, dsr, greal, ts, half, kt0 / 32 + wave);
+                    ++stored;
+                }
                 const uint32_t qb_ = lds_addr(qs) + 32 * half * kRowBytes;
                 const uint32_t db_ = lds_addr(ds_) + 32 * half * kRowBytes;
 #pragma unroll
@@ -1359,7 +1662,17 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // wait for the next sub-tile's staging; the dS stores of the last half
+        // (issued after it, completing in order with it) stay in flight into
+        // the next sub-tile
+        if (DS && stored) {
+            if constexpr (kDsStoresPerHalf<G> == 4)
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            else
+                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         tile_barrier();
         if (n + 2 < n_sub) stage_sub(n + 2, stage0 + (n & 1) * kSubStage);
     }
@@ -1479,6 +1792,38 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
     const dim3 grid_k((unsigned)(n_pre_pad + (n_kb - kb_pre) * n_bg));
     const size_t lds_q = (size_t)kStages * kStageBytes;
     const int gi = group == 1 ? 0 : group == 2 ? 1 : group == 4 ? 2 : 3;
+    if (p.ds) {
+        // dS stored by the dK/dV kernel, dQ from it (no second S and dP)
+        const size_t lds_qd = (size_t)kStages * kTileBytes + (size_t)kWaves * 4 * kDsXpose;
+        const void* fqd = nullptr;
+        const void* fkd = nullptr;
+        switch (group) {
+            case 1: fqd = (const void*)bwd_dq_ds_kernel<1>; fkd = (const void*)bwd_dkdv_kernel<1, true>; break;
+            case 2: fqd = (const void*)bwd_dq_ds_kernel<2>; fkd = (const void*)bwd_dkdv_kernel<2, true>; break;
+            case 4: fqd = (const void*)bwd_dq_ds_kernel<4>; fkd = (const void*)bwd_dkdv_kernel<4, true>; break;
+            case 8: fqd = (const void*)bwd_dq_ds_kernel<8>; fkd = (const void*)bwd_dkdv_kernel<8, true>; break;
+            default: return hipErrorInvalidValue;
+        }
+        bool* set_d = lds_flag(12 + gi);
+        if (!set_d || !*set_d) {
+            hipError_t e = hipFuncSetAttribute(fqd, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_qd);
+            if (e != hipSuccess) return e;
+            e = hipFuncSetAttribute(fkd, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kDkdvLds);
+            if (e != hipSuccess) return e;
+            if (set_d) *set_d = true;
+        }
+        switch (group) {
+            case 1: hipLaunchKernelGGL((bwd_dkdv_kernel<1, true>), grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                    hipLaunchKernelGGL(bwd_dq_ds_kernel<1>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
+            case 2: hipLaunchKernelGGL((bwd_dkdv_kernel<2, true>), grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                    hipLaunchKernelGGL(bwd_dq_ds_kernel<2>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
+            case 4: hipLaunchKernelGGL((bwd_dkdv_kernel<4, true>), grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                    hipLaunchKernelGGL(bwd_dq_ds_kernel<4>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
+            case 8: hipLaunchKernelGGL((bwd_dkdv_kernel<8, true>), grid_k, dim3(kThreads), kDkdvLds, stream, p);
+                    hipLaunchKernelGGL(bwd_dq_ds_kernel<8>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
+        }
+        return hipGetLastError();
+    }
     const void* fq = nullptr;
     const void* fk = nullptr;
     switch (group) {

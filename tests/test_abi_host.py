@@ -7,6 +7,7 @@ import os
 import random
 import re
 
+import numpy as np
 import pytest
 
 import oracle
@@ -166,6 +167,54 @@ def test_prefill_bwd_rejects_bad_arguments_before_any_launch():
     assert call(delta=0) == ps.PS_ERR_INVALID
     # nothing to do: no pointer is touched
     assert call(seq_len=0, q=0, k=0, v=0, out=0, lse=0, dout=0, dq=0, dk=0, dv=0, delta=0) == ps.PS_OK
+
+
+def test_prefill_bwd_ds_workspace_size_and_capacity():
+    """The stored-dS workspace of the backward: per (sequence, query head,
+    block of 32 chunk positions) one 2 KB tile per slot of the band -- the
+    prefix key blocks, then the window blocks that end at the row block.
+    Checked against a brute force over the visibility rule: every key block
+    some row of a row block sees is a prefix block or lies in the window
+    slots, so the band the size provides for holds all of dS."""
+    def size(**kw):
+        out = ctypes.c_int64(-1)
+        st = ps.lib.ps_prefill_bwd_ds_bytes(ctypes.byref(_bwd_args(**kw)), ctypes.byref(out))
+        return st, out.value
+
+    for B, T, hq, start, P, W in [(1, 16, 4, 0, 4, 8), (2, 300, 4, 0, 20, 70), (1, 333, 2, 1000, 1100, 100),
+                                  (1, 190, 2, 0, 3, 1), (1, 300, 2, 0, 400, 8), (3, 97, 8, 50, 0, 500),
+                                  (1, 1, 2, 0, 0, 5), (1, 64, 2, 2**33, 2**33 + 40, 33)]:
+        st, nbytes = size(batch=B, seq_len=T, n_q_heads=hq, start_pos=start, prefix_len=P, window=W)
+        assert st == ps.PS_OK
+        # the chunk's frame: positions counted from the chunk start
+        Pc, Wc = min(max(P - start, 0), T), min(W, T)
+        nrb = (T + 31) // 32
+        t = np.arange(T)
+        npre = (Pc + 31) // 32
+        lowest = 0  # most window blocks below a row block that hold a visible non-prefix key
+        for rb in range(nrb):
+            rows = t[32 * rb: 32 * rb + 32]
+            vis = (t[None, :] <= rows[:, None]) & ((t[None, :] < Pc) | (t[None, :] > rows[:, None] - Wc))
+            for kb in sorted(set(np.nonzero(vis.any(axis=0))[0] // 32)):
+                if kb >= npre:
+                    lowest = max(lowest, rb - kb)
+        nwin = min((Wc - 1 + 31) // 32 + 1, nrb)
+        assert lowest < nwin
+        assert nbytes == B * hq * nrb * (npre + nwin) * 2048, (T, P, W, nbytes)
+    assert size(seq_len=0) == (ps.PS_OK, 0)
+    assert size(batch=0)[0] == ps.PS_ERR_INVALID
+    assert size(window=0)[0] == ps.PS_ERR_INVALID
+    assert size(start_pos=(1 << 62) - 8)[0] == ps.PS_ERR_UNSUPPORTED
+    assert ps.lib.ps_prefill_bwd_ds_bytes(None, None) == ps.PS_ERR_INVALID
+    _, need = size()
+    call = lambda **kw: ps.lib.ps_prefill_attn_bwd(ctypes.byref(_bwd_args(**kw)), None)
+    assert call(ds_work=1, ds_work_bytes=need - 1) == ps.PS_ERR_CAPACITY   # before any launch
+    assert ps.ps_prefill_bwd_ds_bytes(2, 300, 4, 2, start_pos=0, prefix_len=20, window=70) == \
+        2 * 4 * 10 * (1 + 4) * 2048
+    # one kv head's share past 2^31 bytes: no stored dS (long rows, wide window)
+    assert size(batch=1, seq_len=300000, n_q_heads=2, n_kv_heads=1, window=300000) == (ps.PS_OK, 0)
+    assert size(batch=1, seq_len=300000, n_q_heads=2, n_kv_heads=2, window=2000)[1] > 0
+    assert size(n_kv_heads=3)[0] == ps.PS_ERR_INVALID
 
 
 def test_rerotate_rejects_null_cache_before_any_launch():

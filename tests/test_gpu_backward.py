@@ -47,7 +47,12 @@ def bwd_inputs(seed, B, start, T, hq, hkv, d, scale):
     return pos, q, k, v, do
 
 
-def run_bwd(q, k, v, do, P, W, start):
+def run_bwd(q, k, v, do, P, W, start, stored_ds=False):
+    """Forward, then the backward; with stored_ds also the backward that keeps
+    dS in a workspace (filled with NaN bytes first, so that any read of a
+    tile the dK/dV pass did not write shows) -- its dq is returned as a
+    second array, and its dk and dv must equal the first path's bit for bit
+    (the same dK/dV arithmetic, plus the stores)."""
     B, T, hq, d = q.shape
     hkv = k.shape[2]
     sc = 1.0 / math.sqrt(d)
@@ -60,7 +65,18 @@ def run_bwd(q, k, v, do, P, W, start):
     ps.ps_prefill_attn_bwd(qd, kd, vd, out, lse, dod, dq, dk, dv, delta, start_pos=start, prefix_len=P,
                            window=W, scale=sc)
     torch.cuda.synchronize()
-    return dev_to_f32(dq), dev_to_f32(dk), dev_to_f32(dv), dev_to_f32(delta), dev_to_f32(out)
+    res = [dev_to_f32(dq), dev_to_f32(dk), dev_to_f32(dv), dev_to_f32(delta), dev_to_f32(out)]
+    if stored_ds:
+        nbytes = ps.ps_prefill_bwd_ds_bytes(B, T, hq, hkv, start_pos=start, prefix_len=P, window=W)
+        ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+        dq2, dk2, dv2 = torch.full_like(qd, float("nan")), torch.empty_like(kd), torch.empty_like(vd)
+        delta2 = torch.empty(B, T, hq, device="cuda")
+        ps.ps_prefill_attn_bwd(qd, kd, vd, out, lse, dod, dq2, dk2, dv2, delta2, start_pos=start, prefix_len=P,
+                               window=W, scale=sc, ds_work=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(dk2, dk) and torch.equal(dv2, dv) and torch.equal(delta2, delta)
+        res.append(dev_to_f32(dq2))
+    return tuple(res)
 
 
 def check(name, got, ref):
@@ -100,18 +116,21 @@ def test_trainer_backward_small(hq, hkv, B, T, P, W, start, scale):
     note(f"backward hq={hq} hkv={hkv} B={B} T={T} P={P} W={W} start={start} s={scale}")
     d = 128
     pos, q, k, v, do = bwd_inputs(21, B, start, T, hq, hkv, d, scale)
-    dq, dk, dv, delta, out = run_bwd(q, k, v, do, P, W, start)
+    dq, dk, dv, delta, out, dq_s = run_bwd(q, k, v, do, P, W, start, stored_ds=True)
     for b in range(B):
         rq, rk, rv = oracle.attention_bwd(as_f32(q[b]), pos, as_f32(k[b]), as_f32(v[b]), pos, as_f32(do[b]),
                                           P, W, 1.0 / math.sqrt(d), threads=16)
         check("dq", dq[b], rq)
+        check("dq stored dS", dq_s[b], rq)
         check("dk", dk[b], rk)
         check("dv", dv[b], rv)
         check_kernel_part(q[b], k[b], v[b], do[b], delta[b], pos, P, W, (dq[b], dk[b], dv[b]))
+        check_kernel_part(q[b], k[b], v[b], do[b], delta[b], pos, P, W, (dq_s[b], dk[b], dv[b]))
         if scale == 1.0:
             # non-peaky rows: no cancellation in dP - Delta, so the total
             # error stays near the kernel's own (measured <= 2.9e-3)
-            for name, g_, r_ in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
+            for name, g_, r_ in (("dq", dq[b], rq), ("dq stored dS", dq_s[b], rq), ("dk", dk[b], rk),
+                                 ("dv", dv[b], rv)):
                 fro = float(np.linalg.norm(g_ - r_) / max(np.linalg.norm(r_), 1.0))
                 assert fro <= 1e-2, ("non-peaky total", name, fro)
         # Delta is rowsum(dout * out) of the bf16 forward output
@@ -139,14 +158,16 @@ def test_trainer_backward_random(case):
     note(f"backward random {case}: hq={hq} hkv={hkv} B={B} T={T} P={P} W={W} start={start} s={scale}")
     d = 128
     pos, q, k, v, do = bwd_inputs(300 + case, B, start, T, hq, hkv, d, scale)
-    dq, dk, dv, delta, out = run_bwd(q, k, v, do, P, W, start)
+    dq, dk, dv, delta, out, dq_s = run_bwd(q, k, v, do, P, W, start, stored_ds=True)
     for b in range(B):
         rq, rk, rv = oracle.attention_bwd(as_f32(q[b]), pos, as_f32(k[b]), as_f32(v[b]), pos, as_f32(do[b]),
                                           P, W, 1.0 / math.sqrt(d), threads=16)
         check("dq", dq[b], rq)
+        check("dq stored dS", dq_s[b], rq)
         check("dk", dk[b], rk)
         check("dv", dv[b], rv)
         check_kernel_part(q[b], k[b], v[b], do[b], delta[b], pos, P, W, (dq[b], dk[b], dv[b]))
+        check_kernel_part(q[b], k[b], v[b], do[b], delta[b], pos, P, W, (dq_s[b], dk[b], dv[b]))
         np.testing.assert_allclose(delta[b], np.sum(as_f32(do[b]) * out[b], axis=-1), rtol=0, atol=1e-3)
 
 
@@ -161,8 +182,12 @@ def test_trainer_backward_qwen_config():
     B, T, hq, hkv, d, P, W = 8, 8192, 16, 8, 128, 256, 2048
     note("backward qwen config")
     pos, q, k, v, do = bwd_inputs(0, B, 0, T, hq, hkv, d, 1.0)
-    dq, dk, dv, delta, _ = run_bwd(q, k, v, do, P, W, 0)
+    dq_r, dk, dv, delta, _, dq = run_bwd(q, k, v, do, P, W, 0, stored_ds=True)
     assert np.all(np.isfinite(dq)) and np.all(np.isfinite(dk)) and np.all(np.isfinite(dv))
+    # dq from the stored dS (the path the benchmark times) against dq with S
+    # and dP rebuilt: the same bf16 dS, summed in another order
+    fro = float(np.linalg.norm(dq - dq_r) / max(np.linalg.norm(dq_r), 1.0))
+    assert fro <= 2e-3, ("stored dS against rebuilt", fro)
     sc = 1.0 / math.sqrt(d)
     rng = np.random.default_rng(2)
     for b in range(B):
