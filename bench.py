@@ -698,7 +698,8 @@ def r1_distill_bench(torch, ps, np):
         e1.record(stream)
         torch.cuda.synchronize()
         t = e0.elapsed_time(e1) / 5
-        res[name] = {"config": "B=8, T=8192, P=256, W=2048" + (", stored dS" if name == "trainer_backward" else ""),
+        res[name] = {"config": "B=8, T=8192, P=256, W=2048" +
+                               (", stored dS" if name == "trainer_backward" and ds_work.numel() else ""),
                      "ms": round(t, 3),
                      "tflops_exact": round(flops / t / 1e9, 1),
                      "frac_mfma_exact": round(flops / t / 1e9 / MFMA_BF16_PEAK_TFLOPS, 4)}

@@ -408,9 +408,10 @@ int ps_prefill_attn(const ps_prefill_args* args, void* stream);
  * batch * n_q_heads * seq_len * (min(window, seq_len) + min(P', seq_len) + 64) * 2
  * bytes with P' the prefix keys inside the chunk.  Its contents on return are
  * unspecified; nothing needs clearing before a call.  With ds_work NULL
- * (ds_work_bytes ignored), or when ps_prefill_bwd_ds_bytes gives 0 (one kv
- * head's share of the workspace would reach 2^31 bytes), S and dP are
- * rebuilt and ds_work is not touched.
+ * (ds_work_bytes ignored), or when ps_prefill_bwd_ds_bytes gives 0 (GQA
+ * groups of more than 4 query heads, where storing costs more than it saves,
+ * or one kv head's share of the workspace would reach 2^31 bytes), S and dP
+ * are rebuilt and ds_work is not touched.
  *
  * Errors: PS_ERR_INVALID (NULL pointer, batch < 1, seq_len < 0, start_pos < 0,
  * prefix_len < 0, window < 1, n_q_heads not a multiple of n_kv_heads, scale

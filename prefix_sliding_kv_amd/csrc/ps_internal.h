@@ -425,7 +425,9 @@ struct BwdParams {
 // chunk start, P <= T, W <= T).
 // The dK/dV kernel addresses one kv head's part (its `group` query heads)
 // with 32-bit offsets, so the band is used only while that part stays below
-// 2^31 bytes (bytes = 0 otherwise).
+// 2^31 bytes, and only for groups of up to 4 query heads: on the 8-head
+// layout a 16-byte piece of dS spans two heads and takes two stores, which
+// cost the dK/dV kernel more than the dQ kernel saves (bytes = 0 otherwise).
 struct DsBand {
     int64_t nrb, npre, nwin, nband, bytes;
 };
@@ -436,7 +438,7 @@ inline DsBand ds_band(int64_t batch, int64_t T, int64_t hq, int64_t group, int64
     const int64_t nw0 = (W - 1 + 31) / 32;  // window blocks below the row block
     d.nwin = nw0 + 1 < d.nrb ? nw0 + 1 : d.nrb;
     d.nband = d.npre + d.nwin;
-    const bool fits = group * d.nrb * d.nband * 2048 < ((int64_t)1 << 31);
+    const bool fits = group <= 4 && group * d.nrb * d.nband * 2048 < ((int64_t)1 << 31);
     d.bytes = fits ? batch * hq * d.nrb * d.nband * 2048 : 0;
     return d;
 }

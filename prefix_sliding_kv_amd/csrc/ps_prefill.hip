@@ -1381,51 +1381,37 @@ constexpr size_t kDkdvLds = (size_t)kVBlock + 2 * kSubStage;
 // dS of one 32-row half of a dK/dV sub-tile into the dS band (DsBand), as the
 // dK/dV kernel holds it: key on the lane, sb[st] = rows 16 st + 4h + 0..3
 // (words 0-1) and 16 st + 8 + 4h + 0..3 (words 2-3) of the half's stacked
-// rows.  Each 4-row piece goes to its head's tile of its 32-position block,
-// into the lane's own 16-byte slot of the 1 KB half that holds its 16
-// positions: up to four heads share a half, but a piece never straddles two
-// (G <= 4: one 16-byte store per st; G = 8: the two pieces of a slot belong
-// to different heads, one 8-byte store each).  Pieces of rows past the chunk
-// or of missing heads get an offset past the resource (dsr: this sequence
-// and kv head's part of the band), which the hardware drops, so every call
-// issues exactly kDsStoresPerHalf stores -- the caller's vmcnt accounting
+// rows.  Those 16 rows are one head's (G <= 4: 16 or more positions per
+// head in a sub-tile), so each st is one 16-byte store into the lane's own
+// slot of the 1 KB half-tile that holds their positions.  Rows of a piece
+// past the chunk or of missing heads get an offset past the resource (dsr:
+// this sequence and kv head's part of the band), which the hardware drops,
+// so every call issues exactly two stores -- the caller's vmcnt accounting
 // relies on that.  Non-temporal: the band is read once, by the dQ kernel,
 // after this kernel has ended (measured 1.5% faster than plain stores).
 template <int G>
-constexpr int kDsStoresPerHalf = G == 8 ? 4 : 2;
-template <int G>
 __device__ inline void store_ds_native(const BwdParams& bp, const Vec16 (&sb)[2], i32x4 dsr, int greal, int ts,
                                        int half, int kb) {
+    static_assert(G <= 4, "stored dS covers groups of up to 4 heads");
     constexpr int QS = kSubRows / G;
     const int lane = lane_now(), h = lane >> 5;
     const int rb = uniform_int((ts + (G == 1 ? 32 * half : 0)) >> 5);
     const int slot = kb < bp.ds_npre ? kb : bp.ds_npre + kb - rb + bp.ds_nwin - 1;
     const int tile0 = rb * bp.ds_nband + slot;  // tile index within one head's band
-    // A piece starts at stacked row r = 32 half + 16 st + 8 part + 4h: its head
-    // r / QS does not depend on h (QS is a multiple of 8), its position is
+    // The piece starts at stacked row r = 32 half + 16 st + 4h: its head
+    // r / QS does not depend on h (QS is a multiple of 16), its position is
     // ts + (r - 4h) % QS + 4h.
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int part = 0; part < (G <= 4 ? 1 : 2); ++part) {
-            const int rr = 32 * half + 16 * st + 8 * part;  // the piece's row without the 4h
-            const int hh = rr / QS;
-            const int tu = uniform_int(ts + rr % QS);      // its position without the 4h
-            const int base = uniform_int((hh * bp.ds_nrb * bp.ds_nband + tile0) * 2048 + ((tu & 31) >> 4) * 1024 +
-                                         (G <= 4 ? 0 : ((tu >> 3) & 1) * 8));
-            const int voff = tu + 4 * h < bp.f.seq_len && hh < greal ? base + lane * 16 : (int)0x80000000u;
-            if constexpr (G <= 4) {
-                i32x4 d;
-                __builtin_memcpy(&d, &sb[st], 16);
-                asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt" ::"v"(d), "v"(voff), "s"(dsr) : "memory");
-            } else {
-                typedef int i32x2 __attribute__((ext_vector_type(2)));
-                i32x2 d;
-                d.x = (int)sb[st].w[2 * part];
-                d.y = (int)sb[st].w[2 * part + 1];
-                asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen nt" ::"v"(d), "v"(voff), "s"(dsr) : "memory");
-            }
-        }
+    for (int st = 0; st < 2; ++st) {
+        const int rr = 32 * half + 16 * st;  // the piece's row without the 4h
+        const int hh = rr / QS;
+        const int tu = uniform_int(ts + rr % QS);  // its position without the 4h
+        const int base = uniform_int((hh * bp.ds_nrb * bp.ds_nband + tile0) * 2048 + ((tu & 31) >> 4) * 1024);
+        const int voff = tu + 4 * h < bp.f.seq_len && hh < greal ? base + lane * 16 : (int)0x80000000u;
+        i32x4 d;
+        __builtin_memcpy(&d, &sb[st], 16);
+        asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen nt" ::"v"(d), "v"(voff), "s"(dsr) : "memory");
+    }
 }
 
 // DS: also store each half's dS into the band the dQ kernel reads.
@@ -1665,14 +1651,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
         // wait for the next sub-tile's staging; the dS stores of the last half
         // (issued after it, completing in order with it) stay in flight into
         // the next sub-tile
-        if (DS && stored) {
-            if constexpr (kDsStoresPerHalf<G> == 4)
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            else
-                asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-        } else {
+        if (DS && stored)
+            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
         tile_barrier();
         if (n + 2 < n_sub) stage_sub(n + 2, stage0 + (n & 1) * kSubStage);
     }
@@ -1801,8 +1783,7 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
             case 1: fqd = (const void*)bwd_dq_ds_kernel<1>; fkd = (const void*)bwd_dkdv_kernel<1, true>; break;
             case 2: fqd = (const void*)bwd_dq_ds_kernel<2>; fkd = (const void*)bwd_dkdv_kernel<2, true>; break;
             case 4: fqd = (const void*)bwd_dq_ds_kernel<4>; fkd = (const void*)bwd_dkdv_kernel<4, true>; break;
-            case 8: fqd = (const void*)bwd_dq_ds_kernel<8>; fkd = (const void*)bwd_dkdv_kernel<8, true>; break;
-            default: return hipErrorInvalidValue;
+            default: return hipErrorInvalidValue;  // (the host uses the band for groups up to 4 only)
         }
         bool* set_d = lds_flag(12 + gi);
         if (!set_d || !*set_d) {
@@ -1819,8 +1800,6 @@ hipError_t launch_prefill_bwd(int group, const BwdParams& p, hipStream_t stream)
                     hipLaunchKernelGGL(bwd_dq_ds_kernel<2>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
             case 4: hipLaunchKernelGGL((bwd_dkdv_kernel<4, true>), grid_k, dim3(kThreads), kDkdvLds, stream, p);
                     hipLaunchKernelGGL(bwd_dq_ds_kernel<4>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
-            case 8: hipLaunchKernelGGL((bwd_dkdv_kernel<8, true>), grid_k, dim3(kThreads), kDkdvLds, stream, p);
-                    hipLaunchKernelGGL(bwd_dq_ds_kernel<8>, grid_q, dim3(kThreads), lds_qd, stream, p); break;
         }
         return hipGetLastError();
     }

@@ -215,6 +215,10 @@ def test_prefill_bwd_ds_workspace_size_and_capacity():
     assert size(batch=1, seq_len=300000, n_q_heads=2, n_kv_heads=1, window=300000) == (ps.PS_OK, 0)
     assert size(batch=1, seq_len=300000, n_q_heads=2, n_kv_heads=2, window=2000)[1] > 0
     assert size(n_kv_heads=3)[0] == ps.PS_ERR_INVALID
+    # groups of more than 4 query heads (the 8-head layout) rebuild dS: no workspace
+    assert size(n_q_heads=16, n_kv_heads=2) == (ps.PS_OK, 0)
+    assert size(n_q_heads=28, n_kv_heads=4) == (ps.PS_OK, 0)
+    assert size(n_q_heads=8, n_kv_heads=2)[1] > 0
 
 
 def test_rerotate_rejects_null_cache_before_any_launch():
