@@ -1183,7 +1183,8 @@ __device__ inline void load_tile_k(const Cursor& c, const LaneOffsets& lo, int w
 // K tiles go through a 2-stage LDS ring (read transposed); each wave loads
 // its dS tiles from the band straight into registers, two tiles in flight,
 // and turns them to the query row on the lane through its own LDS
-// (ds_transpose, one 2 KB buffer per key block of the tile, after the K ring).  Blocks of 32 keys the wave's rows cannot see are skipped; on
+// (ds_transpose, one 2 KB buffer per key block of the tile, after the K
+// ring).  Blocks of 32 keys the wave's rows cannot see are skipped; on
 // blocks that straddle the rule the invisible pairs are zeroed (the band
 // holds only what the dK/dV kernel stored: its skipped halves are never
 // written).
