@@ -1387,9 +1387,9 @@ constexpr size_t kDkdvLds = (size_t)kVBlock + 2 * kSubStage;
 // slot of the 1 KB half-tile that holds their positions.  Rows of a piece
 // past the chunk or of missing heads get an offset past the resource (dsr:
 // this sequence and kv head's part of the band), which the hardware drops,
-// so every call issues exactly two stores -- the caller's vmcnt accounting
-// relies on that.  Non-temporal: the band is read once, by the dQ kernel,
-// after this kernel has ended (measured 1.5% faster than plain stores).
+// so the stores need no branch.  Non-temporal: the band is read once, by
+// the dQ kernel, after this kernel has ended (measured 1.5% faster than
+// plain stores).
 template <int G>
 __device__ inline void store_ds_native(const BwdParams& bp, const Vec16 (&sb)[2], i32x4 dsr, int greal, int ts,
                                        int half, int kb) {
@@ -1551,7 +1551,6 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
         dsr = rsrc_words(bp.ds + ((int64_t)b * hq + g * greal) * bp.ds_nrb * bp.ds_nband * 2048,
                          greal * bp.ds_nrb * bp.ds_nband * 2048);
     for (int n = 0; n < n_sub; ++n) {
-        int stored = 0;  // DS: halves whose dS was stored in this sub-tile (uniform)
         const char* st = stage0 + (n & 1) * kSubStage;
         const char* qs = st;
         const char* ds_ = st + kSubRowBytes;
@@ -1628,10 +1627,7 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
                         }
                         sb[st2].w[w] = pack_bf16x2(dv2[0], dv2[1]);
                     }
-                if constexpr (DS) {
-                    store_ds_native<G>(bp, sb, dsr, greal, ts, half, kt0 / 32 + wave);
-                    ++stored;
-                }
+                if constexpr (DS) store_ds_native<G>(bp, sb, dsr, greal, ts, half, kt0 / 32 + wave);
                 const uint32_t qb_ = lds_addr(qs) + 32 * half * kRowBytes;
                 const uint32_t db_ = lds_addr(ds_) + 32 * half * kRowBytes;
 #pragma unroll
@@ -1649,13 +1645,10 @@ __global__ void __launch_bounds__(kThreads, 1) bwd_dkdv_kernel(BwdParams bp) {
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // wait for the next sub-tile's staging; the dS stores of the last half
-        // (issued after it, completing in order with it) stay in flight into
-        // the next sub-tile
-        if (DS && stored)
-            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        // (the dS stores count here too: a wait that let the last half's
+        // stores stay in flight, vmcnt(2), measured no faster, and it would
+        // rest on loads and stores completing in order)
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         tile_barrier();
         if (n + 2 < n_sub) stage_sub(n + 2, stage0 + (n & 1) * kSubStage);
     }
