@@ -24,10 +24,16 @@
 // before its MFMAs.  K and V tiles go from global memory straight into two
 // LDS stages (buffer_load ... lds), the next tile loading while the current
 // one is computed, one barrier per tile.  The tile walk is kept in scalar
-// registers and touches LDS only at range boundaries.  Plain path: one
-// thread per query row with 64-key tiles, the same walk and classification,
-// fp32 arithmetic; it serves fp32 inputs and the bf16 shapes the MFMA kernel
-// is not built for (head_dim 64, GQA groups other than 1, 2, 4, 8).
+// registers and touches LDS only at range boundaries.  GQA groups 3 and 5-7
+// run on the 4- and 8-head layouts with the missing heads' rows idle.  Plain
+// path: one thread per query row with 64-key tiles, the same walk and
+// classification, fp32 arithmetic; it serves fp32 inputs and the bf16 shapes
+// the MFMA kernel is not built for (head_dim 64, GQA groups above 8).
+//
+// Trainer backward (bf16, head_dim 128): Delta = rowsum(dO * O); dK/dV with
+// one workgroup per 256-key block walking the query sub-tiles that see it;
+// dQ either in the forward's layout, rebuilding S and dP, or -- with the
+// caller's stored-dS workspace -- from the dS the dK/dV kernel stored.
 #include <mutex>
 
 #include "ps_internal.h"
