@@ -68,13 +68,18 @@ def run_bwd(q, k, v, do, P, W, start, stored_ds=False):
     res = [dev_to_f32(dq), dev_to_f32(dk), dev_to_f32(dv), dev_to_f32(delta), dev_to_f32(out)]
     if stored_ds:
         nbytes = ps.ps_prefill_bwd_ds_bytes(B, T, hq, hkv, start_pos=start, prefix_len=P, window=W)
-        ws = torch.full((max(nbytes, 1),), 0xFF, dtype=torch.uint8, device="cuda")
+        # NaN bytes; a shape that takes no workspace (groups above 4) must leave a
+        # buffer passed anyway untouched and rebuild dS
+        ws = torch.full((max(nbytes, 4096),), 0xFF, dtype=torch.uint8, device="cuda")
         dq2, dk2, dv2 = torch.full_like(qd, float("nan")), torch.empty_like(kd), torch.empty_like(vd)
         delta2 = torch.empty(B, T, hq, device="cuda")
         ps.ps_prefill_attn_bwd(qd, kd, vd, out, lse, dod, dq2, dk2, dv2, delta2, start_pos=start, prefix_len=P,
                                window=W, scale=sc, ds_work=ws)
         torch.cuda.synchronize()
         assert torch.equal(dk2, dk) and torch.equal(dv2, dv) and torch.equal(delta2, delta)
+        if nbytes == 0:
+            assert bool((ws == 0xFF).all()), "workspace written although the shape takes none"
+            assert torch.equal(dq2, dq)
         res.append(dev_to_f32(dq2))
     return tuple(res)
 
