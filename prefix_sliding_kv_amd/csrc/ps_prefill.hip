@@ -1138,33 +1138,33 @@ __device__ inline int lane_now() {
 // One 32 x 32 tile of bf16 dS from the key-on-the-lane layout the dK/dV
 // kernel stores (v[st]: rows 16 st + 4h + 0..3 in words 0-1 and
 // 16 st + 8 + 4h + 0..3 in words 2-3, the lane's key) to the query row on the
-// lane, through 2 KB of the wave's own LDS at tb: key rows of 32 query rows,
-// 8-byte units placed at u ^ ((key >> 2) & 7).  The transposing reads give
-// lane (row j, half h) keys 16 st + 4h + 0..3 and 16 st + 8 + 4h + 0..3, the
-// order of the K^T operands read_t_kswz gives.
+// lane, through 2 KB of the wave's own LDS at tb: one 64-byte row per key,
+// the lane's 16 bytes of step st at 16-byte slot (2 st + h) ^ ((key >> 2) & 3)
+// (one 128-bit write per step).  The transposing reads give lane (row j,
+// half h) keys 16 st + 4h + 0..3 and 16 st + 8 + 4h + 0..3, the order of the
+// K^T operands read_t_kswz gives; the slot swizzle keeps both the writes and
+// the reads free of bank conflicts.
 __device__ inline void ds_transpose(uint32_t tba, const Vec16 (&v)[2], Vec16 (&out)[2]) {
     const int lane = lane_now();
     const int h = lane >> 5, col = lane & 31, q = lane >> 4, gp = lane & 15;
-    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-        for (int part = 0; part < 2; ++part) {
-            const int u = 4 * st + 2 * part + h;
-            u32x2 w;
-            w.x = v[st].w[2 * part];
-            w.y = v[st].w[2 * part + 1];
-            *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
-                (uintptr_t)(tba + col * 64 + ((u ^ ((col >> 2) & 7)) << 3))) = w;
-        }
+    for (int st = 0; st < 2; ++st) {
+        i32x4 w;
+        __builtin_memcpy(&w, &v[st], 16);
+        *reinterpret_cast<__attribute__((address_space(3))) i32x4*>(
+            (uintptr_t)(tba + col * 64 + (((2 * st + h) ^ ((col >> 2) & 3)) << 4))) = w;
+    }
+    // lane (q, gp) fetches rows 16 (q & 1) + 4 (gp & 3) .. + 3 of key
+    // 16 st + 8 hf + 4 (q >> 1) + (gp >> 2): the 8-byte half (gp >> 1) & 1 of
+    // the slot written for step q & 1 by the lane half gp & 1
+    const int slot_r = 2 * (q & 1) + (gp & 1), part_r = (gp >> 1) & 1;
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             const int key = 16 * st + 8 * hf + 4 * h + (gp >> 2);
-            const int u = 4 * (q & 1) + (gp & 3);
-            const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4*)(uintptr_t)(tba + key * 64 + ((u ^ ((key >> 2) & 7)) << 3)));
+            const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+                uintptr_t)(tba + key * 64 + ((slot_r ^ ((key >> 2) & 3)) << 4) + (part_r << 3)));
             __builtin_memcpy(&out[st].w[2 * hf], &r, 8);
         }
 }
