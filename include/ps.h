@@ -406,8 +406,10 @@ int ps_prefill_attn(const ps_prefill_args* args, void* stream);
  * block of 32 positions), the 32 x 32 tiles of the key blocks those rows can
  * see: ps_prefill_bwd_ds_bytes gives its size, about
  * batch * n_q_heads * seq_len * (min(window, seq_len) + min(P', seq_len) + 64) * 2
- * bytes with P' the prefix keys inside the chunk.  Its contents on return are
- * unspecified; nothing needs clearing before a call.  With ds_work NULL
+ * bytes with P' the prefix keys inside the chunk.  dk and dv are the same
+ * either way, and dq is formed from the same bf16 dS in the same order.  The
+ * workspace's contents on return are unspecified; nothing needs clearing
+ * before a call.  With ds_work NULL
  * (ds_work_bytes ignored), or when ps_prefill_bwd_ds_bytes gives 0 (GQA
  * groups of more than 4 query heads, where storing costs more than it saves,
  * or one kv head's share of the workspace would reach 2^31 bytes), S and dP
