@@ -242,7 +242,9 @@ def decode_phases(torch, ps, cache, batch, pos_t, q_all, k_all, v_all, out, scal
     the library's decode trace (s_memrealtime stamps, 10 ns, written by thread
     0 of every workgroup).  Per launch, each phase ends when its last
     workgroup passes it; times are from the launch's first workgroup start."""
-    n_wg = 17 * HKV
+    # room for any split of 128 rows or more (the library's automatic choice
+    # at batch 1 is 192 rows); rows of workgroups that did not run stay 0
+    n_wg = -(-(P + W) // 128) * HKV
     buf = torch.zeros(LAYERS, n_wg, 8, dtype=torch.int64, device="cuda")
     g = torch.cuda.CUDAGraph()
     pos_t.fill_(TRACE - 1)
@@ -276,19 +278,22 @@ def decode_phases(torch, ps, cache, batch, pos_t, q_all, k_all, v_all, out, scal
              "arrival counted", "merged"]
     per = {n: [] for n in names}
     gaps, spans = [], []
+    ran = []
     for layer in range(LAYERS):
-        t = ts[layer]
+        t = ts[layer][ts[layer][:, 0] > 0]
+        ran.append(len(t))
         start = t[:, 0].min()
         for c, n in enumerate(names, start=1):
             col = t[:, c] if c < 7 else t[t[:, 7] > 0, 7]
             per[n].append(col.max() - start)
         spans.append(t[t[:, 7] > 0, 7].max() - start)
         if layer + 1 < LAYERS:
-            gaps.append(ts[layer + 1][:, 0].min() - t[t[:, 7] > 0, 7].max())
+            nxt = ts[layer + 1][ts[layer + 1][:, 0] > 0]
+            gaps.append(nxt[:, 0].min() - t[t[:, 7] > 0, 7].max())
     med = lambda xs: round(float(sorted(xs)[len(xs) // 2]), 2)
     res = {"note": "median over the 28 launches of one replayed step; each phase ends when the last workgroup "
                    "passes it, microseconds from the launch's first workgroup start (s_memrealtime, 10 ns)",
-           "workgroups": n_wg, "phase_end_us": {n: med(v) for n, v in per.items()},
+           "workgroups": max(ran), "phase_end_us": {n: med(v) for n, v in per.items()},
            "first_start_to_merge_end_us": med(spans), "merge_end_to_next_start_us": med(gaps),
            "traced_us_per_launch": round(traced_us, 3)}
     log(f"decode phases: {res}")

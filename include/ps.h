@@ -189,15 +189,16 @@ int ps_cache_set_checks(ps_cache* cache, int32_t on);
 int ps_cache_check_flags(ps_cache* cache, uint32_t* flags, int32_t clear, void* stream);
 
 /* Split-K granularity of decode: rows (keys) handled per workgroup.  0 picks
- * automatically (default); otherwise one of 16, 32, 64, 128, 256, 512 for
- * bf16 head_dim 128 and fp32 head_dim 64 (32..1024 for bf16 head_dim 64,
- * 16..256 for fp32 head_dim 128).  Errors: PS_ERR_INVALID (NULL, negative),
+ * automatically (default: the largest size whose launch has at least 160
+ * workgroups); otherwise one of 16, 32, 64, 128, 192, 256, 512 for bf16
+ * head_dim 128 and fp32 head_dim 64 (the same sizes times 2 for bf16
+ * head_dim 64, divided by 2 for fp32 head_dim 128).  Errors: PS_ERR_INVALID (NULL, negative),
  * PS_ERR_UNSUPPORTED (a size the kernel is not built for). */
 int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
 
 /* Decode phase trace, a profiling aid (off by default).  With dev_buf
  * non-NULL every later decode call on the cache (ps_decode_attn,
- * ps_decode_step) runs the same decode kernel, at 256 key rows per split and
+ * ps_decode_step) runs the same decode kernel, at its split size and
  * without the non-temporal hint, with thread 0 of each workgroup writing
  * s_memrealtime stamps (100 MHz) at eight points: entry, sequence metadata
  * in, K rows in and scored, V rows summed, waves combined, partial stored and
@@ -208,8 +209,9 @@ int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
  * the slot each call had at capture.  The stamps observe the kernel and skip
  * none of its work; the waits they need cost a little time.  NULL turns the
  * trace off.  While it is on, decode calls return PS_ERR_UNSUPPORTED for
- * shapes other than bf16, head_dim 128, GQA 1, 2 or 4 (split size automatic
- * or 256), or a launch of more than max_wg workgroups.
+ * shapes other than bf16, head_dim 128, GQA 1, 2 or 4 with a split of 192
+ * or 256 rows (set, or chosen automatically), or a launch of more than
+ * max_wg workgroups.
  * Errors: PS_ERR_INVALID (NULL cache; n_launches or max_wg < 1 with a
  * buffer). */
 int ps_cache_set_decode_trace(ps_cache* cache, uint64_t* dev_buf, int32_t n_launches, int32_t max_wg);

@@ -174,6 +174,17 @@ __device__ inline float rowgroup_max(float x) {
     return x;
 }
 
+// A wave-uniform address in scalar registers, for scalar loads written in asm
+// (an address the compiler happened to form in vector registers would not
+// assemble there).
+template <typename P>
+__device__ inline P* sgpr_ptr(P* ptr) {
+    const uint64_t a = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    return reinterpret_cast<P*>(((uint64_t)hi << 32) | lo);
+}
+
 // Phase timestamp of a traced launch (thread 0 of each workgroup).
 __device__ inline void trace_mark(const DecodeParams& p, int point) {
     p.trace[(size_t)blockIdx.x * kDecodeTracePoints + point] = __builtin_amdgcn_s_memrealtime();
@@ -214,16 +225,15 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         }
     }
     const int n_groups = p.n_seqs * p.c.hkv;
-    const int group = (int)blockIdx.x % n_groups, split = (int)blockIdx.x / n_groups;
-    const int g = group % p.c.hkv, b = group / p.c.hkv;
+    // (the divisions run through the vector unit: readfirstlane keeps the
+    // results, and every address made from them, in scalar registers)
+    const int group = __builtin_amdgcn_readfirstlane((int)blockIdx.x % n_groups);
+    const int split = __builtin_amdgcn_readfirstlane((int)blockIdx.x / n_groups);
+    const int g = __builtin_amdgcn_readfirstlane(group % p.c.hkv), b = __builtin_amdgcn_readfirstlane(group / p.c.hkv);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar address arithmetic
     const int sub = lane % LPR, rg = lane / LPR;
 
-    // Metadata and queries first: independent loads, issued together.
-    const int64_t P = p.plen[b];
-    const int64_t i = p.pos[b];
-    const int64_t crow = PAGED ? 0 : p.c.rows[b], prow = PAGED ? 0 : p.c.prows[b];
     // paged: the page of this wave's rows (independent of the metadata)
     const int64_t wave_row0 = (int64_t)split * R + (int64_t)wave * U * RPW;
     // (a wave wholly past the last row reads entry 0; its loads are masked off)
@@ -231,12 +241,28 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
         PAGED ? (int64_t)p.c.pages[(int64_t)b * p.c.pages_per_seq +
                                    (wave_row0 < p.rows_per_head ? (wave_row0 >> p.c.page_shift) : 0)]
               : 0;
-    // The debug-check flag word is read beside the metadata rather than
-    // before it (when checks are off any readable word stands in and the
-    // value is ignored), so no round trip precedes the metadata; nothing
-    // below the test is addressed from the metadata before it.
+    // Metadata first: prefix length, position, the sequence's blocks and the
+    // debug-check flag word (when checks are off any readable word stands in
+    // and its value is ignored) are five scalar loads issued back to back
+    // and waited for once.  Left to the compiler they were spaced by a
+    // round trip each, which put about a microsecond before the first K load.
     const uint32_t* guard_p = p.c.guard ? p.c.guard : reinterpret_cast<const uint32_t*>(p.plen);
-    const uint32_t guard_v = *guard_p;
+    int32_t P32, crow32, prow32;
+    int64_t i;
+    uint32_t guard_v;
+    asm volatile(
+        "s_load_dword %0, %5, 0x0\n\t"
+        "s_load_dwordx2 %1, %6, 0x0\n\t"
+        "s_load_dword %2, %7, 0x0\n\t"
+        "s_load_dword %3, %8, 0x0\n\t"
+        "s_load_dword %4, %9, 0x0\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(P32), "=&s"(i), "=&s"(crow32), "=&s"(prow32), "=&s"(guard_v)
+        : "s"(sgpr_ptr(p.plen + b)), "s"(sgpr_ptr(p.pos + b)), "s"(sgpr_ptr(p.c.rows + b)),
+          "s"(sgpr_ptr(p.c.prows + b)), "s"(sgpr_ptr(guard_p))
+        : "memory");
+    const int64_t P = P32;
+    const int64_t crow = PAGED ? 0 : crow32, prow = PAGED ? 0 : prow32;
     Vec16 qraw[G];
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
@@ -289,37 +315,37 @@ __global__ void __launch_bounds__(NW * 64) decode_kernel(DecodeParams p) {
     const T* knew_row = fused ? reinterpret_cast<const T*>(p.knew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
     const T* vnew_row = fused ? reinterpret_cast<const T*>(p.vnew) + ((int64_t)b * p.c.hkv + g) * D : nullptr;
 
-    // Issue every K/V load of this lane's rows before any math.  Rows past
-    // the end are clamped to the last valid row (a harmless in-bounds read,
-    // no branch) and masked out of the softmax below.
+    // This lane's K loads, then its V loads.  Rows past the end are clamped
+    // to the last valid row (a harmless in-bounds read, no branch) and masked
+    // out of the softmax below.  (The compiler issues the V loads after the
+    // scores; pinning them before the scores with a scheduling barrier, so
+    // that K and V share one round trip, measured 1.5% slower at batch 1.)
     const int64_t r0 = (int64_t)split * R;
     Vec16 kr[U], vr[U];
+    const T* vps[U];
     bool valid[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t r = r0 + (int64_t)(wave * U + u) * RPW + rg;
+        const char* ka;
         if constexpr (PAGED) {
             // Every row is loaded (its page is a pool page, so the read is in
             // bounds); an unfilled slot may hold anything, so its score is
             // replaced by -inf and its V row by zeros below.
             valid[u] = r < p.c.pcap ? r < n_pre : (r - p.c.pcap < n_ring);
-            const bool is_new = fused && r == new_r;
-            const char* ka = lane_k + (int64_t)u * RPW * kRowBytes;
-            const T* kp = is_new ? knew_row : reinterpret_cast<const T*>(ka);
-            const T* vp = is_new ? vnew_row : reinterpret_cast<const T*>(ka + v_off);
-            kr[u] = load16_stream<NTL>(kp + sub * VEC);
-            vr[u] = load16_stream<NTL>(vp + sub * VEC);
-            continue;
+            ka = lane_k + (int64_t)u * RPW * kRowBytes;
+        } else {
+            valid[u] = r < n;
+            r = valid[u] ? r : n - 1;
+            ka = (r < n_pre ? kpre_a : kwin_a) + r * kRowBytes;
         }
-        valid[u] = r < n;
-        r = valid[u] ? r : n - 1;
         const bool is_new = fused && r == new_r;
-        const char* ka = (r < n_pre ? kpre_a : kwin_a) + r * kRowBytes;
         const T* kp = is_new ? knew_row : reinterpret_cast<const T*>(ka);
-        const T* vp = is_new ? vnew_row : reinterpret_cast<const T*>(ka + v_off);
+        vps[u] = is_new ? vnew_row : reinterpret_cast<const T*>(ka + v_off);
         kr[u] = load16_stream<NTL>(kp + sub * VEC);
-        vr[u] = load16_stream<NTL>(vp + sub * VEC);
     }
+#pragma unroll
+    for (int u = 0; u < U; ++u) vr[u] = load16_stream<NTL>(vps[u] + sub * VEC);
 
     // Scores (log2 units): q.k over this lane's slice, summed over the row's
     // lanes, then scaled.
@@ -918,7 +944,7 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
 
 // rows_per_split = NW * RPW * U: four waves for the two smallest sizes,
 // sixteen for 16 RPW and 128 RPW, eight (longer per-lane row chains, a
-// cheaper combine across waves) for 32 RPW and 64 RPW.
+// cheaper combine across waves) for 32 RPW, 48 RPW and 64 RPW.
 template <typename T, int D, int G>
 hipError_t dispatch_rows(int rows, const DecodeParams& p, hipStream_t stream) {
     constexpr int RPW = 64 / (D / Elem<T>::kPerVec);
@@ -927,6 +953,7 @@ hipError_t dispatch_rows(int rows, const DecodeParams& p, hipStream_t stream) {
     if (rows == 2 * r4) return launch_one<T, D, G, 4, 2>(p, stream);
     if (rows == r16) return launch_one<T, D, G, 16, 1>(p, stream);
     if (rows == 2 * r16) return launch_one<T, D, G, 8, 4>(p, stream);
+    if (rows == 3 * r16) return launch_one<T, D, G, 8, 6>(p, stream);
     if (rows == 4 * r16) {
         // many workgroups (several per CU) stream far more than the caches
         // hold: mark the K/V loads non-temporal (a single sequence's few
@@ -964,7 +991,8 @@ bool decode_rows_valid(int dtype, int head_dim, int rows) {
     const int rpw = decode_rows_per_load(dtype, head_dim);
     const int r4 = 4 * rpw, r16 = 16 * rpw;
     if (rows < kMinSplitRows) return false;
-    return rows == r4 || rows == 2 * r4 || rows == r16 || rows == 2 * r16 || rows == 4 * r16 || rows == 8 * r16;
+    return rows == r4 || rows == 2 * r4 || rows == r16 || rows == 2 * r16 || rows == 3 * r16 || rows == 4 * r16 ||
+           rows == 8 * r16;
 }
 
 hipError_t launch_decode_mfma(const DecodeParams& p, hipStream_t stream) {
@@ -981,16 +1009,23 @@ int64_t decode_grid(int rows_per_split, const DecodeParams& p) {
     return ((p.rows_per_head + rows_per_split - 1) / rows_per_split) * (int64_t)p.c.hkv * p.n_seqs;
 }
 
-hipError_t launch_decode_traced(int group, const DecodeParams& p, hipStream_t stream) {
-    const int64_t n_wg = decode_grid(256, p);
+template <int U>
+hipError_t launch_traced_u(int group, const DecodeParams& p, hipStream_t stream) {
+    const int64_t n_wg = decode_grid(8 * 4 * U, p);
     const dim3 grid((unsigned)n_wg), block(512);
     switch (group) {
-        case 1: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 1, 8, 8, false, true>), grid, block, 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 2, 8, 8, false, true>), grid, block, 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 4, 8, 8, false, true>), grid, block, 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 1, 8, U, false, true>), grid, block, 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 2, 8, U, false, true>), grid, block, 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((decode_kernel<uint16_t, 128, 4, 8, U, false, true>), grid, block, 0, stream, p); break;
         default: return hipErrorNotSupported;
     }
     return hipGetLastError();
+}
+
+hipError_t launch_decode_traced(int group, int rows_per_split, const DecodeParams& p, hipStream_t stream) {
+    if (rows_per_split == 256) return launch_traced_u<8>(group, p, stream);
+    if (rows_per_split == 192) return launch_traced_u<6>(group, p, stream);
+    return hipErrorNotSupported;
 }
 
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split, const DecodeParams& p,

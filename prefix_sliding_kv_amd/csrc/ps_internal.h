@@ -165,8 +165,8 @@ constexpr int kDecodeTracePoints = 8;
 // Workgroups of a decode launch with rows_per_split rows per split.
 int64_t decode_grid(int rows_per_split, const DecodeParams& p);
 // Traced decode (p.trace set): bf16, head_dim 128, GQA 1, 2 or 4, splits of
-// 256 rows, no non-temporal hint; other shapes return hipErrorNotSupported.
-hipError_t launch_decode_traced(int group, const DecodeParams& p, hipStream_t stream);
+// 192 or 256 rows, no non-temporal hint; other shapes return hipErrorNotSupported.
+hipError_t launch_decode_traced(int group, int rows_per_split, const DecodeParams& p, hipStream_t stream);
 // Launch decode attention; rows_per_split chosen by the caller (host).
 hipError_t launch_decode(int dtype, int head_dim, int group, int rows_per_split,
                          const DecodeParams& p, hipStream_t stream);

@@ -151,7 +151,7 @@ def test_qwen_shape_decode(L, layers, seed):
     check_cache_map(c, layers[-1], 0, P, W, i, seed, 0, hkv, d, base, DT_BF16)
 
 
-@pytest.mark.parametrize("split", [0, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("split", [0, 16, 32, 64, 96, 128, 256])
 def test_fp32_decode_over_4196_keys(split):
     """fp32 debug path at the decode configuration's key count: Hq=16, Hkv=8,
     d=128, P=100, W=4096, query at position 131071 (4196 retained keys), one
@@ -235,6 +235,7 @@ def test_ragged_batched_decode(fused, seed, layers):
     (500, 64, 300, 8, 1, 128, DT_F32, 16),   # all prefix (P > L), GQA 8, fp32 d=128
     (10, 1000, 600, 2, 2, 64, DT_BF16, 64),  # no eviction yet (W > L), MHA, bf16 d=64
     (7, 33, 777, 16, 8, 128, DT_BF16, 256),  # large split, ragged tail
+    (7, 300, 777, 16, 8, 128, DT_BF16, 192),  # 192-row split (48 row groups), ragged tail
     (12, 90, 500, 28, 4, 128, DT_BF16, 0),   # GQA 7 (28 q heads over 4 kv heads), automatic split
     (5, 40, 300, 15, 3, 128, DT_BF16, 32),   # GQA 5
     (9, 64, 350, 12, 2, 64, DT_BF16, 32),    # GQA 6, bf16 d=64
@@ -402,14 +403,17 @@ def test_flat_cost_once_window_is_full():
         c.close()
 
 
-def test_decode_trace_observes_without_changing_results():
+@pytest.mark.parametrize("split", [0, 192, 256])
+def test_decode_trace_observes_without_changing_results(split):
     """The decode phase trace (a profiling aid) runs the same kernel: outputs
     and cache bytes are bit-identical to an untraced step, every workgroup's
     stamps rise phase by phase, and exactly one workgroup per kv head merges.
-    Shapes the traced kernel is not built for are refused."""
+    Automatic split (192 rows at batch 1 here), 192 and 256 rows.  Shapes the
+    traced kernel is not built for are refused."""
     seed, P, W, hq, hkv, d, base = 8, 100, 4096, 16, 8, 128, 1e6
-    note("decode trace")
+    note(f"decode trace split={split}")
     c = new_cache(1, 1, hq, hkv, d, P, W, DT_BF16, poison=False)
+    ps.ps_cache_set_decode_split(c.handle, split)
     i = 9000
     fill_retained(ps, c, 0, 0, P, W, i - 1, seed, 0, hkv, d, base, DT_BF16)
     q = to_dev(gen(seed, synth.Q, 0, 0, [i], hq, d, base, DT_BF16))
@@ -418,7 +422,7 @@ def test_decode_trace_observes_without_changing_results():
     b = seq_batch(ps, [0], [P], [i])
     snap = c.buffer.clone()
     outs, lses, bufs = [], [], []
-    n_wg = 17 * hkv
+    n_wg = -(-(P + W) // (split or 192)) * hkv
     trace = torch.zeros(2, n_wg, 8, dtype=torch.int64, device="cuda")
     for traced in (False, True):
         c.buffer.copy_(snap)
