@@ -582,23 +582,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         const char* ks_lds = smem + (f & 1) * kStageBytes;
         __builtin_amdgcn_sched_barrier(0);
 
-        // S^T = K Q^T (raw scores, unscaled), one 32-key block per accumulator
-        f32x16 s[kMB];
-        {
-            const f32x16 zero = {};
-#pragma unroll
-            for (int kk = 0; kk < 8; ++kk)
-#pragma unroll
-                for (int mb = 0; mb < kMB; ++mb) {
-                    const int krow = 32 * mb + col;
-                    const Vec16 ka = *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
-                    s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qreg[kk]),
-                                                                     kk == 0 ? zero : s[mb], 0, 0, 0);
-                }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        tr_mark(0);
-
+        // S^T = K Q^T (raw scores, unscaled), one 32-key block per accumulator,
+        // in two halves of two interleaved blocks.  The mask and the running
+        // maximum of the first half need none of the second half's products,
+        // so they are written inside the same basic block as its MFMAs (one
+        // copy of that block per tile kind) and go out between them, while the
+        // matrix core is busy, instead of after the last product (0.5% on both
+        // prefill shapes, bit-identical).  Four one-block chains, each block's
+        // maximum beside the next block's products, were 2% slower: a chain of
+        // dependent products stalls the matrix core.
+        //
         // Elementwise mask, straddling tiles only.  For this lane's query the
         // visible keys of the tile (tile-relative index kr) form at most two
         // intervals: [0, min(pj, hic + 1)) -- the prefix -- and
@@ -606,14 +599,16 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
         // relw = rel - W, pj = P - j0, hic = min(rel, nrows - 1).  They become
         // one 32-bit bitmap per 32-key block, and each score is kept or set to
         // -inf with a bit extract and a bitfield select (no per-element compares).
-        if (cls == kMasked) {
+        f32x16 s[kMB];
+        float tmax = -INFINITY;
+        {
+            const f32x16 zero = {};
             const int pj = P32 - j0;
             const int rel = my_i - j0;
             const int hic = rel < nrows - 1 ? rel : nrows - 1;
             const int a_hi = pj < hic + 1 ? pj : hic + 1;
             const int b_lo = rel - w32 + 1 > 0 ? rel - w32 + 1 : 0;
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb) {
+            auto mask_block = [&](int mb) __attribute__((always_inline)) {
                 const uint32_t bits = range_bits(0, a_hi - 32 * mb) | range_bits(b_lo - 32 * mb, hic + 1 - 32 * mb);
                 const uint32_t bits_h = bits >> (4 * h);  // this lane half's keys start at bit 4h
 #pragma unroll
@@ -621,15 +616,45 @@ __global__ void __launch_bounds__(kThreads, 1) prefill_bf16_kernel(PrefillParams
                     const uint32_t km = (uint32_t)__builtin_amdgcn_sbfe((int)bits_h, 8 * (r >> 2) + (r & 3), 1);
                     s[mb][r] = __uint_as_float((km & __float_as_uint(s[mb][r])) | (~km & 0xFF800000u));
                 }
+            };
+            auto max_block = [&](int mb) __attribute__((always_inline)) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
+            };
+            auto qk_pair = [&](int half) __attribute__((always_inline)) {
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+                    for (int mb = 2 * half; mb < 2 * half + 2; ++mb) {
+                        const int krow = 32 * mb + col;
+                        const Vec16 ka = *reinterpret_cast<const Vec16*>(ks_lds + krow * kRowBytes + (((2 * kk + h) ^ k_chunk_swz(krow)) << 4));
+                        s[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka), as_bf16x8(qreg[kk]),
+                                                                         kk == 0 ? zero : s[mb], 0, 0, 0);
+                    }
+            };
+            qk_pair(0);
+            if (cls == kMasked) {
+                qk_pair(1);
+                mask_block(0);
+                mask_block(1);
+                max_block(0);
+                max_block(1);
+                __builtin_amdgcn_sched_barrier(0);
+                tr_mark(0);
+                mask_block(2);
+                mask_block(3);
+            } else {
+                qk_pair(1);
+                max_block(0);
+                max_block(1);
+                __builtin_amdgcn_sched_barrier(0);
+                tr_mark(0);
             }
+            max_block(2);
+            max_block(3);
         }
         // online softmax in raw-score units: the reference first
         {
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, s[mb][r]);
             tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
             // The exponent reference only moves when some row's maximum
             // exceeds it by more than 8 (log2 units): until then terms stay
