@@ -192,7 +192,7 @@ int ps_cache_check_flags(ps_cache* cache, uint32_t* flags, int32_t clear, void* 
  * automatically (default: the largest size whose launch has at least 160
  * workgroups); otherwise one of 16, 32, 64, 128, 192, 256, 512 for bf16
  * head_dim 128 and fp32 head_dim 64 (the same sizes times 2 for bf16
- * head_dim 64, divided by 2 for fp32 head_dim 128).  Errors: PS_ERR_INVALID (NULL, negative),
+ * head_dim 64; 16, 32, 64, 96, 128, 256 for fp32 head_dim 128).  Errors: PS_ERR_INVALID (NULL, negative),
  * PS_ERR_UNSUPPORTED (a size the kernel is not built for). */
 int ps_cache_set_decode_split(ps_cache* cache, int32_t rows_per_split);
 

@@ -49,7 +49,8 @@ def split_sizes(dtype, d):
     """0 (automatic) and the rows-per-split sizes the header lists for the shape."""
     lo = {(DT_BF16, 128): 16, (DT_F32, 64): 16, (DT_BF16, 64): 32, (DT_F32, 128): 16}[(dtype, d)]
     hi = {(DT_BF16, 128): 512, (DT_F32, 64): 512, (DT_BF16, 64): 1024, (DT_F32, 128): 256}[(dtype, d)]
-    return [0] + [r for r in (16, 32, 64, 128, 256, 512, 1024) if lo <= r <= hi]
+    mid = {(DT_BF16, 128): 192, (DT_F32, 64): 192, (DT_BF16, 64): 384, (DT_F32, 128): 96}[(dtype, d)]
+    return [0] + sorted([r for r in (16, 32, 64, 128, 256, 512, 1024) if lo <= r <= hi] + [mid])
 
 
 def draw(case):
